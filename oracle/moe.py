@@ -1,0 +1,242 @@
+"""Oracle for the routed-MoE prefill path (test infrastructure only).
+
+Plain definitions, FP64 unless the pages fix a precision. Grouping and sorting only
+change the order in which the same per-slot products are formed, so the grouped GEMM
+is written here as its plain definition: one dense product per expert segment.
+
+Sources (the pages' own sections):
+- Weight layout and dequant: forward_prefill_gemm module docs, "Layout compatibility"
+  table (rows "packed byte for logical k", "nibble", "codebook", "block scale",
+  "per-tensor scale", "remote expert (EP)", "table index"), and "What is NOT
+  bit-identical", item 2 (the BF16-rounded dequant product).
+- Routing buffers: glm5next_mlp forward.rs (2026-09-25), field docs of
+  Glm5NextMlpWorkspace for sorted_token_ids, sorted_expert_ids, expert_offsets and
+  token_to_perm.
+- SwiGLU with clamp: the doc comment of swiglu / swiglu_rows in both forward.rs pages.
+- Combine: forward_moe (2026-09-25), the glm5next_moe_combine_indexed launch and the
+  comment that the routed rows are expert-sorted and read back through token_to_perm;
+  "Zero FIRST" comment of the older forward_moe for the skipped-slot zeros.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import bf16_bits_from_f32, bf16_bits_to_f64, e2m1_decode, e4m3fn_decode, round_bf16
+
+GROUP_SIZE = 16  # k values per E4M3 block scale ("block scale" row: GROUP_SIZE 16)
+
+
+# ---------------------------------------------------------------------------------------
+# Dequant
+# ---------------------------------------------------------------------------------------
+
+def nibbles_of(packed: np.ndarray, k_total: int) -> np.ndarray:
+    """Unpack an N-major ``[N, K/2]`` byte matrix to ``[N, K]`` nibbles.
+
+    The byte for logical k of row n is ``packed[n, k // 2]``; even k takes the low
+    nibble, odd k the high nibble ("packed byte" and "nibble" rows of the layout table).
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    n_rows = packed.shape[0]
+    assert packed.shape == (n_rows, k_total // 2)
+    k = np.arange(k_total)
+    byte = packed[:, k // 2]
+    return np.where(k % 2 == 0, byte & 0xF, byte >> 4).astype(np.uint8)
+
+
+def dequant_f32(packed: np.ndarray, scales: np.ndarray, scale2: float) -> np.ndarray:
+    """FP32 dequantised weights ``[N, K]`` (returned as float64 holding FP32 values).
+
+    ``w = fl32(fl32(E2M1[q] * E4M3[s]) * scale2)``: the codebook value times the block
+    scale of ``scales[n, k // 16]``, then times the expert's FP32 scale2, each product
+    rounded to FP32 in that order (the grouped GEMM's order, scale2 "multiplied into the
+    dequant"). The first product is exact in FP32.
+    """
+    scales = np.asarray(scales, dtype=np.uint8)
+    n_rows, n_groups = scales.shape
+    k_total = n_groups * GROUP_SIZE
+    q = nibbles_of(packed, k_total)
+    v = e2m1_decode(q).astype(np.float32)
+    d = e4m3fn_decode(scales).astype(np.float32)  # E4M3 values are exact in FP32
+    d_per_k = np.repeat(d, GROUP_SIZE, axis=1)
+    s2 = np.float32(scale2)
+    with np.errstate(invalid="ignore", over="ignore"):
+        w32 = (v * d_per_k).astype(np.float32) * s2
+    return w32.astype(np.float32).astype(np.float64)
+
+
+def dequant(packed: np.ndarray, scales: np.ndarray, scale2: float, mode: str) -> np.ndarray:
+    """Dequantised weights as float64 ``[N, K]``.
+
+    ``mode="exact"``: the FP32 product itself. ``mode="bf16w"``: that FP32 product rounded
+    to BF16 (round-to-nearest-even), the operand the grouped GEMM feeds its BF16 MMA.
+    """
+    w32 = dequant_f32(packed, scales, scale2)
+    if mode == "exact":
+        return w32
+    if mode == "bf16w":
+        return bf16_bits_to_f64(bf16_bits_from_f32(w32.astype(np.float32)))
+    raise ValueError(mode)
+
+
+def dequant_bf16_bits(packed: np.ndarray, scales: np.ndarray, scale2: float) -> np.ndarray:
+    """BF16 bit patterns (uint16 ``[N, K]``) of the BF16-rounded dequantised weights."""
+    return bf16_bits_from_f32(dequant_f32(packed, scales, scale2).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------------------
+# Align: counting sort of the routed slots by expert
+# ---------------------------------------------------------------------------------------
+
+def align(topk_ids: np.ndarray, num_experts: int) -> dict:
+    """Sort the routed slots by expert (stable in the flat slot index).
+
+    Flat slot ``t = r * top_k + j`` of ``topk_ids[r, j]`` is valid when its id is in
+    ``[0, E)``; -1 is the router's "unfilled" sentinel and every out-of-range id is
+    excluded and counted. Returns:
+
+    - ``expert_offsets[E+1]``: exclusive prefix sum of per-expert slot counts.
+    - ``sorted_token_ids[S]``: for sorted row p, the token row ``t // top_k`` it came
+      from ("sorted row to original token").
+    - ``sorted_expert_ids[S]``: the expert of sorted row p.
+    - ``token_to_perm[T, top_k]``: slot t's row in the expert-sorted order, -1 if invalid.
+    - ``n_invalid``: number of excluded slots.
+
+    Rows ``[expert_offsets[E], S)`` of the two sorted arrays hold -1.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    rows, top_k = ids.shape
+    flat = ids.reshape(-1)
+    n_slots = flat.size
+    valid = (flat >= 0) & (flat < num_experts)
+
+    counts = np.zeros(num_experts, dtype=np.int64)
+    for t in range(n_slots):
+        if valid[t]:
+            counts[flat[t]] += 1
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    for e in range(num_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+
+    seen = np.zeros(num_experts, dtype=np.int64)  # slots of each expert placed so far
+    sorted_token_ids = np.full(n_slots, -1, dtype=np.int64)
+    sorted_expert_ids = np.full(n_slots, -1, dtype=np.int64)
+    token_to_perm = np.full(n_slots, -1, dtype=np.int64)
+    for t in range(n_slots):
+        if not valid[t]:
+            continue
+        e = flat[t]
+        pos = offsets[e] + seen[e]
+        seen[e] += 1
+        sorted_token_ids[pos] = t // top_k
+        sorted_expert_ids[pos] = e
+        token_to_perm[t] = pos
+    return {
+        "expert_offsets": offsets.astype(np.int32),
+        "sorted_token_ids": sorted_token_ids.astype(np.int32),
+        "sorted_expert_ids": sorted_expert_ids.astype(np.int32),
+        "token_to_perm": token_to_perm.reshape(rows, top_k).astype(np.int32),
+        "n_invalid": int((~valid).sum()),
+    }
+
+
+# ---------------------------------------------------------------------------------------
+# Grouped GEMM
+# ---------------------------------------------------------------------------------------
+
+def grouped_gemm(a, a_gather, experts, scale2, expert_offsets, out, mode: str,
+                 expert_subset=None):
+    """Grouped W4A16 product over the expert-sorted rows, written into ``out`` (float64).
+
+    For every expert e whose table entry is not null (``experts[e]`` is a
+    ``(packed [N, K/2], scales [N, K/16])`` pair; ``None`` is a null pointer, a remote
+    expert), and every sorted row s in ``[expert_offsets[e], expert_offsets[e+1])``::
+
+        out[s, n] = sum_k a[g(s), k] * w_e[n, k],   g(s) = a_gather[s] if a_gather else s
+
+    in FP64, with ``w_e`` from :func:`dequant` in ``mode``. Rows of null experts are left
+    as they are: the caller's zeros stand. ``expert_subset`` limits the work to some
+    experts (used for sampled checks at large sizes).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    offsets = np.asarray(expert_offsets, dtype=np.int64)
+    num_experts = offsets.size - 1
+    todo = range(num_experts) if expert_subset is None else expert_subset
+    for e in todo:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo or experts[e] is None:
+            continue
+        packed, scales = experts[e]
+        w = dequant(packed, scales, float(scale2[e]), mode)
+        rows = np.arange(lo, hi)
+        src = rows if a_gather is None else np.asarray(a_gather, dtype=np.int64)[rows]
+        out[lo:hi, :] = a[src, :] @ w.T
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# SwiGLU with clamp, combine, layer
+# ---------------------------------------------------------------------------------------
+
+def swiglu_clamp(gate, up, limit: float):
+    """``silu(min(gate, L)) * clamp(up, -L, L)`` elementwise in FP64, silu(x) = x / (1 + e^-x).
+
+    The gate is clamped from above only; the up value on both sides.
+    """
+    g = np.minimum(np.asarray(gate, dtype=np.float64), limit)
+    u = np.minimum(np.maximum(np.asarray(up, dtype=np.float64), -limit), limit)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    return silu * u
+
+
+def combine(expert_out, token_to_perm, topk_weights, shared=None):
+    """``out[r, h] = sum_j w[r, j] * expert_out[token_to_perm[r, j], h] (+ shared[r, h])``.
+
+    Slots with ``token_to_perm < 0`` are skipped. FP64, slots summed in j order.
+    """
+    e_out = np.asarray(expert_out, dtype=np.float64)
+    ttp = np.asarray(token_to_perm, dtype=np.int64)
+    wts = np.asarray(topk_weights, dtype=np.float64)
+    rows, top_k = ttp.shape
+    out = np.zeros((rows, e_out.shape[1]), dtype=np.float64)
+    for j in range(top_k):
+        p = ttp[:, j]
+        ok = p >= 0
+        out[ok] += wts[ok, j][:, None] * e_out[p[ok]]
+    if shared is not None:
+        out += np.asarray(shared, dtype=np.float64)
+    return out
+
+
+def moe_layer(x, topk_ids, topk_weights, gate_up, down, scale2_gate_up, scale2_down,
+              moe_intermediate: int, limit: float, mode: str, shared=None):
+    """One routed MoE layer over the rows of ``x`` (float64 ``[T, H]``).
+
+    Steps, in the order of the grouped-prefill arm of forward_moe (2026-09-25):
+    align -> zero expert_out -> grouped GEMM gate_up (A gathered through
+    sorted_token_ids) -> SwiGLU clamp -> grouped GEMM down (A = activated rows in sorted
+    order) -> indexed combine. ``gate_up[e]`` holds the fused ``[2*mi, H]`` projection,
+    gate rows ``[0, mi)`` then up rows ``[mi, 2*mi)``; ``down[e]`` is ``[H, mi]``.
+
+    In ``mode="bf16w"`` the three buffers the kernels keep in BF16 (gate_up output,
+    activation, expert_out) are rounded to BF16; the returned output is left unrounded.
+    Returns ``(out, intermediates)``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, hidden = x.shape
+    num_experts = len(gate_up)
+    al = align(topk_ids, num_experts)
+    n_slots = al["sorted_token_ids"].size
+    rnd = round_bf16 if mode == "bf16w" else (lambda v: v)
+
+    c = np.full((n_slots, 2 * moe_intermediate), np.nan)  # null-expert rows stay undefined
+    grouped_gemm(x, al["sorted_token_ids"], gate_up, scale2_gate_up, al["expert_offsets"], c, mode)
+    c = rnd(c)
+    act = rnd(swiglu_clamp(c[:, :moe_intermediate], c[:, moe_intermediate:], limit))
+    expert_out = np.zeros((n_slots, hidden))  # zero first: skipped slots add exactly 0
+    grouped_gemm(act, None, down, scale2_down, al["expert_offsets"], expert_out, mode)
+    expert_out = rnd(expert_out)
+    out = combine(expert_out, al["token_to_perm"], topk_weights, shared)
+    return out, {"align": al, "c": c, "act": act, "expert_out": expert_out}
