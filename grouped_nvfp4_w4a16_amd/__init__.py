@@ -1,0 +1,311 @@
+"""grouped_nvfp4_w4a16_amd: routed-MoE prefill with a grouped NVFP4 W4A16 GEMM on MI355X.
+
+Thin Python binding of ``libmoe_w4a16.so`` (the HIP kernels behind the C ABI in
+``include/moe_w4a16.h``). This module only marshals arguments: torch tensors supply device
+memory and the current HIP stream, every step of the computation runs in the library's
+kernels. Nothing here falls back to another implementation: if the library is missing,
+``load()`` raises.
+
+Calls (same names as the C ABI):
+- ``moe_align``: top-k ids -> expert-sorted slot order.
+- ``moe_w4a16_grouped_gemm``: one launch over all experts.
+- ``swiglu_clamp``, ``moe_combine``.
+- ``moe_w4a16_dequant_bf16``: diagnostic, the BF16 weight operand the GEMM decodes.
+
+Helpers: ``ExpertTable`` (device pointer table of per-expert NVFP4 weights),
+``Workspace`` (every buffer of one layer call, allocated once) and ``moe_layer`` (the
+calls of one routed layer in order).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "load", "MoeError", "moe_align", "moe_w4a16_grouped_gemm", "swiglu_clamp", "moe_combine",
+    "moe_w4a16_dequant_bf16", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
+
+# Every symbol include/moe_w4a16.h declares.
+EXPORTS = (
+    "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
+    "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
+)
+
+_LIB = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+_SIGNATURES = {
+    "moe_w4a16_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_w4a16_last_error": ([], ctypes.c_char_p),
+    "moe_align": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_w4a16_grouped_gemm": (
+        [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp],
+        ctypes.c_int),
+    "swiglu_clamp": ([_vp, _vp, _i64, _vp, _i64, _i32, _i32, _f32, _vp], ctypes.c_int),
+    "moe_combine": ([_vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
+                    ctypes.c_int),
+    "moe_w4a16_dequant_bf16": ([_vp, _vp, _f32, _vp, _i32, _i32, _vp], ctypes.c_int),
+}
+
+
+class MoeError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, name: str, status: int, message: str):
+        super().__init__(f"{name} failed with status {status}: {message}")
+        self.status = status
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the shared library (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m grouped_nvfp4_w4a16_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = lib
+    return lib
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        lib = load()
+        msg = lib.moe_w4a16_last_error().decode() or lib.moe_w4a16_status_string(status).decode()
+        raise MoeError(name, status, msg)
+
+
+def _p(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def _want(t, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+
+
+def _bf16_matrix(t, name):
+    """(data tensor, leading dimension in elements) of a row-major 2-D BF16 tensor."""
+    import torch
+
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected BF16 data, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name}: expected a row-major 2-D tensor")
+    return t, t.stride(0)
+
+
+# ------------------------------------------------------------------------------- calls
+
+def moe_align(topk_ids, num_experts: int, sorted_token_ids, sorted_expert_ids, expert_offsets,
+              token_to_perm, active_experts=None, counters=None, stream=None) -> None:
+    """Expert-sorted slot order of ``topk_ids`` (int32 ``[rows, top_k]``); see the header."""
+    import torch
+
+    for t, n in ((topk_ids, "topk_ids"), (sorted_token_ids, "sorted_token_ids"),
+                 (sorted_expert_ids, "sorted_expert_ids"), (expert_offsets, "expert_offsets"),
+                 (token_to_perm, "token_to_perm"), (active_experts, "active_experts"),
+                 (counters, "counters")):
+        _want(t, torch.int32, n)
+    rows, top_k = topk_ids.shape
+    s = rows * top_k
+    if not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be contiguous")
+    for t, need, n in ((sorted_token_ids, s, "sorted_token_ids"),
+                       (sorted_expert_ids, s, "sorted_expert_ids"),
+                       (token_to_perm, s, "token_to_perm"),
+                       (expert_offsets, num_experts + 1, "expert_offsets"),
+                       (active_experts, num_experts, "active_experts"), (counters, 2, "counters")):
+        if t is not None and (t.numel() < need or not t.is_contiguous()):
+            raise ValueError(f"{n}: needs {need} contiguous elements")
+    _check("moe_align", load().moe_align(
+        _p(topk_ids), rows, top_k, num_experts, _p(sorted_token_ids), _p(sorted_expert_ids),
+        _p(expert_offsets), _p(token_to_perm), _p(active_experts), _p(counters),
+        _stream(stream)))
+
+
+def moe_w4a16_grouped_gemm(a, table: "ExpertTable", expert_offsets, c, a_gather=None,
+                           max_rows: int | None = None, stream=None) -> None:
+    """``c[s] = a[g(s)] @ W_e^T`` for every sorted row s of every present expert e."""
+    import torch
+
+    a, lda = _bf16_matrix(a, "a")
+    c, ldc = _bf16_matrix(c, "c")
+    _want(expert_offsets, torch.int32, "expert_offsets")
+    _want(a_gather, torch.int32, "a_gather")
+    if expert_offsets.numel() < table.num_experts + 1:
+        raise ValueError("expert_offsets: needs num_experts + 1 elements")
+    rows = c.shape[0] if max_rows is None else max_rows
+    if rows > c.shape[0] or (a_gather is not None and a_gather.numel() < rows):
+        raise ValueError("max_rows exceeds c or a_gather")
+    if a_gather is None and rows > a.shape[0]:
+        raise ValueError("without a_gather, a needs max_rows rows")
+    if a.shape[1] < table.k or c.shape[1] < table.n:
+        raise ValueError("a or c too narrow for the table's k, n")
+    _check("moe_w4a16_grouped_gemm", load().moe_w4a16_grouped_gemm(
+        _p(a), lda, a.shape[0], _p(a_gather), _p(table.packed_ptrs), _p(table.scale_ptrs),
+        _p(table.scale2), _p(expert_offsets), table.num_experts, _p(c), ldc, rows, table.n,
+        table.k, _stream(stream)))
+
+
+def swiglu_clamp(gate, up, out, limit: float, stream=None) -> None:
+    """``out = silu(min(gate, L)) * clamp(up, -L, L)`` over ``[rows, n]`` views."""
+    if gate.shape != up.shape or gate.stride() != up.stride():
+        raise ValueError("gate and up must be views of the same shape and strides")
+    gate, ld_in = _bf16_matrix(gate, "gate")
+    out, ld_out = _bf16_matrix(out, "out")
+    rows, n = gate.shape
+    if out.shape[0] < rows or out.shape[1] < n:
+        raise ValueError("out too small")
+    _check("swiglu_clamp", load().swiglu_clamp(
+        _p(gate), _p(up), ld_in, _p(out), ld_out, rows, n, float(limit), _stream(stream)))
+
+
+def moe_combine(expert_out, token_to_perm, topk_weights, out, shared=None, stream=None) -> None:
+    """``out[r] = sum_j w[r, j] * expert_out[token_to_perm[r, j]] (+ shared[r])``."""
+    import torch
+
+    expert_out, ld_e = _bf16_matrix(expert_out, "expert_out")
+    out, ld_out = _bf16_matrix(out, "out")
+    _want(token_to_perm, torch.int32, "token_to_perm")
+    _want(topk_weights, torch.float32, "topk_weights")
+    rows, top_k = topk_weights.shape
+    if token_to_perm.numel() < rows * top_k or not token_to_perm.is_contiguous():
+        raise ValueError("token_to_perm: needs rows * top_k contiguous elements")
+    if not topk_weights.is_contiguous():
+        raise ValueError("topk_weights must be contiguous")
+    hidden = out.shape[1]
+    if expert_out.shape[1] < hidden or out.shape[0] < rows:
+        raise ValueError("shape mismatch")
+    ld_s = 0
+    if shared is not None:
+        shared, ld_s = _bf16_matrix(shared, "shared")
+    _check("moe_combine", load().moe_combine(
+        _p(expert_out), ld_e, expert_out.shape[0], _p(token_to_perm), _p(topk_weights),
+        _p(shared), ld_s, _p(out), ld_out, rows, hidden, top_k, _stream(stream)))
+
+
+def moe_w4a16_dequant_bf16(packed, scales, scale2: float, out, stream=None) -> None:
+    """Diagnostic: the BF16 weight operand ``out[n, k]`` the grouped GEMM decodes."""
+    import torch
+
+    _want(packed, torch.uint8, "packed")
+    _want(scales, torch.uint8, "scales")
+    n, half_k = packed.shape
+    k = half_k * 2
+    if scales.shape != (n, k // 16) or out.shape != (n, k):
+        raise ValueError("shape mismatch")
+    _check("moe_w4a16_dequant_bf16", load().moe_w4a16_dequant_bf16(
+        _p(packed), _p(scales), float(scale2), _p(out), n, k, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- helpers
+
+class ExpertTable:
+    """Device pointer table of one NVFP4 projection for all experts.
+
+    ``packed[e]`` is a uint8 ``[n, k/2]`` device tensor and ``scales[e]`` a uint8
+    ``[n, k/16]`` one, or ``None`` for an expert that is not present (a null entry: the
+    GEMM leaves its rows alone). ``scale2`` holds one float per expert. The table keeps
+    the tensors alive.
+    """
+
+    def __init__(self, packed, scales, scale2, n: int, k: int, device=None):
+        import torch
+
+        if len(packed) != len(scales) or len(packed) != len(scale2):
+            raise ValueError("packed, scales and scale2 need one entry per expert")
+        self.n, self.k, self.num_experts = int(n), int(k), len(packed)
+        pp, sp = [], []
+        for e, (p, s) in enumerate(zip(packed, scales)):
+            if (p is None) != (s is None):
+                raise ValueError(f"expert {e}: packed and scales must both be present or None")
+            if p is None:
+                pp.append(0)
+                sp.append(0)
+                continue
+            if p.dtype != torch.uint8 or s.dtype != torch.uint8 or not p.is_cuda:
+                raise TypeError(f"expert {e}: expected uint8 device tensors")
+            if tuple(p.shape) != (n, k // 2) or tuple(s.shape) != (n, k // 16):
+                raise ValueError(f"expert {e}: expected [{n}, {k // 2}] and [{n}, {k // 16}]")
+            if not (p.is_contiguous() and s.is_contiguous()):
+                raise ValueError(f"expert {e}: weights must be contiguous")
+            if p.data_ptr() % 16 or s.data_ptr() % 16:
+                raise ValueError(f"expert {e}: weights must be 16-byte aligned")
+            pp.append(p.data_ptr())
+            sp.append(s.data_ptr())
+            if device is None:
+                device = p.device
+        self._keep = (list(packed), list(scales))
+        self.packed_ptrs = torch.tensor(pp, dtype=torch.int64, device=device)
+        self.scale_ptrs = torch.tensor(sp, dtype=torch.int64, device=device)
+        self.scale2 = torch.as_tensor(scale2, dtype=torch.float32).to(device)
+        self.present = [p is not None for p in packed]
+
+
+class Workspace:
+    """Every buffer one routed-layer call needs, allocated once for up to ``max_rows``."""
+
+    def __init__(self, max_rows: int, top_k: int, num_experts: int, hidden: int,
+                 moe_intermediate: int, device="cuda"):
+        import torch
+
+        s = max_rows * top_k
+        i32 = dict(dtype=torch.int32, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.max_rows, self.top_k, self.num_experts = max_rows, top_k, num_experts
+        self.sorted_token_ids = torch.empty(s, **i32)
+        self.sorted_expert_ids = torch.empty(s, **i32)
+        self.expert_offsets = torch.empty(num_experts + 1, **i32)
+        self.token_to_perm = torch.empty(s, **i32)
+        self.active_experts = torch.empty(num_experts, **i32)
+        self.counters = torch.empty(2, **i32)
+        self.gate_up = torch.empty(s, 2 * moe_intermediate, **bf)
+        self.act = torch.empty(s, moe_intermediate, **bf)
+        self.expert_out = torch.empty(s, hidden, **bf)
+
+
+def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable,
+              moe_intermediate: int, limit: float, ws: Workspace, out, shared=None,
+              stream=None) -> None:
+    """One routed MoE layer over the rows of ``x``, all on the device, in the order of the
+    grouped-prefill arm: align -> zero expert_out -> grouped GEMM gate_up (rows gathered
+    through sorted_token_ids) -> SwiGLU clamp -> grouped GEMM down -> indexed combine.
+    ``ws.expert_out`` is zeroed first so experts that are not present add zero."""
+    rows, top_k = topk_ids.shape
+    s = rows * top_k
+    moe_align(topk_ids, gate_up.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
+              ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters, stream)
+    ws.expert_out[:s].zero_()
+    mi = moe_intermediate
+    moe_w4a16_grouped_gemm(x, gate_up, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
+                           max_rows=s, stream=stream)
+    swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], limit, stream)
+    moe_w4a16_grouped_gemm(ws.act, down, ws.expert_offsets, ws.expert_out, None, max_rows=s,
+                           stream=stream)
+    moe_combine(ws.expert_out[:s], ws.token_to_perm, topk_weights, out, shared, stream)

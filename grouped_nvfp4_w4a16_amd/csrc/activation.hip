@@ -1,0 +1,127 @@
+// swiglu_clamp and moe_combine: the bandwidth-bound steps around the grouped GEMMs.
+//
+// swiglu_clamp follows swiglu_rows on the 2026-09-25 glm5next_mlp forward.rs page:
+// out = silu(min(gate, limit)) * clamp(up, -limit, limit). moe_combine follows that
+// page's forward_moe: one launch for all rows, each slot's expert-sorted row found
+// through token_to_perm, weighted by its top-k weight, plus the shared-expert output.
+//
+// Both kernels move 16 bytes (8 BF16) per thread per operand with 128-bit loads and
+// stores and compute in FP32; a block of 256 threads covers 2048 columns of one row.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kColsPerBlock = kThreads * 8;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+
+__global__ __launch_bounds__(kThreads) void swiglu_clamp_kernel(
+    const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up, int64_t ld_in,
+    uint16_t *__restrict__ out, int64_t ld_out, int32_t n, float limit) {
+  const int row = blockIdx.y;
+  const int col = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (col >= n) return;
+  const size_t in_off = static_cast<size_t>(row) * ld_in + col;
+  float g[8], u[8], o[8];
+  unpack8(*reinterpret_cast<const uint4 *>(gate + in_off), g);
+  unpack8(*reinterpret_cast<const uint4 *>(up + in_off), u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float gc = fminf(g[i], limit);
+    const float uc = fminf(fmaxf(u[i], -limit), limit);
+    o[i] = gc / (1.0f + __expf(-gc)) * uc;
+  }
+  *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(o);
+}
+
+__global__ __launch_bounds__(kThreads) void moe_combine_kernel(
+    const uint16_t *__restrict__ expert_out, int64_t ld_e, int32_t expert_rows,
+    const int32_t *__restrict__ token_to_perm, const float *__restrict__ weights,
+    const uint16_t *__restrict__ shared, int64_t ld_s, uint16_t *__restrict__ out,
+    int64_t ld_out, int32_t hidden, int32_t top_k) {
+  const int row = blockIdx.y;
+  const int col = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (col >= hidden) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < top_k; ++j) {
+    const int p = token_to_perm[static_cast<size_t>(row) * top_k + j];
+    if (p < 0 || p >= expert_rows) continue;  // excluded slot: adds zero
+    const float w = weights[static_cast<size_t>(row) * top_k + j];
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4 *>(expert_out + static_cast<size_t>(p) * ld_e + col), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
+  }
+  if (shared != nullptr) {
+    float s[8];
+    unpack8(*reinterpret_cast<const uint4 *>(shared + static_cast<size_t>(row) * ld_s + col), s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += s[i];
+  }
+  *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(acc);
+}
+
+}  // namespace
+
+extern "C" int swiglu_clamp(const uint16_t *gate, const uint16_t *up, int64_t ld_in,
+                            uint16_t *out, int64_t ld_out, int32_t rows, int32_t n, float limit,
+                            void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(rows >= 0 && n >= 0 && n % 8 == 0,
+              "swiglu_clamp: need rows >= 0 and n >= 0 a multiple of 8 (rows=%d n=%d)", rows, n);
+  MOE_REQUIRE(limit > 0.0f, "swiglu_clamp: limit must be > 0");
+  MOE_REQUIRE(ld_in >= n && ld_in % 8 == 0 && ld_out >= n && ld_out % 8 == 0,
+              "swiglu_clamp: leading dimensions must be >= n and multiples of 8");
+  MOE_REQUIRE(rows <= 65535, "swiglu_clamp: rows must be <= 65535 (got %d)", rows);
+  if (rows == 0 || n == 0) return MOE_OK;
+  MOE_REQUIRE(gate && up && out, "swiglu_clamp: a required pointer is NULL");
+  MOE_REQUIRE(moe::aligned16(gate) && moe::aligned16(up) && moe::aligned16(out),
+              "swiglu_clamp: pointers must be 16-byte aligned");
+  const dim3 grid((n + kColsPerBlock - 1) / kColsPerBlock, rows);
+  return moe::launch("swiglu_clamp", swiglu_clamp_kernel, grid, dim3(kThreads), 0, stream, gate,
+                     up, ld_in, out, ld_out, n, limit);
+}
+
+extern "C" int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
+                           const int32_t *token_to_perm, const float *topk_weights,
+                           const uint16_t *shared, int64_t ld_s, uint16_t *out, int64_t ld_out,
+                           int32_t rows, int32_t hidden, int32_t top_k, void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(rows >= 0 && hidden >= 0 && hidden % 8 == 0,
+              "moe_combine: need rows >= 0 and hidden >= 0 a multiple of 8");
+  MOE_REQUIRE(top_k >= 1 && expert_rows >= 0, "moe_combine: need top_k >= 1, expert_rows >= 0");
+  MOE_REQUIRE(ld_e >= hidden && ld_e % 8 == 0 && ld_out >= hidden && ld_out % 8 == 0,
+              "moe_combine: leading dimensions must be >= hidden and multiples of 8");
+  MOE_REQUIRE(shared == nullptr || (ld_s >= hidden && ld_s % 8 == 0),
+              "moe_combine: ld_s must be >= hidden and a multiple of 8");
+  MOE_REQUIRE(rows <= 65535, "moe_combine: rows must be <= 65535 (got %d)", rows);
+  if (rows == 0 || hidden == 0) return MOE_OK;
+  MOE_REQUIRE(expert_out && token_to_perm && topk_weights && out,
+              "moe_combine: a required pointer is NULL");
+  MOE_REQUIRE(moe::aligned16(expert_out) && moe::aligned16(out) &&
+                  (shared == nullptr || moe::aligned16(shared)),
+              "moe_combine: BF16 pointers must be 16-byte aligned");
+  const dim3 grid((hidden + kColsPerBlock - 1) / kColsPerBlock, rows);
+  return moe::launch("moe_combine", moe_combine_kernel, grid, dim3(kThreads), 0, stream,
+                     expert_out, ld_e, expert_rows, token_to_perm, topk_weights, shared, ld_s,
+                     out, ld_out, hidden, top_k);
+}

@@ -1,0 +1,190 @@
+// moe_align: stable counting sort of the routed slots by expert, in one workgroup.
+//
+// Produces the grouped path's routing buffers as the 2026-09-25 glm5next_mlp forward.rs
+// page documents them (Glm5NextMlpWorkspace fields sorted_token_ids, sorted_expert_ids,
+// expert_offsets, token_to_perm): expert_offsets is the prefix sum over the
+// expert-sorted rows, sorted_token_ids maps a sorted row back to its token, and
+// token_to_perm maps a slot to its sorted row.
+//
+// Design (gfx950, wave64): the slots are split into 16 contiguous ranges, one per wave.
+//   1. Each wave counts its range into a private LDS histogram (LDS atomics; counts do
+//      not depend on order).
+//   2. Per expert, the 16 per-wave counts become per-wave starting positions; a block
+//      scan over experts gives expert_offsets (and the active-expert list).
+//   3. Each wave walks its range again in order, 64 slots at a time. Lanes holding the
+//      same expert id are grouped with a ballot; a lane's rank in its group is the
+//      number of lower lanes in it, so positions follow slot order: the sort is stable
+//      and the result is deterministic (no atomics decide an order).
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan of one value per thread over the block; *total receives the sum.
+// Every thread of the block must call it (it holds barriers).
+__device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int t = lane < kWaves ? wave_tot[lane] : 0;
+    const int ti = wave_inclusive_scan(t);
+    if (lane < kWaves) wave_tot[lane] = ti - t;
+    if (lane == kWaves - 1) wave_tot[kWaves] = ti;
+  }
+  __syncthreads();
+  const int res = wave_tot[wave] + inc - v;
+  *total = wave_tot[kWaves];
+  __syncthreads();  // wave_tot is reused by the next call
+  return res;
+}
+
+__global__ __launch_bounds__(kThreads) void moe_align_kernel(
+    const int32_t *__restrict__ ids, int32_t n_slots, int32_t top_k, int32_t num_experts,
+    int32_t *__restrict__ sorted_token_ids, int32_t *__restrict__ sorted_expert_ids,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ token_to_perm,
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ counters) {
+  extern __shared__ int lds[];
+  const int E = num_experts;
+  int *hist = lds;                        // [kWaves][E]
+  int *wave_tot = lds + kWaves * E;       // [kWaves + 1]
+  int *n_invalid = wave_tot + kWaves + 1;  // [1]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
+  if (tid == 0) *n_invalid = 0;
+  __syncthreads();
+
+  // Contiguous slot range of this wave, a multiple of 64 long.
+  const int per_wave = ((n_slots + kWaves - 1) / kWaves + 63) & ~63;
+  const int begin = min(wave * per_wave, n_slots);
+  const int end = min(begin + per_wave, n_slots);
+  int *my_hist = hist + wave * E;
+
+  // 1. per-wave histograms
+  int invalid = 0;
+  for (int base = begin; base < end; base += 64) {
+    const int t = base + lane;
+    const bool in = t < end;
+    const int id = in ? ids[t] : -1;
+    const bool valid = in && id >= 0 && id < E;
+    if (valid) atomicAdd(&my_hist[id], 1);
+    invalid += __popcll(__ballot(in && !valid));
+  }
+  if (lane == 0 && invalid) atomicAdd(n_invalid, invalid);
+  __syncthreads();
+
+  // 2. per-wave start positions and expert offsets
+  int carry = 0, active_carry = 0;
+  for (int e0 = 0; e0 < E; e0 += kThreads) {
+    const int e = e0 + tid;
+    int cnt = 0;
+    if (e < E) {
+      for (int w = 0; w < kWaves; ++w) {
+        const int h = hist[w * E + e];
+        hist[w * E + e] = cnt;
+        cnt += h;
+      }
+    }
+    int total, act_total;
+    const int excl = block_exclusive_scan(cnt, wave_tot, &total);
+    const int act_excl = block_exclusive_scan(cnt > 0 ? 1 : 0, wave_tot, &act_total);
+    if (e < E) {
+      const int off = carry + excl;
+      expert_offsets[e] = off;
+      for (int w = 0; w < kWaves; ++w) hist[w * E + e] += off;
+      if (active_experts != nullptr && cnt > 0) active_experts[active_carry + act_excl] = e;
+    }
+    carry += total;
+    active_carry += act_total;
+  }
+  if (tid == 0) {
+    expert_offsets[E] = carry;
+    if (counters != nullptr) {
+      counters[0] = active_carry;
+      counters[1] = *n_invalid;
+    }
+  }
+  if (active_experts != nullptr)
+    for (int i = active_carry + tid; i < E; i += kThreads) active_experts[i] = -1;
+  __syncthreads();
+
+  // 3. stable scatter
+  for (int base = begin; base < end; base += 64) {
+    const int t = base + lane;
+    const bool in = t < end;
+    const int id = in ? ids[t] : -1;
+    const bool valid = in && id >= 0 && id < E;
+    int pos = -1;
+    uint64_t todo = __ballot(valid);
+    while (todo != 0) {
+      const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+      const int lid = __shfl(id, leader, 64);
+      const bool mine = valid && id == lid;
+      const uint64_t grp = __ballot(mine);
+      const int start = my_hist[lid];
+      if (mine) pos = start + __popcll(grp & ((1ull << lane) - 1ull));
+      if (lane == leader) my_hist[lid] = start + __popcll(grp);
+      todo &= ~grp;
+    }
+    if (in) {
+      token_to_perm[t] = pos;
+      if (valid) {
+        sorted_token_ids[pos] = t / top_k;
+        sorted_expert_ids[pos] = id;
+      }
+    }
+  }
+  for (int p = carry + tid; p < n_slots; p += kThreads) {
+    sorted_token_ids[p] = -1;
+    sorted_expert_ids[p] = -1;
+  }
+}
+
+}  // namespace
+
+extern "C" int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k,
+                         int32_t num_experts, int32_t *sorted_token_ids,
+                         int32_t *sorted_expert_ids, int32_t *expert_offsets,
+                         int32_t *token_to_perm, int32_t *active_experts, int32_t *counters,
+                         void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(rows >= 0, "moe_align: rows must be >= 0 (got %d)", rows);
+  MOE_REQUIRE(top_k >= 1, "moe_align: top_k must be >= 1 (got %d)", top_k);
+  MOE_REQUIRE(num_experts >= 1 && num_experts <= MOE_ALIGN_MAX_EXPERTS,
+              "moe_align: num_experts must be in [1, %d] (got %d)", MOE_ALIGN_MAX_EXPERTS,
+              num_experts);
+  const int64_t n_slots = static_cast<int64_t>(rows) * top_k;
+  MOE_REQUIRE(n_slots <= INT32_MAX, "moe_align: rows * top_k overflows int32");
+  MOE_REQUIRE(expert_offsets != nullptr, "moe_align: expert_offsets is NULL");
+  if (n_slots > 0) {
+    MOE_REQUIRE(topk_ids && sorted_token_ids && sorted_expert_ids && token_to_perm,
+                "moe_align: a required pointer is NULL");
+  }
+  const size_t lds = (static_cast<size_t>(kWaves) * num_experts + kWaves + 2) * sizeof(int);
+  // Histograms of large expert counts exceed the default 64 KiB of dynamic LDS.
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(moe_align_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>((kWaves * MOE_ALIGN_MAX_EXPERTS + kWaves + 2) * sizeof(int)));
+  if (lds > 65536 && attr_err != hipSuccess) {
+    moe::set_error("moe_align: cannot raise the LDS limit: %s", hipGetErrorString(attr_err));
+    return MOE_ELAUNCH;
+  }
+  return moe::launch("moe_align", moe_align_kernel, dim3(1), dim3(kThreads), lds, stream,
+                     topk_ids, static_cast<int32_t>(n_slots), top_k, num_experts,
+                     sorted_token_ids, sorted_expert_ids, expert_offsets, token_to_perm,
+                     active_experts, counters);
+}

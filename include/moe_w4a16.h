@@ -1,0 +1,183 @@
+/*
+ * moe_w4a16.h - C ABI of the grouped NVFP4 W4A16 routed-MoE prefill library (gfx950).
+ *
+ * The library runs the data-parallel hot path of one routed MoE layer at prefill:
+ *
+ *   moe_align               top-k expert ids -> expert-sorted slot order (counting sort)
+ *   moe_w4a16_grouped_gemm  one launch over all experts: gathered BF16 rows x NVFP4 weights
+ *   swiglu_clamp            silu(min(gate, L)) * clamp(up, -L, L)
+ *   moe_combine             top-k weighted sum of the expert-sorted rows per token
+ *
+ * Sources (the pages this library follows, by title and section):
+ *   [FPG]  "Module forward_prefill_gemm" (glm5next_mlp/forward_prefill_gemm), sections
+ *          "What this replaces", "Layout compatibility - VERIFIED, not assumed" (the
+ *          layout table), "What is NOT bit-identical" (item 2: the BF16 weight operand)
+ *          and "Buffer discipline".
+ *   [FWD]  "glm5next_mlp/forward.rs" (the 2026-09-25 metrale_model_arch page): the
+ *          Glm5NextMlpWorkspace field docs (sorted_token_ids, sorted_expert_ids,
+ *          expert_offsets, token_to_perm, expert_out), swiglu_rows, and forward_moe's
+ *          zero-first memset and glm5next_moe_combine_indexed launch.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise. The caller
+ *     allocates and owns every buffer; the library never allocates, frees, synchronises
+ *     or reads device memory from the host ([FPG] "Buffer discipline": nothing on the
+ *     path allocates). There is no host<->device traffic inside any call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Each call
+ *     only enqueues work on it and returns.
+ *   - BF16 tensors are passed as uint16_t bit patterns. Matrices are row-major with the
+ *     given leading dimension in ELEMENTS.
+ *   - Return value: 0 (MOE_OK) or a moe_status code. On error nothing was enqueued and
+ *     moe_w4a16_last_error() describes the failure (per calling thread).
+ *   - Data that only the device can see (ids, offsets, gather indices) is bounds-checked
+ *     in the kernels: out-of-range values are skipped as documented per call, never
+ *     dereferenced.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,    /* bad argument: NULL required pointer, bad size, misalignment */
+  MOE_ECAPACITY = 2, /* an output buffer is smaller than the work needs */
+  MOE_ELAUNCH = 3    /* the HIP runtime refused the kernel launch */
+} moe_status;
+
+/* Static description of a status code. Never NULL. */
+const char *moe_w4a16_status_string(int status);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char *moe_w4a16_last_error(void);
+
+/* Largest expert count moe_align accepts (one workgroup holds the histograms). */
+#define MOE_ALIGN_MAX_EXPERTS 2048
+
+/*
+ * moe_align - sort the routed slots by expert ([FWD] Glm5NextMlpWorkspace field docs).
+ *
+ * Slot t = r * top_k + j carries expert id topk_ids[t]. A slot is valid when its id is
+ * in [0, num_experts); -1 (an unfilled router slot) and every other out-of-range id are
+ * excluded from the sort. The sort is a stable counting sort: inside an expert's
+ * segment, slots keep ascending t (hence ascending token).
+ *
+ *   topk_ids           int32 [rows * top_k]       in
+ *   sorted_token_ids   int32 [rows * top_k]       out: sorted row p -> token row t / top_k
+ *   sorted_expert_ids  int32 [rows * top_k]       out: sorted row p -> expert id
+ *   expert_offsets     int32 [num_experts + 1]    out: exclusive prefix sum of the per-expert
+ *                                                 slot counts; [num_experts] = valid slots
+ *   token_to_perm      int32 [rows * top_k]       out: slot t -> its sorted row, -1 if invalid
+ *   active_experts     int32 [num_experts] or NULL  out: experts with a non-zero count,
+ *                                                 ascending, then -1 padding
+ *   counters           int32 [2] or NULL          out: {number of active experts,
+ *                                                 number of invalid slots}
+ *
+ * Sorted rows [expert_offsets[num_experts], rows * top_k) of the two sorted arrays are
+ * set to -1. rows == 0 is allowed (offsets and counters become 0).
+ * Errors: MOE_EINVAL if rows < 0, top_k < 1, num_experts < 1, num_experts >
+ * MOE_ALIGN_MAX_EXPERTS, or a required pointer is NULL while rows * top_k > 0.
+ */
+int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+              int32_t *sorted_token_ids, int32_t *sorted_expert_ids, int32_t *expert_offsets,
+              int32_t *token_to_perm, int32_t *active_experts, int32_t *counters,
+              void *stream);
+
+/*
+ * moe_w4a16_grouped_gemm - one launch over all experts ([FPG] "What this replaces" and
+ * the layout table).
+ *
+ * For every expert e whose packed_ptrs[e] is non-zero and every sorted row s in
+ * [expert_offsets[e], expert_offsets[e+1]) (clipped to [0, max_rows)):
+ *
+ *   c[s, n] = bf16( sum_k a[g(s), k] * W_e[n, k] )      n in [0, n), k in [0, k)
+ *   g(s)    = a_gather ? a_gather[s] : s
+ *
+ * W_e is expert e's NVFP4 weight, N-major:
+ *   packed_ptrs[e] -> uint8 [n, k/2]: byte of logical k in row n is n*(k/2) + k/2;
+ *                     even k is the low nibble, odd k the high nibble.
+ *   scale_ptrs[e]  -> uint8 [n, k/16]: E4M3 (OCP FN) block scale of k/16 in row n.
+ *   scale2[e]      -> float: the expert's second-level scale.
+ * Each weight is decoded through the E2M1 codebook (values 0, .5, 1, 1.5, 2, 3, 4, 6;
+ * nibble bit 3 is the sign) and rounded to the BF16 operand the matrix cores take:
+ *   W_e[n, k] = bf16_rne( fp32( fp32(e2m1(q) * e4m3(scale)) * scale2[e] ) )
+ * ([FPG] "What is NOT bit-identical", item 2). Products accumulate in FP32.
+ *
+ *   a               bf16  [a_rows, lda]  activations (row g(s) is read)
+ *   a_gather        int32 [max_rows] or NULL. An index outside [0, a_rows) reads a row
+ *                   of zeros.
+ *   packed_ptrs     uint64 [num_experts] device addresses (0 = expert not present here:
+ *                   its rows of c are not written, the caller's values stand, [FPG]
+ *                   layout table row "remote expert (EP)").
+ *   scale_ptrs      uint64 [num_experts] device addresses (non-zero where packed is).
+ *   scale2          float  [num_experts]
+ *   expert_offsets  int32  [num_experts + 1] as written by moe_align
+ *   c               bf16   [max_rows, ldc] output rows in expert-sorted order
+ *
+ * Requirements (else MOE_EINVAL): n > 0 and n % 16 == 0; k > 0 and k % 256 == 0;
+ * lda >= k and ldc >= n, both multiples of 8; a and c 16-byte aligned; num_experts >= 1;
+ * max_rows >= 0, a_rows >= 0; a, packed_ptrs, scale_ptrs, scale2, expert_offsets and c
+ * non-NULL. Each table address must be 16-byte aligned (not checked: device data).
+ * max_rows == 0 enqueues nothing.
+ */
+int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
+                           const int32_t *a_gather, const uint64_t *packed_ptrs,
+                           const uint64_t *scale_ptrs, const float *scale2,
+                           const int32_t *expert_offsets, int32_t num_experts, uint16_t *c,
+                           int64_t ldc, int32_t max_rows, int32_t n, int32_t k, void *stream);
+
+/*
+ * swiglu_clamp - out[r, j] = bf16( silu(min(gate[r, j], limit)) * clamp(up[r, j], -limit,
+ * limit) ), silu(x) = x / (1 + exp(-x)), computed in FP32 ([FWD] swiglu_rows). The gate is
+ * clamped from above only.
+ *
+ *   gate, up  bf16 [rows, ld_in] (for a fused gate_up buffer: up = gate + n)
+ *   out       bf16 [rows, ld_out]
+ * Requirements (else MOE_EINVAL): rows >= 0, n >= 0, n % 8 == 0, ld_in >= n and
+ * ld_out >= n multiples of 8, pointers 16-byte aligned and non-NULL when rows * n > 0,
+ * limit > 0.
+ */
+int swiglu_clamp(const uint16_t *gate, const uint16_t *up, int64_t ld_in, uint16_t *out,
+                 int64_t ld_out, int32_t rows, int32_t n, float limit, void *stream);
+
+/*
+ * moe_combine - out[r, h] = bf16( sum_{j < top_k} w[r, j] * expert_out[p, h] + shared[r, h] )
+ * with p = token_to_perm[r * top_k + j], summed in FP32 in slot order j = 0..top_k-1,
+ * the shared term added last ([FWD] forward_moe, glm5next_moe_combine_indexed). Slots
+ * with p outside [0, expert_rows) are skipped (an excluded slot adds zero).
+ *
+ *   expert_out     bf16  [expert_rows, ld_e]  expert-sorted rows
+ *   token_to_perm  int32 [rows * top_k]
+ *   topk_weights   float [rows * top_k]
+ *   shared         bf16  [rows, ld_s] or NULL (no shared-expert term)
+ *   out            bf16  [rows, ld_out]
+ * Requirements (else MOE_EINVAL): rows >= 0, hidden >= 0, hidden % 8 == 0, top_k >= 1,
+ * expert_rows >= 0, leading dimensions >= hidden and multiples of 8, pointers 16-byte
+ * aligned and non-NULL (shared excepted) when rows * hidden > 0.
+ */
+int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
+                const int32_t *token_to_perm, const float *topk_weights,
+                const uint16_t *shared, int64_t ld_s, uint16_t *out, int64_t ld_out,
+                int32_t rows, int32_t hidden, int32_t top_k, void *stream);
+
+/*
+ * moe_w4a16_dequant_bf16 - diagnostic: write the BF16 weight operand the grouped GEMM
+ * feeds its matrix cores, out[n, k] = W[n, k] as defined for moe_w4a16_grouped_gemm,
+ * through the same device decoder. Lets the decode be checked bit for bit.
+ *
+ *   packed  uint8 [n, k/2];  scales  uint8 [n, k/16];  out  bf16 [n, k]
+ * Requirements (else MOE_EINVAL): n > 0, k > 0, k % 32 == 0, pointers non-NULL and
+ * 16-byte aligned.
+ */
+int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales, float scale2,
+                           uint16_t *out, int32_t n, int32_t k, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

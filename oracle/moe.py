@@ -26,6 +26,9 @@ from .codecs import bf16_bits_from_f32, bf16_bits_to_f64, e2m1_decode, e4m3fn_de
 
 GROUP_SIZE = 16  # k values per E4M3 block scale ("block scale" row: GROUP_SIZE 16)
 
+E2M1_VALUES = e2m1_decode(np.arange(16))  # value of each 4-bit code
+E4M3_VALUES = e4m3fn_decode(np.arange(256))  # value of each 8-bit scale code
+
 
 # ---------------------------------------------------------------------------------------
 # Dequant
@@ -57,8 +60,9 @@ def dequant_f32(packed: np.ndarray, scales: np.ndarray, scale2: float) -> np.nda
     n_rows, n_groups = scales.shape
     k_total = n_groups * GROUP_SIZE
     q = nibbles_of(packed, k_total)
-    v = e2m1_decode(q).astype(np.float32)
-    d = e4m3fn_decode(scales).astype(np.float32)  # E4M3 values are exact in FP32
+    # Each code is decoded by the format definition once; elements then index the result.
+    v = E2M1_VALUES.astype(np.float32)[q]
+    d = E4M3_VALUES.astype(np.float32)[scales]  # E4M3 values are exact in FP32
     d_per_k = np.repeat(d, GROUP_SIZE, axis=1)
     s2 = np.float32(scale2)
     with np.errstate(invalid="ignore", over="ignore"):

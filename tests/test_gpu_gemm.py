@@ -1,0 +1,301 @@
+"""The grouped W4A16 GEMM and its weight decode on the GPU against the oracle.
+
+- Decode: bit-exact against the oracle's BF16-weight dequant, special scales included.
+- Layout pins: one-hot weights and power-of-two scale patterns give exact answers.
+- Numerics: against the BF16-weight oracle within the gate (max_abs / ||ref||_inf <= 5e-3)
+  and a per-element FP32 accumulation bound; against the exact oracle, reported.
+- Edge cases: null experts untouched, empty experts, ragged N (partial tiles), experts
+  with more rows than one pass, out-of-range gather indices, max_rows cut-off.
+- Full size: the 256-expert prefill sub-chunk shapes, sampled experts.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import codecs, moe
+from gpu_util import (GATE, LazyExperts, bf16_bits_host, bf16_dev, dev, f64, rel_err,
+                      upload_table, workload_tables)
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack(nib):
+    """[N, K] nibbles -> [N, K/2] bytes, even k in the low nibble."""
+    return (nib[:, 0::2] & 0xF) | ((nib[:, 1::2] & 0xF) << 4)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _dequant_gpu(hip, packed, scales, s2):
+    n, half = packed.shape
+    out = torch.empty((n, 2 * half), dtype=torch.bfloat16, device="cuda")
+    hip.moe_w4a16_dequant_bf16(dev(packed), dev(scales), float(s2), out)
+    torch.cuda.synchronize()
+    return bf16_bits_host(out)
+
+
+def _same_bits(got, ref):
+    gn = np.isnan(codecs.bf16_bits_to_f64(got))
+    rn = np.isnan(codecs.bf16_bits_to_f64(ref))
+    assert np.array_equal(gn, rn)
+    bad = (got != ref) & ~gn
+    assert not bad.any(), f"{bad.sum()} mismatches, first at {np.argwhere(bad)[0]}"
+
+
+@pytest.mark.parametrize("s2", [1.0, 0.7310585, 1.9999999, 0.5, 3.3e-36, 2.5e36, -1.25, 1e-40])
+def test_dequant_bit_exact_random(hip, s2):
+    rng = np.random.default_rng(17)
+    packed, scales = wl.random_nvfp4(rng, 96, 512)
+    # every E4M3 code somewhere: zero, subnormals, max, NaN, negative scales
+    scales.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)
+    ref = moe.dequant_bf16_bits(packed, scales, s2)
+    _same_bits(_dequant_gpu(hip, packed, scales, s2), ref)
+
+
+def test_dequant_bit_exact_all_nibbles_all_scales(hip):
+    # every (nibble, scale code) pair with a non-power-of-two scale2
+    codes = np.arange(256, dtype=np.uint8)
+    nib = np.tile(np.arange(16, dtype=np.uint8), (256, 2))  # [256, 32]
+    packed = _pack(nib)
+    scales = np.stack([codes, codes], axis=1)  # one code per row
+    for s2 in (1.3719, 0.51, 1.0 + 2 ** -23):
+        _same_bits(_dequant_gpu(hip, packed, scales, s2), moe.dequant_bf16_bits(packed, scales, s2))
+
+
+# ------------------------------------------------------------------------ GEMM runner
+
+def _gemm(hip, x_bits, experts, s2, offsets, n, k, gather=None, rows=None, fill=-3.0,
+          c_rows=None, table=None):
+    """Run the GPU GEMM; returns the output as float64 (rows not written keep ``fill``)."""
+    if table is None:
+        table = upload_table(hip, experts, s2, n, k)
+    rows = int(offsets[-1]) if rows is None else rows
+    c_rows = rows if c_rows is None else c_rows
+    c = torch.full((max(c_rows, 1), n), fill, dtype=torch.bfloat16, device="cuda")
+    g = None if gather is None else dev(np.asarray(gather, np.int32))
+    hip.moe_w4a16_grouped_gemm(bf16_dev(x_bits), table, dev(np.asarray(offsets, np.int32)), c,
+                               g, max_rows=rows)
+    torch.cuda.synchronize()
+    return f64(c)
+
+
+def _oracle(x_bits, experts, s2, offsets, n, gather, mode, rows=None):
+    rows = int(offsets[-1]) if rows is None else rows
+    out = np.full((rows, n), np.nan)
+    moe.grouped_gemm(codecs.bf16_bits_to_f64(x_bits), gather, experts, s2, offsets, out, mode)
+    return out
+
+
+def _acc_bound(x_bits, experts, s2, offsets, gather, k):
+    """Per-element bound on FP32 accumulation plus BF16 output rounding."""
+    ax = np.abs(codecs.bf16_bits_to_f64(x_bits))
+    rows = int(offsets[-1])
+    s = None
+    for e in range(len(offsets) - 1):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi <= lo or experts[e] is None:
+            continue
+        ex = experts[e]
+        if s is None:
+            s = np.zeros((rows, ex[0].shape[0]))
+        w = np.abs(moe.dequant(ex[0], ex[1], float(s2[e]), "bf16w"))
+        src = np.arange(lo, hi) if gather is None else np.asarray(gather)[lo:hi]
+        s[lo:hi] = ax[src] @ w.T
+    gamma = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
+    return gamma * s
+
+
+def _check_gemm(got, ref, bound, exact=None):
+    mask = ~np.isnan(ref)
+    err = np.abs(got - ref)
+    # half a BF16 ulp of the FP32 result (whose magnitude is at most |ref| + bound) plus
+    # the accumulation bound
+    lim = np.ldexp(1.0, np.frexp(np.abs(ref) + bound)[1] - 8) * 0.5 + bound * 1.001 + 1e-30
+    assert np.all(err[mask] <= lim[mask]), float(np.max((err - lim)[mask]))
+    r = rel_err(got[mask], ref[mask])
+    assert r <= GATE, r
+    return r
+
+
+# ------------------------------------------------------------------------ layout pins
+
+def test_one_hot_layout_is_exact(hip):
+    # W_e[n, k] = 1 at k = pi_e(n): y[s, n] = a[g(s), pi_e(n)] exactly. Pins N-major order,
+    # even-low nibble order, K/2 byte and K/16 scale indexing, the global-id table, the
+    # gather and the output row.
+    rng = np.random.default_rng(3)
+    t, e_n, n, k = 40, 5, 48, 512
+    x_bits = wl.bf16_normal(rng, (t, k))
+    experts, pis = [], []
+    for e in range(e_n):
+        pi = rng.integers(0, k, n)
+        nib = np.zeros((n, k), np.uint8)
+        nib[np.arange(n), pi] = 2 if e % 2 == 0 else 10  # +1.0 / -1.0
+        experts.append((_pack(nib), np.full((n, k // 16), 0x38, np.uint8)))
+        pis.append(pi)
+    counts = [7, 0, 19, 40, 5]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    gather = rng.integers(0, t, offsets[-1])
+    got = _gemm(hip, x_bits, experts, np.ones(e_n, np.float32), offsets, n, k, gather)
+    x = codecs.bf16_bits_to_f64(x_bits)
+    for e in range(e_n):
+        for s in range(offsets[e], offsets[e + 1]):
+            sign = 1.0 if e % 2 == 0 else -1.0
+            assert np.array_equal(got[s], sign * x[gather[s], pis[e]]), (e, s)
+
+
+def test_power_of_two_scale_pattern_is_exact(hip):
+    # One 1.0 per row at k = pi(n) with a distinct power-of-two block scale per (n, k/16)
+    # and scale2 = 2**-3: y = a[g, pi(n)] * 2**(f(n, pi(n)/16) - 3) exactly.
+    rng = np.random.default_rng(4)
+    t, n, k = 16, 32, 768
+    x_bits = wl.bf16_normal(rng, (t, k))
+    pi = rng.integers(0, k, n)
+    nib = np.zeros((n, k), np.uint8)
+    nib[np.arange(n), pi] = 2
+    exps = (np.arange(n)[:, None] * 5 + np.arange(k // 16)[None, :] * 3) % 13 - 6
+    codes = ((exps + 7) << 3).astype(np.uint8)
+    ex = [(_pack(nib), codes)]
+    offsets = np.array([0, t])
+    got = _gemm(hip, x_bits, ex, np.array([0.125], np.float32), offsets, n, k)
+    x = codecs.bf16_bits_to_f64(x_bits)
+    want = x[:, pi] * np.exp2(exps[np.arange(n), pi // 16] - 3)[None, :]
+    assert np.array_equal(got, want)
+
+
+def test_all_ones_gives_row_sums(hip):
+    rng = np.random.default_rng(5)
+    t, n, k = 20, 64, 1024
+    x_bits = wl.bf16_normal(rng, (t, k))
+    ex = [(np.full((n, k // 2), 0x22, np.uint8), np.full((n, k // 16), 0x38, np.uint8))]
+    offsets = np.array([0, t])
+    got = _gemm(hip, x_bits, ex, np.ones(1, np.float32), offsets, n, k)
+    ref = _oracle(x_bits, ex, np.ones(1, np.float32), offsets, n, None, "bf16w")
+    _check_gemm(got, ref, _acc_bound(x_bits, ex, np.ones(1), offsets, None, k))
+    assert np.all(got == got[:, :1])  # every weight row is the same
+
+
+# --------------------------------------------------------------------------- numerics
+
+def _routed_problem(w: wl.Workload):
+    ids, _ = wl.routing(w)
+    al = moe.align(ids, w.num_experts)
+    x_bits = wl.activations(w)
+    return al, x_bits
+
+
+def test_single_gemm_workload_vs_oracle(hip):
+    w = wl.WORKLOADS["single_gemm"]
+    al, x_bits = _routed_problem(w)
+    n, k = wl.gate_up_shape(w)
+    experts = LazyExperts(w, "gate_up")
+    s2 = wl.scale2_gate_up(w)
+    offsets, gather = al["expert_offsets"], al["sorted_token_ids"]
+    got = _gemm(hip, x_bits, experts, s2, offsets, n, k, gather)
+    ref = _oracle(x_bits, experts, s2, offsets, n, gather, "bf16w")
+    r = _check_gemm(got, ref, _acc_bound(x_bits, experts, s2, offsets, gather, k))
+    exact = _oracle(x_bits, experts, s2, offsets, n, gather, "exact")
+    r_exact = rel_err(got, exact)
+    print(f"single_gemm: vs bf16w {r:.6f}, vs exact {r_exact:.6f}")
+    # the BF16 weight operand moves the result by about 2**-9 per weight, no more
+    assert r_exact < 2 * GATE
+
+
+@pytest.mark.parametrize("n,k,counts,null,seed", [
+    (16, 256, [3, 0, 1, 33, 16], (), 0),            # one wave's rows, one pass and two
+    (144, 768, [70, 1, 0, 15, 32, 9], (2,), 1),     # partial block of rows, long expert
+    (400, 512, [5, 64, 0, 17], (0,), 2),            # ragged N tiles, exactly two passes
+    (256, 2048, [129, 0, 2], (), 3),                # five passes
+])
+def test_ragged_shapes_and_nulls(hip, n, k, counts, null, seed):
+    rng = np.random.default_rng(seed)
+    t = 50
+    x_bits = wl.bf16_normal(rng, (t, k))
+    experts = [None if e in null else wl.random_nvfp4(rng, n, k) for e in range(len(counts))]
+    s2 = rng.uniform(0.5, 2, len(counts)).astype(np.float32)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    gather = rng.integers(0, t, offsets[-1])
+    got = _gemm(hip, x_bits, experts, s2, offsets, n, k, gather)
+    ref = _oracle(x_bits, experts, s2, offsets, n, gather, "bf16w")
+    for e in null:  # rows of null experts keep the caller's values
+        assert np.all(got[offsets[e]:offsets[e + 1]] == -3.0)
+    _check_gemm(got, ref, _acc_bound(x_bits, experts, s2, offsets, gather, k))
+
+
+def test_no_gather_and_row_cut_off(hip):
+    rng = np.random.default_rng(6)
+    n, k = 64, 512
+    counts = [10, 20, 30]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    x_bits = wl.bf16_normal(rng, (offsets[-1], k))
+    experts = [wl.random_nvfp4(rng, n, k) for _ in counts]
+    s2 = np.ones(3, np.float32)
+    ref = _oracle(x_bits, experts, s2, offsets, n, None, "bf16w")
+    got = _gemm(hip, x_bits, experts, s2, offsets, n, k)
+    _check_gemm(got, ref, _acc_bound(x_bits, experts, s2, offsets, None, k))
+    # max_rows = 35 < offsets[-1]: rows >= 35 are never written
+    got = _gemm(hip, x_bits, experts, s2, offsets, n, k, rows=35, c_rows=60)
+    assert np.all(got[35:] == -3.0)
+    assert rel_err(got[:35], ref[:35]) <= GATE
+
+
+def test_out_of_range_gather_reads_zeros(hip):
+    rng = np.random.default_rng(7)
+    n, k, t = 32, 256, 8
+    x_bits = wl.bf16_normal(rng, (t, k))
+    ex = [wl.random_nvfp4(rng, n, k)]
+    gather = np.array([0, -1, 3, t, 7, 100000])
+    got = _gemm(hip, x_bits, ex, np.ones(1, np.float32), np.array([0, 6]), n, k, gather)
+    assert np.all(got[[1, 3, 5]] == 0.0)
+    ok = [0, 2, 4]
+    ref = _oracle(x_bits, ex, np.ones(1, np.float32), np.array([0, 3]), n,
+                  gather[ok], "bf16w")
+    assert rel_err(got[ok], ref) <= GATE
+
+
+def test_rejects_bad_shapes(hip):
+    table = upload_table(hip, [wl.random_nvfp4(np.random.default_rng(0), 32, 256)],
+                         [1.0], 32, 256)
+    a = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((4, 32), dtype=torch.bfloat16, device="cuda")
+    off = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    table.k = 200  # not a multiple of 256
+    with pytest.raises(hip.MoeError):
+        hip.moe_w4a16_grouped_gemm(a, table, off, c)
+    table.k, table.n = 256, 24  # not a multiple of 16
+    with pytest.raises(hip.MoeError):
+        hip.moe_w4a16_grouped_gemm(a, table, off, c)
+
+
+# ------------------------------------------------------------------ full-size samples
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_prefill_subchunk_shapes_sampled(hip, which):
+    """The 256-expert, 256-row sub-chunk GEMMs at full size in the bench's launch
+    configuration, checked on sampled experts (all rows and columns of each)."""
+    w = wl.WORKLOADS["prefill_subchunk"]
+    ids, _ = wl.routing(w)
+    al = moe.align(ids, w.num_experts)
+    offsets = al["expert_offsets"]
+    n, k = wl.gate_up_shape(w) if which == "gate_up" else wl.down_shape(w)
+    gu, dn, gt, dt = workload_tables(hip, w)
+    experts, table = (gu, gt) if which == "gate_up" else (dn, dt)
+    s2 = wl.scale2_gate_up(w) if which == "gate_up" else wl.scale2_down(w)
+    if which == "gate_up":
+        x_bits, gather = wl.activations(w), al["sorted_token_ids"]
+    else:  # the down GEMM reads its rows in order; seeded BF16 rows stand in for act
+        x_bits = wl.bf16_normal(np.random.default_rng(99), (offsets[-1], k))
+        gather = None
+    counts = np.diff(offsets)
+    sample = [int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 999))), 77]
+    got = _gemm(hip, x_bits, experts, s2, offsets, n, k, gather, fill=0.0, table=table)
+    # sampled experts against the oracle
+    ref = np.full(got.shape, np.nan)
+    moe.grouped_gemm(codecs.bf16_bits_to_f64(x_bits), gather, experts, s2, offsets, ref,
+                     "bf16w", expert_subset=sample)
+    mask = ~np.isnan(ref[:, 0])
+    assert rel_err(got[mask], ref[mask]) <= GATE
+    # every row written, finite, not zero
+    assert np.all(np.isfinite(got)) and np.all(np.abs(got).max(axis=1) > 0)

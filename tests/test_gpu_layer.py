@@ -1,0 +1,170 @@
+"""SwiGLU clamp, combine and the whole routed layer on the GPU against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import codecs, moe
+from gpu_util import GATE, LazyExperts, bf16_dev, dev, f64, rel_err, upload_table, workload_tables
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp_bf16(v):
+    return np.ldexp(1.0, np.frexp(np.maximum(np.abs(v), 2.0 ** -126))[1] - 8)
+
+
+# ------------------------------------------------------------------------------ SwiGLU
+
+@pytest.mark.parametrize("rows,mi,seed", [(1, 8, 0), (37, 768, 1), (5, 4104, 2), (300, 2048, 3)])
+def test_swiglu_clamp_vs_oracle(hip, rows, mi, seed):
+    rng = np.random.default_rng(seed)
+    c_bits = codecs.bf16_bits_from_f32((rng.standard_normal((rows, 2 * mi)) * 5).astype(np.float32))
+    c_bits[0, :4] = codecs.bf16_bits_from_f32(np.array([7.0, 9.0, -30.0, 0.0], np.float32))
+    c = bf16_dev(c_bits)
+    out = torch.full((rows, mi), 99.0, dtype=torch.bfloat16, device="cuda")
+    hip.swiglu_clamp(c[:, :mi], c[:, mi:], out, 7.0)
+    torch.cuda.synchronize()
+    cf = codecs.bf16_bits_to_f64(c_bits)
+    ref = moe.swiglu_clamp(cf[:, :mi], cf[:, mi:], 7.0)
+    got = f64(out)
+    assert np.all(np.abs(got - ref) <= _ulp_bf16(ref) * 0.5 * (1 + 2 ** -4) + 1e-38)
+
+
+# ----------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_combine_vs_oracle(hip, shared):
+    rng = np.random.default_rng(11)
+    rows, top_k, hidden, s_rows = 70, 8, 2056, 600
+    e_bits = wl.bf16_normal(rng, (s_rows, hidden))
+    ttp = rng.integers(0, s_rows, (rows, top_k)).astype(np.int32)
+    ttp[3, 2] = -1
+    ttp[5, 0] = s_rows + 4  # out of range: skipped like an excluded slot
+    wts = rng.random((rows, top_k)).astype(np.float32)
+    sh_bits = wl.bf16_normal(rng, (rows, hidden)) if shared else None
+    out = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    hip.moe_combine(bf16_dev(e_bits), dev(ttp), dev(wts), out,
+                    None if sh_bits is None else bf16_dev(sh_bits))
+    torch.cuda.synchronize()
+    ttp_ref = np.where(ttp < s_rows, ttp, -1)
+    ref = moe.combine(codecs.bf16_bits_to_f64(e_bits), ttp_ref, wts,
+                      None if sh_bits is None else codecs.bf16_bits_to_f64(sh_bits))
+    got = f64(out)
+    bound = _ulp_bf16(ref) * 0.5 + 2 ** -20 * (np.abs(codecs.bf16_bits_to_f64(e_bits)).max() * 8 + 8)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_combine_top1_unit_weight_copies(hip):
+    rng = np.random.default_rng(12)
+    e_bits = wl.bf16_normal(rng, (32, 64))
+    perm = rng.permutation(32).astype(np.int32).reshape(32, 1)
+    out = torch.empty((32, 64), dtype=torch.bfloat16, device="cuda")
+    hip.moe_combine(bf16_dev(e_bits), dev(perm), dev(np.ones((32, 1), np.float32)), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), e_bits[perm[:, 0]])
+
+
+# ------------------------------------------------------------------------------- layer
+
+def _layer_inputs(w: wl.Workload, rows=None):
+    ids, wts = wl.routing(w)
+    x_bits = wl.activations(w)
+    if rows is not None:
+        ids, wts, x_bits = ids[rows], wts[rows], x_bits[rows]
+    return ids, wts, x_bits
+
+
+def _run_layer(hip, w, ids, wts, x_bits, gu_table, dn_table):
+    rows, top_k = ids.shape
+    ws = hip.Workspace(rows, top_k, w.num_experts, w.hidden, w.moe_intermediate)
+    out = torch.empty((rows, w.hidden), dtype=torch.bfloat16, device="cuda")
+    hip.moe_layer(bf16_dev(x_bits), dev(ids), dev(wts), gu_table, dn_table,
+                  w.moe_intermediate, w.limit, ws, out)
+    torch.cuda.synchronize()
+    return f64(out), ws
+
+
+def _tables(hip, w, null=(), only=None):
+    gu = LazyExperts(w, "gate_up", null)
+    dn = LazyExperts(w, "down", null)
+    gt = upload_table(hip, gu, wl.scale2_gate_up(w), *wl.gate_up_shape(w), only=only)
+    dt = upload_table(hip, dn, wl.scale2_down(w), *wl.down_shape(w), only=only)
+    return gu, dn, gt, dt
+
+
+def _oracle_rows(w, ids, wts, x_bits, gu, dn, mode, null=()):
+    gu_l = [None if e in null else gu[e] for e in range(w.num_experts)] if null else gu
+    dn_l = [None if e in null else dn[e] for e in range(w.num_experts)] if null else dn
+    out, _ = moe.moe_layer(codecs.bf16_bits_to_f64(x_bits), ids, wts, gu_l, dn_l,
+                           wl.scale2_gate_up(w), wl.scale2_down(w), w.moe_intermediate,
+                           w.limit, mode)
+    return out
+
+
+def test_layer_e64_vs_oracle(hip):
+    """Full routed layer, 256 rows x 64 experts, every output against the oracle."""
+    w = wl.WORKLOADS["layer_e64"]
+    ids, wts, x_bits = _layer_inputs(w)
+    gu, dn, gt, dt = _tables(hip, w)
+    got, ws = _run_layer(hip, w, ids, wts, x_bits, gt, dt)
+    ref = _oracle_rows(w, ids, wts, x_bits, gu, dn, "bf16w")
+    r = rel_err(got, ref)
+    exact = _oracle_rows(w, ids, wts, x_bits, gu, dn, "exact")
+    print(f"layer_e64: vs bf16w {r:.6f}, vs exact {rel_err(got, exact):.6f}")
+    assert r <= GATE
+    # routing outputs of the layer call are the oracle's, bit for bit
+    al = moe.align(ids, w.num_experts)
+    assert np.array_equal(ws.expert_offsets.cpu().numpy(), al["expert_offsets"])
+    assert np.array_equal(ws.token_to_perm.cpu().numpy(), al["token_to_perm"].reshape(-1))
+
+
+def test_small_m_half_null_vs_oracle(hip):
+    """8 rows over 256 experts with experts [128, 256) null: every output row."""
+    w = wl.WORKLOADS["small_m"]
+    ids, wts, x_bits = _layer_inputs(w)
+    live = sorted({int(e) for e in ids.reshape(-1) if not w.is_null(int(e))})
+    gu, dn, gt, dt = _tables(hip, w, only=set(live))
+    got, _ = _run_layer(hip, w, ids, wts, x_bits, gt, dt)
+    ref = _oracle_rows(w, ids, wts, x_bits, gu, dn, "bf16w")
+    assert rel_err(got, ref) <= GATE
+    # a token whose experts are all null gets exactly zero
+    for r in range(w.rows):
+        if all(w.is_null(int(e)) for e in ids[r]):
+            assert np.all(got[r] == 0.0)
+
+
+def test_expert_parallel_halves_sum_to_full(hip):
+    """Complementary null halves of the table give partial outputs that sum to the full
+    output (the per-GPU partial sums an all-reduce would add)."""
+    w = wl.custom("ep_halves", 77, rows=96, num_experts=16, top_k=4, hidden=512,
+                  moe_intermediate=256)
+    ids, wts, x_bits = _layer_inputs(w)
+    half = w.num_experts // 2
+    _, _, gt, dt = _tables(hip, w)
+    full, _ = _run_layer(hip, w, ids, wts, x_bits, gt, dt)
+    _, _, gt0, dt0 = _tables(hip, w, only=set(range(half)))
+    _, _, gt1, dt1 = _tables(hip, w, only=set(range(half, w.num_experts)))
+    a, _ = _run_layer(hip, w, ids, wts, x_bits, gt0, dt0)
+    b, _ = _run_layer(hip, w, ids, wts, x_bits, gt1, dt1)
+    # each of the three is BF16-rounded once from FP32 sums of the same products
+    tol = (_ulp_bf16(a) + _ulp_bf16(b) + _ulp_bf16(full)) * 0.5 + 2.0 ** -18 * np.abs(full).max()
+    assert np.all(np.abs(a + b - full) <= tol)
+
+
+@pytest.mark.parametrize("name,rows", [("prefill_subchunk", [0, 131]), ("long_prefill", [4000])])
+def test_full_size_layer_sampled_rows(hip, name, rows):
+    """The 256-expert layer at full size (whole sub-chunk on the GPU, in the bench's launch
+    configuration); sampled output rows against the oracle computed row by row."""
+    w = wl.WORKLOADS[name]
+    ids, wts = wl.routing(w)
+    x_bits = wl.activations(w)
+    c = rows[0] // w.chunk  # the sub-chunk holding the sampled rows
+    sl = slice(c * w.chunk, (c + 1) * w.chunk)
+    gu, dn, gt, dt = workload_tables(hip, w)
+    got, _ = _run_layer(hip, w, ids[sl], wts[sl], x_bits[sl], gt, dt)
+    assert np.all(np.isfinite(got)) and np.all(np.abs(got).max(axis=1) > 0)
+    local = [r - c * w.chunk for r in rows]
+    ref = _oracle_rows(w, ids[rows], wts[rows], x_bits[rows], gu, dn, "bf16w")
+    assert rel_err(got[local], ref) <= GATE

@@ -1,0 +1,92 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/*.h declares, and
+rejects bad arguments before anything reaches the GPU (no compute calls here)."""
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import grouped_nvfp4_w4a16_amd as pkg
+from grouped_nvfp4_w4a16_amd import build as builder
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkg.LIB_PATH):
+        builder.build()
+    return pkg.load()
+
+
+def _declared_functions():
+    names = []
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = _declared_functions()
+    for want in ("moe_align", "moe_w4a16_grouped_gemm", "swiglu_clamp", "moe_combine"):
+        assert want in names
+    assert sorted(pkg.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pkg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    assert lib.moe_w4a16_status_string(0) == b"ok"
+    assert lib.moe_w4a16_status_string(1) == b"invalid argument"
+    assert lib.moe_w4a16_status_string(99) == b"unknown status"
+
+
+def _bad(ptr=0x1000):
+    return ctypes.c_void_p(ptr)
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    n = None
+    # moe_align: negative rows, zero experts, too many experts, NULL offsets
+    assert lib.moe_align(n, -1, 8, 16, n, n, _bad(), n, n, n, n) == 1
+    assert lib.moe_align(n, 4, 8, 0, n, n, _bad(), n, n, n, n) == 1
+    assert lib.moe_align(n, 4, 8, 4096, n, n, _bad(), n, n, n, n) == 1
+    assert lib.moe_align(n, 4, 8, 16, n, n, n, n, n, n, n) == 1
+    assert b"expert_offsets" in lib.moe_w4a16_last_error()
+    # grouped GEMM: k not a multiple of 256, n not a multiple of 16, misaligned a, NULL table
+    args = dict(a=_bad(), lda=512, a_rows=8, g=n, pp=_bad(), sp=_bad(), s2=_bad(), off=_bad(),
+                e=4, c=_bad(), ldc=64, rows=8, nn=64, k=512)
+
+    def gemm(**kw):
+        a = {**args, **kw}
+        return lib.moe_w4a16_grouped_gemm(a["a"], a["lda"], a["a_rows"], a["g"], a["pp"], a["sp"],
+                                          a["s2"], a["off"], a["e"], a["c"], a["ldc"], a["rows"],
+                                          a["nn"], a["k"], n)
+    assert gemm(k=500) == 1
+    assert gemm(nn=40) == 1
+    assert gemm(a=_bad(0x1008)) == 1
+    assert gemm(pp=n) == 1
+    assert gemm(lda=256) == 1
+    assert gemm(rows=0) == 0  # nothing to do: returns without a launch
+    # swiglu: n not a multiple of 8, non-positive limit
+    assert lib.swiglu_clamp(_bad(), _bad(), 16, _bad(), 16, 4, 12, 7.0, n) == 1
+    assert lib.swiglu_clamp(_bad(), _bad(), 16, _bad(), 16, 4, 16, 0.0, n) == 1
+    assert lib.swiglu_clamp(n, n, 16, n, 16, 0, 16, 7.0, n) == 0  # empty
+    # combine: hidden not a multiple of 8, zero top_k
+    assert lib.moe_combine(_bad(), 16, 4, _bad(), _bad(), n, 0, _bad(), 16, 4, 12, 2, n) == 1
+    assert lib.moe_combine(_bad(), 16, 4, _bad(), _bad(), n, 0, _bad(), 16, 4, 16, 0, n) == 1
+    # dequant: k not a multiple of 32
+    assert lib.moe_w4a16_dequant_bf16(_bad(), _bad(), 1.0, _bad(), 4, 48, n) == 1
