@@ -1,0 +1,272 @@
+"""Benchmark of the routed-MoE prefill hot path on one MI355X.
+
+One step = one pass of the whole path over one 256-row batch of the prefill sub-chunk
+workload (256 experts, top_k 8, hidden 6144, moe_intermediate 2048, NVFP4 weights):
+moe_align -> zero expert_out -> grouped GEMM gate_up -> swiglu_clamp -> grouped GEMM down
+-> moe_combine, all enqueued on one HIP stream with every input already in HBM.
+
+Prints ONE JSON line. ``value`` is HBM GB/s on the unique expert-weight bytes the step
+reads (experts touched by the batch, both projections) divided by the step time;
+``tflops`` is the useful FLOP rate. ``roofline`` covers the dominant kernel (the gate_up
+grouped GEMM), timed with HIP events on the stream it runs on. ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--copy-probe]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+METRIC = "grouped MoE W4A16 GEMM: HBM GB/s on unique weights + TFLOP/s, 256-row prefill"
+
+
+def proj_bytes(n: int, k: int) -> int:
+    """HBM bytes of one expert's NVFP4 projection: packed nibbles, E4M3 scales, scale2."""
+    return n * k // 2 + n * k // 16 + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_subchunk")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration runs)")
+    return ap.parse_args()
+
+
+def upload_workload(hip, w, torch):
+    """Device copies of every input of the workload (weights drawn per expert)."""
+    import workloads as wl
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    gp, gs, dp, ds = [], [], [], []
+    for e in range(w.num_experts):
+        if w.is_null(e):
+            for lst in (gp, gs, dp, ds):
+                lst.append(None)
+            continue
+        p, s = wl.expert_gate_up(w, e)
+        gp.append(dev(p))
+        gs.append(dev(s))
+        p, s = wl.expert_down(w, e)
+        dp.append(dev(p))
+        ds.append(dev(s))
+    n_gu, k_gu = wl.gate_up_shape(w)
+    n_dn, k_dn = wl.down_shape(w)
+    gt = hip.ExpertTable(gp, gs, wl.scale2_gate_up(w), n_gu, k_gu)
+    dt = hip.ExpertTable(dp, ds, wl.scale2_down(w), n_dn, k_dn)
+    ids, wts = wl.routing(w)
+    x = dev(wl.activations(w).view(np.int16)).view(torch.bfloat16)
+    return gt, dt, dev(ids), dev(wts), x, ids
+
+
+def cpu_baseline(w, ids_chunk, seconds_budget=15.0):
+    """The oracle (BF16-weight mode) on a bounded sample: whole experts of the batch, both
+    projections, in expert order, until about ``seconds_budget`` of host time is spent."""
+    import workloads as wl
+    from oracle import codecs, moe
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    al = moe.align(ids_chunk, w.num_experts)
+    offsets = al["expert_offsets"]
+    x = codecs.bf16_bits_to_f64(wl.activations(w)[:ids_chunk.shape[0]])
+    s2gu, s2dn = wl.scale2_gate_up(w), wl.scale2_down(w)
+    n_gu, k_gu = wl.gate_up_shape(w)
+    n_dn, k_dn = wl.down_shape(w)
+    mi = w.moe_intermediate
+    done_bytes, flops, experts = 0, 0.0, 0
+    c = np.zeros((int(offsets[-1]), n_gu))
+    act = np.zeros((int(offsets[-1]), mi))
+    out = np.zeros((int(offsets[-1]), n_dn))
+    spent = 0.0
+    for e in range(w.num_experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo or w.is_null(e):
+            continue
+        gu = [None] * w.num_experts
+        dn = [None] * w.num_experts
+        gu[e] = wl.expert_gate_up(w, e)  # input generation: not timed
+        dn[e] = wl.expert_down(w, e)
+        t0 = time.perf_counter()
+        moe.grouped_gemm(x, al["sorted_token_ids"], gu, s2gu, offsets, c, "bf16w",
+                         expert_subset=[e])
+        cr = codecs.round_bf16(c[lo:hi])
+        act[lo:hi] = codecs.round_bf16(moe.swiglu_clamp(cr[:, :mi], cr[:, mi:], w.limit))
+        moe.grouped_gemm(act, None, dn, s2dn, offsets, out, "bf16w", expert_subset=[e])
+        spent += time.perf_counter() - t0
+        done_bytes += proj_bytes(n_gu, k_gu) + proj_bytes(n_dn, k_dn)
+        flops += 2.0 * (hi - lo) * (n_gu * k_gu + n_dn * k_dn)
+        experts += 1
+        if spent > seconds_budget:
+            break
+    dt = spent
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{experts} experts of the {w.name} batch (gate_up + SwiGLU + down, "
+                       f"all their routed rows, BF16-weight mode, generation excluded), "
+                       f"{dt:.1f} s"),
+            "tflops": round(flops / dt / 1e12, 6)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the expert-parallel split across GPUs is a design note, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import grouped_nvfp4_w4a16_amd as hip
+    import workloads as wl
+
+    if not os.path.exists(hip.LIB_PATH):
+        from grouped_nvfp4_w4a16_amd import build as builder
+        builder.build()
+    hip.load()
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    gt, dt, ids_all, wts_all, x_all, ids_host = upload_workload(hip, w, torch)
+    print(f"bench: uploaded {w.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+    rows = w.chunk
+    mi, hidden = w.moe_intermediate, w.hidden
+    ws = hip.Workspace(rows, w.top_k, w.num_experts, hidden, mi)
+    out = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    n_chunks = w.n_chunks
+
+    # Per-step work (first sub-chunk of the batch; for a multi-chunk workload each step
+    # runs one sub-chunk, cycling through them).
+    n_gu, k_gu = wl.gate_up_shape(w)
+    n_dn, k_dn = wl.down_shape(w)
+    step_bytes, step_flops, gu_bytes_alg = [], [], []
+    for c in range(n_chunks):
+        ids_c = ids_host[c * rows:(c + 1) * rows]
+        cnt = np.bincount(ids_c.reshape(-1), minlength=w.num_experts)
+        live = [e for e in range(w.num_experts) if cnt[e] > 0 and not w.is_null(e)]
+        slots_live = int(sum(cnt[e] for e in live))
+        wb = len(live) * (proj_bytes(n_gu, k_gu) + proj_bytes(n_dn, k_dn))
+        step_bytes.append(wb)
+        step_flops.append(2.0 * slots_live * (n_gu * k_gu + n_dn * k_dn))
+        # gate_up launch, algorithmic bytes: touched weights + the activation rows read
+        # once + the output rows written once + routing metadata
+        gu_bytes_alg.append(len(live) * proj_bytes(n_gu, k_gu) + rows * hidden * 2
+                            + slots_live * n_gu * 2 + (w.num_experts + 1) * 4 + rows * w.top_k * 4)
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+
+    def step(i, events=None):
+        c = i % n_chunks
+        sl = slice(c * rows, (c + 1) * rows)
+        ids, wts, x = ids_all[sl], wts_all[sl], x_all[sl]
+        s = rows * w.top_k
+        rec = (lambda j: events[j].record(stream)) if events else (lambda j: None)
+        rec(0)
+        hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
+                      ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
+        rec(1)
+        ws.expert_out[:s].zero_()
+        rec(2)
+        hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
+                                   max_rows=s)
+        rec(3)
+        hip.swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], w.limit)
+        rec(4)
+        hip.moe_w4a16_grouped_gemm(ws.act, dt, ws.expert_offsets, ws.expert_out, None,
+                                   max_rows=s)
+        rec(5)
+        hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out)
+        rec(6)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = gpu_ms / args.steps
+
+    names = ["moe_align", "zero_expert_out", "grouped_gemm_gate_up", "swiglu_clamp",
+             "grouped_gemm_down", "moe_combine"]
+    per = {n: [] for n in names}
+    for i in range(args.steps):
+        for j, n in enumerate(names):
+            per[n].append(ev[i][j].elapsed_time(ev[i][j + 1]))
+    kern_us = {n: round(1000.0 * float(np.mean(v)), 2) for n, v in per.items()}
+
+    chunk_of = [i % n_chunks for i in range(args.steps)]
+    total_bytes = sum(step_bytes[c] for c in chunk_of)
+    total_flops = sum(step_flops[c] for c in chunk_of)
+    value = total_bytes / (gpu_ms / 1000.0) / 1e9
+    tflops = total_flops / (gpu_ms / 1000.0) / 1e12
+
+    gu_s = np.array(per["grouped_gemm_gate_up"]) / 1000.0
+    gu_alg = np.array([gu_bytes_alg[c] for c in chunk_of])
+    achieved = float(np.mean(gu_alg) / np.mean(gu_s) / 1e9)
+    roofline = {"kernel": "moe_w4a16_grouped_gemm (gate_up)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_us": round(float(np.mean(gu_s)) * 1e6, 2),
+                "alg_bytes_per_launch": int(np.mean(gu_alg))}
+
+    if args.copy_probe:  # a plain copy of known size, for scaling HBM counters
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, ids_host[:rows])
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded NVFP4 weights and BF16 N(0,1) activations, random init)",
+        "config": {"workload": w.name, "rows_per_step": rows, "experts": w.num_experts,
+                   "top_k": w.top_k, "hidden": hidden, "moe_intermediate": mi,
+                   "routing": w.routing, "weight_format": "NVFP4 (E2M1 + E4M3/16 + FP32)",
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
+        "wall_s": round(wall, 4),
+        "kernel_us": kern_us,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,11 +12,15 @@
 // gfx950 design (the pages' mma.sync/shared-memory tiling is not used):
 //   - grid = (N / 128 weight-row tiles, experts); a block of 8 wave64s owns 128 weight
 //     rows of one expert (16 per wave) over the whole K, and loops over that expert's
-//     sorted rows 32 at a time, so its weight bytes are streamed once per 32 rows.
+//     sorted rows 16 at a time (one MFMA tile), so its weight bytes are streamed once per
+//     16 rows (once per launch for an expert with at most 16 routed rows).
 //   - The weights are the MFMA A operand (v_mfma_f32_16x16x32_bf16, M = 16 weight rows):
 //     each lane loads 2 x 16 bytes of packed nibbles (64 k of one row) plus the row's 16
-//     scale bytes per 256-k step with 128-bit loads, and decodes them in registers
-//     (nvfp4_decode.h) straight into A; no dequantised weight goes through LDS.
+//     scale bytes per 256-k step with 128-bit global loads, two steps ahead in a
+//     three-slot register ring, and decodes them in registers (nvfp4_decode.h) straight
+//     into A; no dequantised weight goes through LDS. The decode takes a wave-uniform
+//     branch: the byte-table path when every block of the wave allows it, else the exact
+//     per-element path.
 //   - The gathered activation rows are the B operand (16 rows per MFMA tile). They are
 //     staged per 256-k step in LDS (double buffered, one barrier per step), shared by the
 //     8 waves, with k permuted inside each group of 8 to match the decoder's order.
@@ -29,70 +33,108 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 16;
 constexpr int kBlockN = kWaves * kRowsPerWave;    // weight rows per block
 constexpr int kChunkK = 256;                      // k per main-loop step
-constexpr int kTokTiles = 2;                      // 16-row MFMA tiles per pass
-constexpr int kBlockM = 16 * kTokTiles;           // sorted rows per pass
+constexpr int kBlockM = 16;                       // sorted rows per pass: one MFMA tile
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
-constexpr int kPiecesPerThread = kBlockM * kPiecesPerRow / kThreads;
-static_assert(kPiecesPerThread * kThreads == kBlockM * kPiecesPerRow, "staging split");
+static_assert(kBlockM * kPiecesPerRow == kThreads, "one staging piece per thread");
 
+// One lane's share of a step: 64 k of one weight row (two 16-byte loads, contiguous
+// 64-byte runs per row across the wave) and that row's 16 block-scale bytes.
 struct WeightRegs {
-  uint4 a;  // packed bytes for k in [32 kb, 32 kb + 32) of the step
-  uint4 b;  // packed bytes for k in [128 + 32 kb, 128 + 32 kb + 32)
-  uint4 s;  // the row's 16 block-scale bytes of the step
+  u32x4_t a;   // k in [32 kb, 32 kb + 32) of the step
+  u32x4_t b;   // k in [128 + 32 kb, 128 + 32 kb + 32)
+  uint32_t sa;  // block scales of groups 2kb, 2kb+1 (low 16 bits)
+  uint32_t sb;  // block scales of groups 8+2kb, 9+2kb (low 16 bits)
 };
 
-__device__ __forceinline__ WeightRegs load_weights(const uint8_t *wrow, const uint8_t *srow,
-                                                   int step, int kb) {
-  WeightRegs r;
+// Global-memory view of a pointer read from the expert table. Without it the compiler
+// issues flat loads, which may alias LDS, and drains them before every LDS read.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *global_ptr(const void *p) {
+  return (const __attribute__((address_space(1))) T *)(p);
+}
+
+__device__ __forceinline__ u32x4_t load_w16(const uint8_t *p) { return *global_ptr<u32x4_t>(p); }
+
+__device__ __forceinline__ void load_weights(WeightRegs &w, const uint8_t *wrow,
+                                             const uint8_t *srow, int step, int kb) {
   const uint8_t *p = wrow + static_cast<size_t>(step) * (kChunkK / 2);
-  r.a = *reinterpret_cast<const uint4 *>(p + 16 * kb);
-  r.b = *reinterpret_cast<const uint4 *>(p + 64 + 16 * kb);
-  r.s = *reinterpret_cast<const uint4 *>(srow + static_cast<size_t>(step) * (kChunkK / 16));
-  return r;
+  w.a = load_w16(p + 16 * kb);
+  w.b = load_w16(p + 64 + 16 * kb);
+  const auto *q = global_ptr<uint16_t>(srow + static_cast<size_t>(step) * (kChunkK / 16));
+  w.sa = q[kb];
+  w.sb = q[4 + kb];
 }
 
 // 8 BF16 (k0..k7) -> order (k0,k2) (k4,k6) (k1,k3) (k5,k7), the decoder's order.
-__device__ __forceinline__ uint4 permute_k8(uint4 v) {
-  uint4 o;
-  o.x = moe::byte_perm(v.y, v.x, 0x05040100u);
-  o.y = moe::byte_perm(v.w, v.z, 0x05040100u);
-  o.z = moe::byte_perm(v.y, v.x, 0x07060302u);
-  o.w = moe::byte_perm(v.w, v.z, 0x07060302u);
+__device__ __forceinline__ u32x4_t permute_k8(u32x4_t v) {
+  u32x4_t o;
+  o[0] = moe::byte_perm(v[1], v[0], 0x05040100u);
+  o[1] = moe::byte_perm(v[3], v[2], 0x05040100u);
+  o[2] = moe::byte_perm(v[1], v[0], 0x07060302u);
+  o[3] = moe::byte_perm(v[3], v[2], 0x07060302u);
   return o;
 }
 
-__device__ __forceinline__ void stage_load(uint4 (&v)[kPiecesPerThread],
-                                           const uint16_t *const (&src)[kPiecesPerThread],
-                                           const int (&kofs)[kPiecesPerThread], int step) {
-#pragma unroll
-  for (int i = 0; i < kPiecesPerThread; ++i) {
-    v[i] = src[i] != nullptr
-               ? *reinterpret_cast<const uint4 *>(src[i] + step * kChunkK + kofs[i])
-               : make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void stage_store(uint8_t *buf, const uint4 (&v)[kPiecesPerThread],
-                                            const int (&lds_off)[kPiecesPerThread]) {
-#pragma unroll
-  for (int i = 0; i < kPiecesPerThread; ++i)
-    *reinterpret_cast<uint4 *>(buf + lds_off[i]) = permute_k8(v[i]);
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&w)[4]) {
-  uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
+  const u32x4_t u = {w[0], w[1], w[2], w[3]};
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
+// Multiply four decoded words (j0 .. j0+3) into acc against B operands read from LDS.
+template <bool kFast>
+__device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Block &b0,
+                                      const moe::Fp4Block &b1, const uint8_t *brow,
+                                      float scale2, f32x4_t &acc) {
+  bf16x8_t B[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) B[j] = *reinterpret_cast<const bf16x8_t *>(brow + 16 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t wd[4];
+    if (kFast) {
+      moe::decode8_fast(words[j], j < 2 ? b0 : b1, wd);
+    } else {
+      moe::decode8(words[j], j < 2 ? b0 : b1, scale2, wd);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wd), B[j], acc, 0, 0, 0);
+  }
+}
+
+// Decode this lane's 64 weights of the step and multiply them into acc against the
+// staged activation tile `xb` (rows = sorted rows of the pass, k permuted by 8s).
+__device__ __forceinline__ void compute_step(const WeightRegs &w, const uint8_t *xb, int r16,
+                                             int kb, float scale2, f32x4_t &acc) {
+  // B operands: row r16 of the tile, k in [32 kb + 8 j, +8) for j < 4, then +128.
+  const uint8_t *brow = xb + r16 * kLdsRowBytes + 64 * kb;
+  // Scale codes of groups 2kb, 2kb+1 (first 32 k) and 8+2kb, 9+2kb (second 32 k).
+  float d[4];
+  moe::e4m3x2_to_f32(w.sa, d[0], d[1]);
+  moe::e4m3x2_to_f32(w.sb, d[2], d[3]);
+  moe::Fp4Block blk[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) blk[g] = moe::make_block(d[g], scale2);
+  const uint32_t wa[4] = {w.a[0], w.a[1], w.a[2], w.a[3]};
+  const uint32_t wb[4] = {w.b[0], w.b[1], w.b[2], w.b[3]};
+  if (__all(moe::fast_pq4(blk[0].pq, blk[1].pq, blk[2].pq, blk[3].pq))) {
+    mfma4<true>(wa, blk[0], blk[1], brow, scale2, acc);
+    mfma4<true>(wb, blk[2], blk[3], brow + 256, scale2, acc);
+  } else {  // some block of the wave needs the exact per-element path
+    mfma4<false>(wa, blk[0], blk[1], brow, scale2, acc);
+    mfma4<false>(wb, blk[2], blk[3], brow + 256, scale2, acc);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t a_rows,
     const int32_t *__restrict__ gather, const uint64_t *__restrict__ packed_ptrs,
     const uint64_t *__restrict__ scale_ptrs, const float *__restrict__ scale2s,
@@ -117,92 +159,59 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
   const uint8_t *wrow = packed + static_cast<size_t>(n_row) * (K / 2);
   const uint8_t *srow = scales + static_cast<size_t>(n_row) * (K / 16);
   const int n_steps = K / kChunkK;
-
-  // This lane's scale bytes within a step: groups 2kb, 2kb+1 (first 32 k) and
-  // 8+2kb, 9+2kb (second 32 k).
-  const int s_shift = (kb & 1) * 16;
+  // this thread's staging piece: row piece_row of the pass, k [8 piece_col, +8) of a step
+  const int piece_row = tid / kPiecesPerRow, piece_col = tid % kPiecesPerRow;
+  const int lds_off = piece_row * kLdsRowBytes + piece_col * 16;
 
   for (int m0 = lo; m0 < hi; m0 += kBlockM) {
     const int m_cnt = min(kBlockM, hi - m0);
-
-    const uint16_t *src[kPiecesPerThread];
-    int kofs[kPiecesPerThread], lds_off[kPiecesPerThread];
-#pragma unroll
-    for (int i = 0; i < kPiecesPerThread; ++i) {
-      const int piece = tid + i * kThreads;
-      const int row = piece / kPiecesPerRow, col = piece % kPiecesPerRow;
-      kofs[i] = col * 8;
-      lds_off[i] = row * kLdsRowBytes + col * 16;
-      src[i] = nullptr;
-      if (row < m_cnt) {
-        const int s = m0 + row;
-        const int g = gather != nullptr ? gather[s] : s;
-        if (g >= 0 && g < a_rows) src[i] = a + static_cast<size_t>(g) * lda;
-      }
+    const uint16_t *xsrc = nullptr;  // rows past the pass are not staged: their output
+    if (piece_row < m_cnt) {         // columns are never stored
+      const int s = m0 + piece_row;
+      const int g = gather != nullptr ? gather[s] : s;
+      if (g >= 0 && g < a_rows) xsrc = a + static_cast<size_t>(g) * lda + piece_col * 8;
     }
+    const bool stage = piece_row < m_cnt;
 
-    f32x4_t acc[kTokTiles];
-#pragma unroll
-    for (int t = 0; t < kTokTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    WeightRegs w{};
-    if (wave_on) w = load_weights(wrow, srow, 0, kb);
-    uint4 xv[kPiecesPerThread];
-    stage_load(xv, src, kofs, 0);
-    stage_store(xs[0], xv, lds_off);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    WeightRegs w0, w1, w2;
+    if (wave_on) {
+      load_weights(w0, wrow, srow, 0, kb);
+      if (n_steps > 1) load_weights(w1, wrow, srow, 1, kb);
+    }
+    if (stage) {
+      const u32x4_t v = xsrc != nullptr ? *reinterpret_cast<const u32x4_t *>(xsrc)
+                                        : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t *>(xs[0] + lds_off) = permute_k8(v);
+    }
     __syncthreads();
 
-    for (int step = 0; step < n_steps; ++step) {
+    // One step: stage the next activation chunk, prefetch the weights two steps ahead,
+    // compute this step, publish the staged chunk.
+    auto run_step = [&](int step, WeightRegs &cur, WeightRegs &ahead) {
       const bool more = step + 1 < n_steps;
-      WeightRegs wn{};
-      if (more) {
-        if (wave_on) wn = load_weights(wrow, srow, step + 1, kb);
-        stage_load(xv, src, kofs, step + 1);
-      }
+      u32x4_t xv = {0u, 0u, 0u, 0u};
+      if (more && xsrc != nullptr)
+        xv = *reinterpret_cast<const u32x4_t *>(xsrc + (step + 1) * kChunkK);
       if (wave_on) {
-        const uint8_t *xb = xs[step & 1];
-        const uint32_t s_lo = ((kb & 2) ? w.s.y : w.s.x) >> s_shift;
-        const uint32_t s_hi = ((kb & 2) ? w.s.w : w.s.z) >> s_shift;
-        float d0, d1, d2, d3;
-        moe::e4m3x2_to_f32(s_lo, d0, d1);
-        moe::e4m3x2_to_f32(s_hi, d2, d3);
-        const moe::Fp4Block blk[4] = {moe::make_block(d0, scale2), moe::make_block(d1, scale2),
-                                      moe::make_block(d2, scale2), moe::make_block(d3, scale2)};
-        const uint32_t words[8] = {w.a.x, w.a.y, w.a.z, w.a.w, w.b.x, w.b.y, w.b.z, w.b.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          uint32_t wd[4];
-          moe::decode8(words[j], blk[j >> 1], scale2, wd);
-          const bf16x8_t A = as_bf16x8(wd);
-          const int kx = (j < 4 ? 32 * kb + 8 * j : 128 + 32 * kb + 8 * (j - 4)) * 2;
-#pragma unroll
-          for (int t = 0; t < kTokTiles; ++t) {
-            if (t * 16 < m_cnt) {
-              const bf16x8_t B =
-                  *reinterpret_cast<const bf16x8_t *>(xb + (t * 16 + r16) * kLdsRowBytes + kx);
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
-            }
-          }
-        }
+        if (step + 2 < n_steps) load_weights(ahead, wrow, srow, step + 2, kb);
+        compute_step(cur, xs[step & 1], r16, kb, scale2, acc);
       }
-      if (more) stage_store(xs[(step + 1) & 1], xv, lds_off);
+      if (more && stage) *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xv);
       __syncthreads();
-      w = wn;
+    };
+    for (int step = 0; step < n_steps; step += 3) {
+      run_step(step, w0, w2);
+      if (step + 1 < n_steps) run_step(step + 1, w1, w0);
+      if (step + 2 < n_steps) run_step(step + 2, w2, w1);
     }
 
-    // acc[t][i] = result for weight row n_wave0 + 4 kb + i and sorted row m0 + 16 t + r16.
-    if (wave_on) {
-#pragma unroll
-      for (int t = 0; t < kTokTiles; ++t) {
-        const int tok = t * 16 + r16;
-        if (tok < m_cnt) {
-          uint2 o;
-          o.x = moe::pack_bf16x2(acc[t][0], acc[t][1]);
-          o.y = moe::pack_bf16x2(acc[t][2], acc[t][3]);
-          *reinterpret_cast<uint2 *>(c + static_cast<size_t>(m0 + tok) * ldc + n_wave0 + 4 * kb) =
-              o;
-        }
-      }
+    // acc[i] = result for weight row n_wave0 + 4 kb + i and sorted row m0 + r16.
+    if (wave_on && r16 < m_cnt) {
+      uint2 o;
+      o.x = moe::pack_bf16x2(acc[0], acc[1]);
+      o.y = moe::pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<uint2 *>(c + static_cast<size_t>(m0 + r16) * ldc + n_wave0 + 4 * kb) = o;
     }
   }
 }
