@@ -34,7 +34,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -45,34 +44,38 @@ constexpr int kBlockM = 16;                       // sorted rows per pass: one M
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
-static_assert(kBlockM * kPiecesPerRow == kThreads, "one staging piece per thread");
+constexpr int kStageSteps = 4;                    // steps per staged block of scales
+constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 4 steps x 16 scale bytes, padded
+constexpr int kScaleBufBytes = kBlockN * kScaleRowBytes;
+static_assert(kBlockM * kPiecesPerRow == kThreads, "one activation piece per thread");
+static_assert(kBlockN * kStageSteps == kThreads, "one scale piece per thread");
 
-// One lane's share of a step: 64 k of one weight row (two 16-byte loads, contiguous
-// 64-byte runs per row across the wave) and that row's 16 block-scale bytes.
-struct WeightRegs {
-  u32x4_t a;   // k in [32 kb, 32 kb + 32) of the step
-  u32x4_t b;   // k in [128 + 32 kb, 128 + 32 kb + 32)
-  uint32_t sa;  // block scales of groups 2kb, 2kb+1 (low 16 bits)
-  uint32_t sb;  // block scales of groups 8+2kb, 9+2kb (low 16 bits)
-};
-
-// Global-memory view of a pointer read from the expert table. Without it the compiler
-// issues flat loads, which may alias LDS, and drains them before every LDS read.
-template <typename T>
-__device__ __forceinline__ const __attribute__((address_space(1))) T *global_ptr(const void *p) {
-  return (const __attribute__((address_space(1))) T *)(p);
+// Raw buffer access (gfx9 resource word 3): offsets past num_records read as zero
+// without touching memory, which masks padded and invalid rows at no cost.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                           static_cast<int>(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ u32x4_t load_w16(const uint8_t *p) { return *global_ptr<u32x4_t>(p); }
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                          uint32_t soff) {
+  return __builtin_bit_cast(
+      u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                     static_cast<int>(soff), 0));
+}
 
-__device__ __forceinline__ void load_weights(WeightRegs &w, const uint8_t *wrow,
-                                             const uint8_t *srow, int step, int kb) {
-  const uint8_t *p = wrow + static_cast<size_t>(step) * (kChunkK / 2);
-  w.a = load_w16(p + 16 * kb);
-  w.b = load_w16(p + 64 + 16 * kb);
-  const auto *q = global_ptr<uint16_t>(srow + static_cast<size_t>(step) * (kChunkK / 16));
-  w.sa = q[kb];
-  w.sb = q[4 + kb];
+// One lane's packed weights of a step: 64 k of one row as two 16-byte loads; the wave
+// reads 16 rows x 64 contiguous bytes per load.
+struct WeightRegs {
+  u32x4_t a;  // k in [32 kb, 32 kb + 32) of the step
+  u32x4_t b;  // k in [128 + 32 kb, 128 + 32 kb + 32)
+};
+
+__device__ __forceinline__ void load_weights(WeightRegs &w, __amdgpu_buffer_rsrc_t r,
+                                             uint32_t voff, int step) {
+  const uint32_t soff = static_cast<uint32_t>(step) * (kChunkK / 2);
+  w.a = load16(r, voff, soff);
+  w.b = load16(r, voff + 64, soff);
 }
 
 // 8 BF16 (k0..k7) -> order (k0,k2) (k4,k6) (k1,k3) (k5,k7), the decoder's order.
@@ -82,6 +85,17 @@ __device__ __forceinline__ u32x4_t permute_k8(u32x4_t v) {
   o[1] = moe::byte_perm(v[3], v[2], 0x05040100u);
   o[2] = moe::byte_perm(v[1], v[0], 0x07060302u);
   o[3] = moe::byte_perm(v[3], v[2], 0x07060302u);
+  return o;
+}
+
+// A row's 16 scale bytes of one step -> four dwords, dword kb holding the bytes lane kb
+// needs: groups 2kb, 2kb+1 (low half) and 8+2kb, 9+2kb (high half).
+__device__ __forceinline__ u32x4_t permute_scales(u32x4_t v) {
+  u32x4_t o;
+  o[0] = moe::byte_perm(v[2], v[0], 0x05040100u);
+  o[1] = moe::byte_perm(v[2], v[0], 0x07060302u);
+  o[2] = moe::byte_perm(v[3], v[1], 0x05040100u);
+  o[3] = moe::byte_perm(v[3], v[1], 0x07060302u);
   return o;
 }
 
@@ -112,14 +126,14 @@ __device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Block
 
 // Decode this lane's 64 weights of the step and multiply them into acc against the
 // staged activation tile `xb` (rows = sorted rows of the pass, k permuted by 8s).
-__device__ __forceinline__ void compute_step(const WeightRegs &w, const uint8_t *xb, int r16,
-                                             int kb, float scale2, f32x4_t &acc) {
-  // B operands: row r16 of the tile, k in [32 kb + 8 j, +8) for j < 4, then +128.
+// `sc` holds the lane's four scale codes (see permute_scales).
+__device__ __forceinline__ void compute_step(const WeightRegs &w, uint32_t sc,
+                                             const uint8_t *xb, int r16, int kb, float scale2,
+                                             f32x4_t &acc) {
   const uint8_t *brow = xb + r16 * kLdsRowBytes + 64 * kb;
-  // Scale codes of groups 2kb, 2kb+1 (first 32 k) and 8+2kb, 9+2kb (second 32 k).
   float d[4];
-  moe::e4m3x2_to_f32(w.sa, d[0], d[1]);
-  moe::e4m3x2_to_f32(w.sb, d[2], d[3]);
+  moe::e4m3x2_to_f32(sc, d[0], d[1]);
+  moe::e4m3x2_to_f32_hi(sc, d[2], d[3]);
   moe::Fp4Block blk[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) blk[g] = moe::make_block(d[g], scale2);
@@ -141,6 +155,7 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
     const int32_t *__restrict__ offsets, uint16_t *__restrict__ c, int64_t ldc,
     int32_t max_rows, int32_t N, int32_t K) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kLdsBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
 
   const int e = blockIdx.y;
   const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_ptrs[e]);
@@ -151,59 +166,82 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
   const uint8_t *scales = reinterpret_cast<const uint8_t *>(scale_ptrs[e]);
   const float scale2 = scale2s[e];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r16 = lane & 15, kb = lane >> 4;
   const int n_wave0 = blockIdx.x * kBlockN + wave * kRowsPerWave;
   const bool wave_on = n_wave0 < N;  // N % 16 == 0: a wave's 16 rows are all in or all out
-  const int n_row = wave_on ? n_wave0 + r16 : 0;
-  const uint8_t *wrow = packed + static_cast<size_t>(n_row) * (K / 2);
-  const uint8_t *srow = scales + static_cast<size_t>(n_row) * (K / 16);
+  const uint32_t row_bytes = static_cast<uint32_t>(K) / 2, srow_bytes = static_cast<uint32_t>(K) / 16;
   const int n_steps = K / kChunkK;
-  // this thread's staging piece: row piece_row of the pass, k [8 piece_col, +8) of a step
+  const int n_stages = (n_steps + kStageSteps - 1) / kStageSteps;
+
+  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(packed, static_cast<uint32_t>(N) * row_bytes);
+  const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(scales, static_cast<uint32_t>(N) * srow_bytes);
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      make_rsrc(a, static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(lda) * 2u);
+
+  // This lane's weight row (row 0 for a wave past N: loaded, never used).
+  const uint32_t w_voff = static_cast<uint32_t>(wave_on ? n_wave0 + r16 : 0) * row_bytes + 16u * kb;
+  // Scale staging: thread -> (block row, step within the stage); 64 contiguous bytes per row.
+  const int s_row = blockIdx.x * kBlockN + (tid >> 2), s_sub = tid & 3;
+  const uint32_t s_voff = static_cast<uint32_t>(s_row < N ? s_row : 0) * srow_bytes;
+  const int s_lds = (tid >> 2) * kScaleRowBytes + s_sub * 16;
+  const auto scale_off = [&](int stage) {
+    return s_voff + static_cast<uint32_t>(min(stage * kStageSteps + s_sub, n_steps - 1)) * 16u;
+  };
+  // This lane's scale dword within a staged block: row of the wave's 16, lane's kb.
+  const int s_read = (wave * kRowsPerWave + r16) * kScaleRowBytes + 4 * kb;
+  // Activation staging: thread -> (row of the pass, 16-byte piece of a step).
   const int piece_row = tid / kPiecesPerRow, piece_col = tid % kPiecesPerRow;
   const int lds_off = piece_row * kLdsRowBytes + piece_col * 16;
 
   for (int m0 = lo; m0 < hi; m0 += kBlockM) {
     const int m_cnt = min(kBlockM, hi - m0);
-    const uint16_t *xsrc = nullptr;  // rows past the pass are not staged: their output
-    if (piece_row < m_cnt) {         // columns are never stored
-      const int s = m0 + piece_row;
-      const int g = gather != nullptr ? gather[s] : s;
-      if (g >= 0 && g < a_rows) xsrc = a + static_cast<size_t>(g) * lda + piece_col * 8;
+    // Rows past the pass and out-of-range gather indices read zeros (offset past the end).
+    int g = -1;
+    if (piece_row < m_cnt) {
+      const int srow = m0 + piece_row;
+      g = gather != nullptr ? gather[srow] : srow;
     }
-    const bool stage = piece_row < m_cnt;
+    const uint32_t x_voff = (g >= 0 && g < a_rows)
+                                ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) +
+                                   piece_col * 8u) * 2u
+                                : 0x80000000u;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    WeightRegs w0, w1, w2;
-    if (wave_on) {
-      load_weights(w0, wrow, srow, 0, kb);
-      if (n_steps > 1) load_weights(w1, wrow, srow, 1, kb);
-    }
-    if (stage) {
-      const u32x4_t v = xsrc != nullptr ? *reinterpret_cast<const u32x4_t *>(xsrc)
-                                        : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t *>(xs[0] + lds_off) = permute_k8(v);
-    }
+    WeightRegs w0, w1, w2, w3;
+    load_weights(w0, w_rsrc, w_voff, 0);
+    load_weights(w1, w_rsrc, w_voff, min(1, n_steps - 1));
+    load_weights(w2, w_rsrc, w_voff, min(2, n_steps - 1));
+    *reinterpret_cast<u32x4_t *>(ss[0] + s_lds) = permute_scales(load16(s_rsrc, scale_off(0), 0));
+    *reinterpret_cast<u32x4_t *>(xs[0] + lds_off) = permute_k8(load16(x_rsrc, x_voff, 0));
     __syncthreads();
 
-    // One step: stage the next activation chunk, prefetch the weights two steps ahead,
-    // compute this step, publish the staged chunk.
-    auto run_step = [&](int step, WeightRegs &cur, WeightRegs &ahead) {
-      const bool more = step + 1 < n_steps;
-      u32x4_t xv = {0u, 0u, 0u, 0u};
-      if (more && xsrc != nullptr)
-        xv = *reinterpret_cast<const u32x4_t *>(xsrc + (step + 1) * kChunkK);
+    // Steps of one scale stage, weights prefetched three steps ahead in a four-slot ring.
+    // Every load here is unconditional (clamped indices): a load behind a branch leaves
+    // the wait counters unknown at the join, and the compiler then drains all of them.
+    u32x4_t sc_next;
+    auto run_step = [&](int q, int i, WeightRegs &cur, WeightRegs &ahead) {
+      const int step = q * kStageSteps + i;
+      if (i == 0) sc_next = load16(s_rsrc, scale_off(q + 1), 0);
+      const u32x4_t xv = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(step + 1, n_steps - 1)) *
+                                                    (kChunkK * 2));
+      load_weights(ahead, w_rsrc, w_voff, min(step + 3, n_steps - 1));
       if (wave_on) {
-        if (step + 2 < n_steps) load_weights(ahead, wrow, srow, step + 2, kb);
-        compute_step(cur, xs[step & 1], r16, kb, scale2, acc);
+        const uint32_t sc = *reinterpret_cast<const uint32_t *>(ss[q & 1] + s_read + 16 * i);
+        compute_step(cur, sc, xs[step & 1], r16, kb, scale2, acc);
       }
-      if (more && stage) *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xv);
+      *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xv);
+      if (i == kStageSteps - 1)
+        *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds) = permute_scales(sc_next);
       __syncthreads();
     };
-    for (int step = 0; step < n_steps; step += 3) {
-      run_step(step, w0, w2);
-      if (step + 1 < n_steps) run_step(step + 1, w1, w0);
-      if (step + 2 < n_steps) run_step(step + 2, w2, w1);
+    for (int q = 0; q < n_stages; ++q) {
+      const int s0 = q * kStageSteps;
+      run_step(q, 0, w0, w3);
+      if (s0 + 1 < n_steps) run_step(q, 1, w1, w0);
+      if (s0 + 2 < n_steps) run_step(q, 2, w2, w1);
+      if (s0 + 3 < n_steps) run_step(q, 3, w3, w2);
     }
 
     // acc[i] = result for weight row n_wave0 + 4 kb + i and sorted row m0 + r16.
@@ -272,6 +310,13 @@ extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_
   MOE_REQUIRE(moe::aligned16(a) && moe::aligned16(c),
               "grouped_gemm: a and c must be 16-byte aligned");
   if (max_rows == 0) return MOE_OK;
+  MOE_REQUIRE(a_rows >= 1, "grouped_gemm: a_rows must be >= 1 when max_rows > 0");
+  // Buffer offsets are 32-bit: activations below 2 GiB, one expert's packed weights
+  // below 4 GiB.
+  MOE_REQUIRE(static_cast<uint64_t>(a_rows) * lda * 2 < (1ull << 31),
+              "grouped_gemm: the activation buffer must be smaller than 2 GiB");
+  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 32),
+              "grouped_gemm: one expert's packed weights must be smaller than 4 GiB");
   const dim3 grid((n + kBlockN - 1) / kBlockN, num_experts);
   return moe::launch("moe_w4a16_grouped_gemm", grouped_gemm_kernel, grid, dim3(kThreads), 0,
                      stream, a, lda, a_rows, a_gather, packed_ptrs, scale_ptrs, scale2,

@@ -51,6 +51,14 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t codes, float &d0, float &
   d1 = v[1];
 }
 
+// Two E4M3 codes in the high 16 bits of `codes` -> FP32 (exact).
+__device__ __forceinline__ void e4m3x2_to_f32_hi(uint32_t codes, float &d0, float &d1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes), true);
+  d0 = v[0];
+  d1 = v[1];
+}
+
 struct Fp4Block {
   uint32_t lo03, lo47;  // low bytes of the 8 BF16 magnitudes (codes 0-3, 4-7)
   uint32_t hi03, hi47;  // high bytes

@@ -120,9 +120,9 @@ int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_
  *
  * Requirements (else MOE_EINVAL): n > 0 and n % 16 == 0; k > 0 and k % 256 == 0;
  * lda >= k and ldc >= n, both multiples of 8; a and c 16-byte aligned; num_experts >= 1;
- * max_rows >= 0, a_rows >= 0; a, packed_ptrs, scale_ptrs, scale2, expert_offsets and c
- * non-NULL. Each table address must be 16-byte aligned (not checked: device data).
- * max_rows == 0 enqueues nothing.
+ * max_rows >= 0; a_rows >= 1 when max_rows > 0; a, packed_ptrs, scale_ptrs, scale2,
+ * expert_offsets and c non-NULL. Each table address must be 16-byte aligned (not checked:
+ * device data). max_rows == 0 enqueues nothing.
  */
 int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
                            const int32_t *a_gather, const uint64_t *packed_ptrs,
