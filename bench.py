@@ -29,12 +29,47 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+# Counter-measured HBM traffic of the gate_up GEMM, valid only for the kernel source it
+# was measured on (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated with a copy kernel).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_prefill_subchunk_hbm_traffic.md")
+KERNEL_SOURCES = ("grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip",
+                  "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h")
 METRIC = "grouped MoE W4A16 GEMM: HBM GB/s on unique weights + TFLOP/s, 256-row prefill"
 
 
 def proj_bytes(n: int, k: int) -> int:
     """HBM bytes of one expert's NVFP4 projection: packed nibbles, E4M3 scales, scale2."""
     return n * k // 2 + n * k // 16 + 4
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate_up launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith("- `"):
+            key, _, val = line.strip()[3:].partition("`:")
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -235,7 +270,7 @@ def main():
     achieved = float(np.mean(gu_alg) / np.mean(gu_s) / 1e9)
     roofline = {"kernel": "moe_w4a16_grouped_gemm (gate_up)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "avg_launch_us": round(float(np.mean(gu_s)) * 1e6, 2),
                 "alg_bytes_per_launch": int(np.mean(gu_alg))}
 
