@@ -44,11 +44,11 @@ constexpr int kBlockM = 16;                       // sorted rows per pass: one M
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
-constexpr int kStageSteps = 4;                    // steps per staged block of scales
-constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 4 steps x 16 scale bytes, padded
+constexpr int kStageSteps = 8;  // steps per staged block of scales: 128 bytes, a whole line
+constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 8 steps x 16 scale bytes, padded
 constexpr int kScaleBufBytes = kBlockN * kScaleRowBytes;
 static_assert(kBlockM * kPiecesPerRow == kThreads, "one activation piece per thread");
-static_assert(kBlockN * kStageSteps == kThreads, "one scale piece per thread");
+static_assert(kBlockN * kStageSteps == 2 * kThreads, "two scale pieces per thread");
 
 // Raw buffer access (gfx9 resource word 3): offsets past num_records read as zero
 // without touching memory, which masks padded and invalid rows at no cost.
@@ -126,25 +126,51 @@ __device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Block
 
 // Decode this lane's 64 weights of the step and multiply them into acc against the
 // staged activation tile `xb` (rows = sorted rows of the pass, k permuted by 8s).
-// `sc` holds the lane's four scale codes (see permute_scales).
+// `sc` holds the lane's four scale codes (see permute_scales); `lut` maps a scale code to
+// the byte tables of its block (code_table_lut).
 __device__ __forceinline__ void compute_step(const WeightRegs &w, uint32_t sc,
-                                             const uint8_t *xb, int r16, int kb, float scale2,
-                                             f32x4_t &acc) {
+                                             const uint8_t *xb, const uint8_t *lut, int r16,
+                                             int kb, float scale2, f32x4_t &acc) {
   const uint8_t *brow = xb + r16 * kLdsRowBytes + 64 * kb;
-  float d[4];
-  moe::e4m3x2_to_f32(sc, d[0], d[1]);
-  moe::e4m3x2_to_f32_hi(sc, d[2], d[3]);
   moe::Fp4Block blk[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) blk[g] = moe::make_block(d[g], scale2);
+  for (int g = 0; g < 4; ++g) {
+    const u32x4_t t =
+        *reinterpret_cast<const u32x4_t *>(lut + (((sc >> (8 * g)) & 0xFFu) << 4));
+    blk[g].lo03 = t[0];
+    blk[g].lo47 = t[1];
+    blk[g].hi03 = t[2];
+    blk[g].hi47 = t[3];
+  }
+  // Byte 0 of lo03 (the table entry of magnitude 0) is zero exactly for codes whose
+  // byte tables are valid; the LUT marks the others there.
+  const bool lane_fast = ((blk[0].lo03 | blk[1].lo03 | blk[2].lo03 | blk[3].lo03) & 0xFFu) == 0;
   const uint32_t wa[4] = {w.a[0], w.a[1], w.a[2], w.a[3]};
   const uint32_t wb[4] = {w.b[0], w.b[1], w.b[2], w.b[3]};
-  if (__all(moe::fast_pq4(blk[0].pq, blk[1].pq, blk[2].pq, blk[3].pq))) {
+  if (__all(lane_fast)) {
     mfma4<true>(wa, blk[0], blk[1], brow, scale2, acc);
     mfma4<true>(wb, blk[2], blk[3], brow + 256, scale2, acc);
   } else {  // some block of the wave needs the exact per-element path
+    float d[4];
+    moe::e4m3x2_to_f32(sc, d[0], d[1]);
+    moe::e4m3x2_to_f32_hi(sc, d[2], d[3]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) blk[g] = moe::make_block(d[g], scale2);
     mfma4<false>(wa, blk[0], blk[1], brow, scale2, acc);
     mfma4<false>(wb, blk[2], blk[3], brow + 256, scale2, acc);
+  }
+}
+
+// The byte tables of every E4M3 scale code for this expert's scale2, one 16-byte entry
+// per code {lo03, lo47, hi03, hi47}; byte 0 of lo03 is set for codes that must take the
+// exact path. Built once per block by threads 0..255.
+__device__ __forceinline__ void build_code_table_lut(uint8_t *lut, int tid, float scale2) {
+  if (tid < 256) {
+    float d, unused;
+    moe::e4m3x2_to_f32(static_cast<uint32_t>(tid), d, unused);
+    const moe::Fp4Block b = moe::make_block(d, scale2);
+    const u32x4_t t = {b.lo03 | (moe::fast_pq(b.pq) ? 0u : 1u), b.lo47, b.hi03, b.hi47};
+    *reinterpret_cast<u32x4_t *>(lut + tid * 16) = t;
   }
 }
 
@@ -156,6 +182,7 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
     int32_t max_rows, int32_t N, int32_t K) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kLdsBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
 
   const int e = blockIdx.y;
   const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_ptrs[e]);
@@ -180,13 +207,17 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
   const __amdgpu_buffer_rsrc_t x_rsrc =
       make_rsrc(a, static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(lda) * 2u);
 
-  // This lane's weight row (row 0 for a wave past N: loaded, never used).
-  const uint32_t w_voff = static_cast<uint32_t>(wave_on ? n_wave0 + r16 : 0) * row_bytes + 16u * kb;
-  // Scale staging: thread -> (block row, step within the stage); 64 contiguous bytes per row.
-  const int s_row = blockIdx.x * kBlockN + (tid >> 2), s_sub = tid & 3;
-  const uint32_t s_voff = static_cast<uint32_t>(s_row < N ? s_row : 0) * srow_bytes;
-  const int s_lds = (tid >> 2) * kScaleRowBytes + s_sub * 16;
-  const auto scale_off = [&](int stage) {
+  // This lane's weight row. Rows past N lie past the buffer end and read zeros.
+  const uint32_t w_voff = static_cast<uint32_t>(n_wave0 + r16) * row_bytes + 16u * kb;
+  // Scale staging: thread -> rows (tid / 8) and 64 + (tid / 8) of the block, step tid % 8
+  // of the stage; eight threads read a row's 128 contiguous bytes.
+  // Rows past N lie past the buffer end and read zeros.
+  const int s_sub = tid & 7;
+  const uint32_t s_voff = static_cast<uint32_t>(blockIdx.x * kBlockN + (tid >> 3)) * srow_bytes;
+  const uint32_t s_half = (kBlockN / 2) * srow_bytes;  // second row: scalar offset
+  const int s_lds = (tid >> 3) * kScaleRowBytes + s_sub * 16;
+  constexpr int kScaleHalfLds = (kBlockN / 2) * kScaleRowBytes;
+  const auto scale_voff = [&](int stage) {
     return s_voff + static_cast<uint32_t>(min(stage * kStageSteps + s_sub, n_steps - 1)) * 16u;
   };
   // This lane's scale dword within a staged block: row of the wave's 16, lane's kb.
@@ -194,6 +225,7 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
   // Activation staging: thread -> (row of the pass, 16-byte piece of a step).
   const int piece_row = tid / kPiecesPerRow, piece_col = tid % kPiecesPerRow;
   const int lds_off = piece_row * kLdsRowBytes + piece_col * 16;
+  build_code_table_lut(lut, tid, scale2);  // published by the first pass's barrier
 
   for (int m0 = lo; m0 < hi; m0 += kBlockM) {
     const int m_cnt = min(kBlockM, hi - m0);
@@ -213,27 +245,37 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
     load_weights(w0, w_rsrc, w_voff, 0);
     load_weights(w1, w_rsrc, w_voff, min(1, n_steps - 1));
     load_weights(w2, w_rsrc, w_voff, min(2, n_steps - 1));
-    *reinterpret_cast<u32x4_t *>(ss[0] + s_lds) = permute_scales(load16(s_rsrc, scale_off(0), 0));
+    *reinterpret_cast<u32x4_t *>(ss[0] + s_lds) =
+        permute_scales(load16(s_rsrc, scale_voff(0), 0));
+    *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + kScaleHalfLds) =
+        permute_scales(load16(s_rsrc, scale_voff(0), s_half));
     *reinterpret_cast<u32x4_t *>(xs[0] + lds_off) = permute_k8(load16(x_rsrc, x_voff, 0));
     __syncthreads();
 
     // Steps of one scale stage, weights prefetched three steps ahead in a four-slot ring.
     // Every load here is unconditional (clamped indices): a load behind a branch leaves
     // the wait counters unknown at the join, and the compiler then drains all of them.
-    u32x4_t sc_next;
+    u32x4_t sc_next0, sc_next1;
     auto run_step = [&](int q, int i, WeightRegs &cur, WeightRegs &ahead) {
       const int step = q * kStageSteps + i;
-      if (i == 0) sc_next = load16(s_rsrc, scale_off(q + 1), 0);
+      if (i == 0) {
+        sc_next0 = load16(s_rsrc, scale_voff(q + 1), 0);
+        sc_next1 = load16(s_rsrc, scale_voff(q + 1), s_half);
+      }
       const u32x4_t xv = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(step + 1, n_steps - 1)) *
                                                     (kChunkK * 2));
       load_weights(ahead, w_rsrc, w_voff, min(step + 3, n_steps - 1));
       if (wave_on) {
         const uint32_t sc = *reinterpret_cast<const uint32_t *>(ss[q & 1] + s_read + 16 * i);
-        compute_step(cur, sc, xs[step & 1], r16, kb, scale2, acc);
+        compute_step(cur, sc, xs[step & 1], lut, r16, kb, scale2, acc);
       }
       *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xv);
-      if (i == kStageSteps - 1)
-        *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds) = permute_scales(sc_next);
+      // The next stage's buffer was last read in the previous stage: fill it mid-stage.
+      if (i == 3) {
+        *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds) = permute_scales(sc_next0);
+        *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds + kScaleHalfLds) =
+            permute_scales(sc_next1);
+      }
       __syncthreads();
     };
     for (int q = 0; q < n_stages; ++q) {
@@ -242,6 +284,10 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
       if (s0 + 1 < n_steps) run_step(q, 1, w1, w0);
       if (s0 + 2 < n_steps) run_step(q, 2, w2, w1);
       if (s0 + 3 < n_steps) run_step(q, 3, w3, w2);
+      if (s0 + 4 < n_steps) run_step(q, 4, w0, w3);
+      if (s0 + 5 < n_steps) run_step(q, 5, w1, w0);
+      if (s0 + 6 < n_steps) run_step(q, 6, w2, w1);
+      if (s0 + 7 < n_steps) run_step(q, 7, w3, w2);
     }
 
     // acc[i] = result for weight row n_wave0 + 4 kb + i and sorted row m0 + r16.
