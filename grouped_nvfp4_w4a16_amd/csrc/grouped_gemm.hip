@@ -15,15 +15,20 @@
 //     sorted rows 16 at a time (one MFMA tile), so its weight bytes are streamed once per
 //     16 rows (once per launch for an expert with at most 16 routed rows).
 //   - The weights are the MFMA A operand (v_mfma_f32_16x16x32_bf16, M = 16 weight rows):
-//     each lane loads 2 x 16 bytes of packed nibbles (64 k of one row) plus the row's 16
-//     scale bytes per 256-k step with 128-bit global loads, two steps ahead in a
-//     three-slot register ring, and decodes them in registers (nvfp4_decode.h) straight
-//     into A; no dequantised weight goes through LDS. The decode takes a wave-uniform
-//     branch: the byte-table path when every block of the wave allows it, else the exact
-//     per-element path.
+//     each lane reads 2 x 16 bytes of packed nibbles (64 k of one row) per 256-k step with
+//     raw buffer loads (16 rows x 64 contiguous bytes per wave instruction), one step
+//     ahead in a two-slot register ring, and decodes them in registers (nvfp4_decode.h)
+//     straight into A; no dequantised weight goes through LDS. The L1 can track only a
+//     step's worth of a CU's weight lines, so a deeper ring only leaves waves stalled at
+//     load issue instead of decoding; one step of lead time covers the latency. The
+//     decode takes a wave-uniform branch: the byte-table path when every block of the
+//     wave allows it, else the exact per-element path.
 //   - The gathered activation rows are the B operand (16 rows per MFMA tile). They are
-//     staged per 256-k step in LDS (double buffered, one barrier per step), shared by the
-//     8 waves, with k permuted inside each group of 8 to match the decoder's order.
+//     loaded four steps ahead into a register ring and staged per 256-k step in LDS
+//     (double buffered, one barrier per step), shared by the 8 waves, with k permuted
+//     inside each group of 8 to match the decoder's order.
+//   - Block scales are staged in LDS 8 steps (a whole 128-byte line per row) at a time;
+//     each block turns every E4M3 code into its decode tables once (a 256-entry LUT).
 //   - Output: each lane holds 4 consecutive weight rows of one sorted row -> one 8-byte
 //     store of BF16 (round-to-nearest-even).
 #include "common.h"
@@ -214,7 +219,9 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
   // Rows past N lie past the buffer end and read zeros.
   const int s_sub = tid & 7;
   const uint32_t s_voff = static_cast<uint32_t>(blockIdx.x * kBlockN + (tid >> 3)) * srow_bytes;
-  const uint32_t s_half = (kBlockN / 2) * srow_bytes;  // second row: scalar offset
+  // Second row of the thread. Every row offset goes into the vector offset: the buffer
+  // range check covers the vector offset, not the scalar one, so rows past N read zeros.
+  const uint32_t s_half = (kBlockN / 2) * srow_bytes;
   const int s_lds = (tid >> 3) * kScaleRowBytes + s_sub * 16;
   constexpr int kScaleHalfLds = (kBlockN / 2) * kScaleRowBytes;
   const auto scale_voff = [&](int stage) {
@@ -241,18 +248,22 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
                                 : 0x80000000u;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    WeightRegs w0, w1, w2, w3;
+    WeightRegs w0, w1;
     load_weights(w0, w_rsrc, w_voff, 0);
-    load_weights(w1, w_rsrc, w_voff, min(1, n_steps - 1));
-    load_weights(w2, w_rsrc, w_voff, min(2, n_steps - 1));
     *reinterpret_cast<u32x4_t *>(ss[0] + s_lds) =
         permute_scales(load16(s_rsrc, scale_voff(0), 0));
     *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + kScaleHalfLds) =
-        permute_scales(load16(s_rsrc, scale_voff(0), s_half));
+        permute_scales(load16(s_rsrc, scale_voff(0) + s_half, 0));
     *reinterpret_cast<u32x4_t *>(xs[0] + lds_off) = permute_k8(load16(x_rsrc, x_voff, 0));
+    // Activation chunks are prefetched kXAhead steps ahead in a register ring.
+    constexpr int kXAhead = 4;
+    u32x4_t xr[kXAhead];
+#pragma unroll
+    for (int d = 1; d < kXAhead; ++d)
+      xr[d] = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(d, n_steps - 1)) * (kChunkK * 2));
     __syncthreads();
 
-    // Steps of one scale stage, weights prefetched three steps ahead in a four-slot ring.
+    // Steps of one scale stage, weights prefetched one step ahead in a two-slot ring.
     // Every load here is unconditional (clamped indices): a load behind a branch leaves
     // the wait counters unknown at the join, and the compiler then drains all of them.
     u32x4_t sc_next0, sc_next1;
@@ -260,16 +271,16 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
       const int step = q * kStageSteps + i;
       if (i == 0) {
         sc_next0 = load16(s_rsrc, scale_voff(q + 1), 0);
-        sc_next1 = load16(s_rsrc, scale_voff(q + 1), s_half);
+        sc_next1 = load16(s_rsrc, scale_voff(q + 1) + s_half, 0);
       }
-      const u32x4_t xv = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(step + 1, n_steps - 1)) *
-                                                    (kChunkK * 2));
-      load_weights(ahead, w_rsrc, w_voff, min(step + 3, n_steps - 1));
+      xr[i % kXAhead] = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(step + kXAhead, n_steps - 1)) *
+                                                  (kChunkK * 2));
+      load_weights(ahead, w_rsrc, w_voff, min(step + 1, n_steps - 1));
       if (wave_on) {
         const uint32_t sc = *reinterpret_cast<const uint32_t *>(ss[q & 1] + s_read + 16 * i);
         compute_step(cur, sc, xs[step & 1], lut, r16, kb, scale2, acc);
       }
-      *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xv);
+      *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xr[(i + 1) % kXAhead]);
       // The next stage's buffer was last read in the previous stage: fill it mid-stage.
       if (i == 3) {
         *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds) = permute_scales(sc_next0);
@@ -280,14 +291,14 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
     };
     for (int q = 0; q < n_stages; ++q) {
       const int s0 = q * kStageSteps;
-      run_step(q, 0, w0, w3);
+      run_step(q, 0, w0, w1);
       if (s0 + 1 < n_steps) run_step(q, 1, w1, w0);
-      if (s0 + 2 < n_steps) run_step(q, 2, w2, w1);
-      if (s0 + 3 < n_steps) run_step(q, 3, w3, w2);
-      if (s0 + 4 < n_steps) run_step(q, 4, w0, w3);
+      if (s0 + 2 < n_steps) run_step(q, 2, w0, w1);
+      if (s0 + 3 < n_steps) run_step(q, 3, w1, w0);
+      if (s0 + 4 < n_steps) run_step(q, 4, w0, w1);
       if (s0 + 5 < n_steps) run_step(q, 5, w1, w0);
-      if (s0 + 6 < n_steps) run_step(q, 6, w2, w1);
-      if (s0 + 7 < n_steps) run_step(q, 7, w3, w2);
+      if (s0 + 6 < n_steps) run_step(q, 6, w0, w1);
+      if (s0 + 7 < n_steps) run_step(q, 7, w1, w0);
     }
 
     // acc[i] = result for weight row n_wave0 + 4 kb + i and sorted row m0 + r16.
