@@ -3,7 +3,9 @@
 One step = one pass of the whole path over one 256-row batch of the prefill sub-chunk
 workload (256 experts, top_k 8, hidden 6144, moe_intermediate 2048, NVFP4 weights):
 moe_align -> zero expert_out -> grouped GEMM gate_up -> swiglu_clamp -> grouped GEMM down
--> moe_combine, all enqueued on one HIP stream with every input already in HBM.
+-> moe_combine, all enqueued on one HIP stream with every input already in HBM. The zeroing
+runs only when the down table has null entries (otherwise every row the combine reads is
+written by the down GEMM).
 
 Prints ONE JSON line. ``value`` is HBM GB/s on the unique expert-weight bytes the step
 reads (experts touched by the batch, both projections) divided by the step time;
@@ -212,6 +214,7 @@ def main():
                             + slots_live * n_gu * 2 + (w.num_experts + 1) * 4 + rows * w.top_k * 4)
 
     stream = torch.cuda.current_stream()
+    need_zero = not all(dt.present)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
 
     def step(i, events=None):
@@ -224,7 +227,8 @@ def main():
         hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
                       ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
         rec(1)
-        ws.expert_out[:s].zero_()
+        if need_zero:  # null down entries: their rows must read as zero in the combine
+            ws.expert_out[:s].zero_()
         rec(2)
         hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
                                    max_rows=s)

@@ -296,12 +296,15 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     """One routed MoE layer over the rows of ``x``, all on the device, in the order of the
     grouped-prefill arm: align -> zero expert_out -> grouped GEMM gate_up (rows gathered
     through sorted_token_ids) -> SwiGLU clamp -> grouped GEMM down -> indexed combine.
-    ``ws.expert_out`` is zeroed first so experts that are not present add zero."""
+    ``ws.expert_out`` is zeroed first so experts that are not present add zero. When every
+    down-projection entry is present the down GEMM writes every row the combine reads
+    (each valid slot's row lies in its expert's segment), so the zeroing is skipped."""
     rows, top_k = topk_ids.shape
     s = rows * top_k
     moe_align(topk_ids, gate_up.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
               ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters, stream)
-    ws.expert_out[:s].zero_()
+    if not all(down.present):
+        ws.expert_out[:s].zero_()
     mi = moe_intermediate
     moe_w4a16_grouped_gemm(x, gate_up, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
                            max_rows=s, stream=stream)

@@ -7,20 +7,34 @@
 // token_to_perm maps a slot to its sorted row.
 //
 // Design (gfx950, wave64): the slots are split into 16 contiguous ranges, one per wave.
-//   1. Each wave counts its range into a private LDS histogram (LDS atomics; counts do
-//      not depend on order).
+//   1. Each wave counts its range into a private LDS histogram: per chunk of 64 slots,
+//      the lowest lane of each group of equal ids adds the group's size.
 //   2. Per expert, the 16 per-wave counts become per-wave starting positions; a block
 //      scan over experts gives expert_offsets (and the active-expert list).
-//   3. Each wave walks its range again in order, 64 slots at a time. Lanes holding the
-//      same expert id are grouped with a ballot; a lane's rank in its group is the
-//      number of lower lanes in it, so positions follow slot order: the sort is stable
-//      and the result is deterministic (no atomics decide an order).
+//   3. Each wave walks its range again in order, 64 slots at a time. The lanes holding
+//      the same expert id are found with one ballot per id bit; a lane's rank in its
+//      group is the number of lower lanes in it, so positions follow slot order: the
+//      sort is stable and the result is deterministic (no atomics decide an order).
+//      The group's lowest lane advances the wave's running position of that expert.
+//   The first two chunks of 64 ids of a wave stay in registers between passes 1 and 3.
 #include "common.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+
+// Lanes of the wave whose valid id equals this lane's: one ballot per id bit.
+// `bits` (wave-uniform) covers every valid id.
+__device__ inline uint64_t same_id_lanes(int id, bool valid, int bits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (id >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    m &= bit ? ones : ~ones;
+  }
+  return valid ? m : 0ull;
+}
 
 __device__ inline int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -74,14 +88,22 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
   const int end = min(begin + per_wave, n_slots);
   int *my_hist = hist + wave * E;
 
-  // 1. per-wave histograms
+  const int bits = E > 1 ? 32 - __clz(E - 1) : 1;
+  const uint64_t lower = (1ull << lane) - 1ull;
+
+  // 1. per-wave histograms: each group's lowest lane adds the group size (the groups of
+  //    a chunk have distinct ids, so the updates do not collide).
+  int cache0 = -1, cache1 = -1;
   int invalid = 0;
-  for (int base = begin; base < end; base += 64) {
+  for (int c = 0, base = begin; base < end; ++c, base += 64) {
     const int t = base + lane;
     const bool in = t < end;
     const int id = in ? ids[t] : -1;
+    if (c == 0) cache0 = id;
+    if (c == 1) cache1 = id;
     const bool valid = in && id >= 0 && id < E;
-    if (valid) atomicAdd(&my_hist[id], 1);
+    const uint64_t grp = same_id_lanes(id, valid, bits);
+    if (valid && (grp & lower) == 0) my_hist[id] += __popcll(grp);
     invalid += __popcll(__ballot(in && !valid));
   }
   if (lane == 0 && invalid) atomicAdd(n_invalid, invalid);
@@ -123,22 +145,17 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
   __syncthreads();
 
   // 3. stable scatter
-  for (int base = begin; base < end; base += 64) {
+  for (int c = 0, base = begin; base < end; ++c, base += 64) {
     const int t = base + lane;
     const bool in = t < end;
-    const int id = in ? ids[t] : -1;
+    const int id = c == 0 ? cache0 : c == 1 ? cache1 : (in ? ids[t] : -1);
     const bool valid = in && id >= 0 && id < E;
+    const uint64_t grp = same_id_lanes(id, valid, bits);
     int pos = -1;
-    uint64_t todo = __ballot(valid);
-    while (todo != 0) {
-      const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
-      const int lid = __shfl(id, leader, 64);
-      const bool mine = valid && id == lid;
-      const uint64_t grp = __ballot(mine);
-      const int start = my_hist[lid];
-      if (mine) pos = start + __popcll(grp & ((1ull << lane) - 1ull));
-      if (lane == leader) my_hist[lid] = start + __popcll(grp);
-      todo &= ~grp;
+    if (valid) {
+      const int start = my_hist[id];  // read by every lane of the group first
+      pos = start + __popcll(grp & lower);
+      if ((grp & lower) == 0) my_hist[id] = start + __popcll(grp);
     }
     if (in) {
       token_to_perm[t] = pos;

@@ -79,6 +79,10 @@ def _layer_inputs(w: wl.Workload, rows=None):
 def _run_layer(hip, w, ids, wts, x_bits, gu_table, dn_table):
     rows, top_k = ids.shape
     ws = hip.Workspace(rows, top_k, w.num_experts, w.hidden, w.moe_intermediate)
+    # NaN in every intermediate buffer: a row the path reads without writing it first
+    # (or without the zeroing that null entries need) poisons the output.
+    for t in (ws.gate_up, ws.act, ws.expert_out):
+        t.view(torch.int16).fill_(-1)
     out = torch.empty((rows, w.hidden), dtype=torch.bfloat16, device="cuda")
     hip.moe_layer(bf16_dev(x_bits), dev(ids), dev(wts), gu_table, dn_table,
                   w.moe_intermediate, w.limit, ws, out)
