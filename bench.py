@@ -2,7 +2,8 @@
 
 One step = one pass of the whole path over one 256-row batch of the prefill sub-chunk
 workload (256 experts, top_k 8, hidden 6144, moe_intermediate 2048, NVFP4 weights):
-moe_align -> zero expert_out -> grouped GEMM gate_up -> swiglu_clamp -> grouped GEMM down
+moe_align -> zero expert_out -> grouped GEMM gate_up with the SwiGLU clamp fused into its
+epilogue (``--unfused``: the GEMM and swiglu_clamp as two calls) -> grouped GEMM down
 -> moe_combine, all enqueued on one HIP stream with every input already in HBM. The zeroing
 runs only when the down table has null entries (otherwise every row the combine reads is
 written by the down GEMM).
@@ -14,7 +15,7 @@ grouped GEMM), timed with HIP events on the stream it runs on. ``cpu_baseline`` 
 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--copy-probe]
+                       [--no-cpu-baseline] [--copy-probe] [--unfused]
 """
 
 from __future__ import annotations
@@ -35,7 +36,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # was measured on (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated with a copy kernel).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_prefill_subchunk_hbm_traffic.md")
 KERNEL_SOURCES = ("grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip",
-                  "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h")
+                  "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h",
+                  "grouped_nvfp4_w4a16_amd/csrc/swiglu.h")
 METRIC = "grouped MoE W4A16 GEMM: HBM GB/s on unique weights + TFLOP/s, 256-row prefill"
 
 
@@ -83,6 +85,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the gate_up GEMM and swiglu_clamp as two calls")
     return ap.parse_args()
 
 
@@ -200,6 +204,7 @@ def main():
     n_gu, k_gu = wl.gate_up_shape(w)
     n_dn, k_dn = wl.down_shape(w)
     step_bytes, step_flops, gu_bytes_alg = [], [], []
+    gu_w, dn_w, gu_fl, dn_fl = [], [], [], []
     for c in range(n_chunks):
         ids_c = ids_host[c * rows:(c + 1) * rows]
         cnt = np.bincount(ids_c.reshape(-1), minlength=w.num_experts)
@@ -208,38 +213,71 @@ def main():
         wb = len(live) * (proj_bytes(n_gu, k_gu) + proj_bytes(n_dn, k_dn))
         step_bytes.append(wb)
         step_flops.append(2.0 * slots_live * (n_gu * k_gu + n_dn * k_dn))
+        gu_w.append(len(live) * proj_bytes(n_gu, k_gu))
+        dn_w.append(len(live) * proj_bytes(n_dn, k_dn))
+        gu_fl.append(2.0 * slots_live * n_gu * k_gu)
+        dn_fl.append(2.0 * slots_live * n_dn * k_dn)
         # gate_up launch, algorithmic bytes: touched weights + the activation rows read
-        # once + the output rows written once + routing metadata
+        # once + the output rows written once (the SwiGLU output when fused, else the
+        # gate_up values) + routing metadata
+        out_cols = n_gu if args.unfused else mi
         gu_bytes_alg.append(len(live) * proj_bytes(n_gu, k_gu) + rows * hidden * 2
-                            + slots_live * n_gu * 2 + (w.num_experts + 1) * 4 + rows * w.top_k * 4)
+                            + slots_live * out_cols * 2 + (w.num_experts + 1) * 4
+                            + rows * w.top_k * 4)
 
     stream = torch.cuda.current_stream()
     need_zero = not all(dt.present)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    s = rows * w.top_k
+
+    # The stages of one step, in order; each is timed with HIP events on the stream.
+    def st_align(x, ids, wts):
+        hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
+                      ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
+
+    def st_zero(x, ids, wts):
+        if need_zero:  # null down entries: their rows must read as zero in the combine
+            ws.expert_out[:s].zero_()
+
+    def st_gate_up(x, ids, wts):
+        hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
+                                   max_rows=s)
+
+    def st_swiglu(x, ids, wts):
+        hip.swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], w.limit)
+
+    def st_gate_up_swiglu(x, ids, wts):
+        hip.moe_w4a16_grouped_gemm_swiglu(x, gt, ws.expert_offsets, ws.act, w.limit,
+                                          ws.sorted_token_ids, max_rows=s)
+
+    def st_down(x, ids, wts):
+        hip.moe_w4a16_grouped_gemm(ws.act, dt, ws.expert_offsets, ws.expert_out, None,
+                                   max_rows=s)
+
+    def st_combine(x, ids, wts):
+        hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out)
+
+    if args.unfused:
+        stages = [("moe_align", st_align), ("zero_expert_out", st_zero),
+                  ("grouped_gemm_gate_up", st_gate_up), ("swiglu_clamp", st_swiglu),
+                  ("grouped_gemm_down", st_down), ("moe_combine", st_combine)]
+    else:
+        stages = [("moe_align", st_align), ("zero_expert_out", st_zero),
+                  ("grouped_gemm_gate_up_swiglu", st_gate_up_swiglu),
+                  ("grouped_gemm_down", st_down), ("moe_combine", st_combine)]
+    gu_name = stages[2][0]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
 
     def step(i, events=None):
         c = i % n_chunks
         sl = slice(c * rows, (c + 1) * rows)
         ids, wts, x = ids_all[sl], wts_all[sl], x_all[sl]
-        s = rows * w.top_k
-        rec = (lambda j: events[j].record(stream)) if events else (lambda j: None)
-        rec(0)
-        hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
-                      ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
-        rec(1)
-        if need_zero:  # null down entries: their rows must read as zero in the combine
-            ws.expert_out[:s].zero_()
-        rec(2)
-        hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
-                                   max_rows=s)
-        rec(3)
-        hip.swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], w.limit)
-        rec(4)
-        hip.moe_w4a16_grouped_gemm(ws.act, dt, ws.expert_offsets, ws.expert_out, None,
-                                   max_rows=s)
-        rec(5)
-        hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out)
-        rec(6)
+        for j, (_, fn) in enumerate(stages):
+            if events:
+                events[j].record(stream)
+            fn(x, ids, wts)
+        if events:
+            events[len(stages)].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -255,12 +293,13 @@ def main():
     gpu_ms = start.elapsed_time(end)
     ms_per_step = gpu_ms / args.steps
 
-    names = ["moe_align", "zero_expert_out", "grouped_gemm_gate_up", "swiglu_clamp",
-             "grouped_gemm_down", "moe_combine"]
+    names = [n for n, _ in stages]
     per = {n: [] for n in names}
+    step_ms = []
     for i in range(args.steps):
         for j, n in enumerate(names):
             per[n].append(ev[i][j].elapsed_time(ev[i][j + 1]))
+        step_ms.append(ev[i][0].elapsed_time(ev[i][len(stages)]))
     kern_us = {n: round(1000.0 * float(np.mean(v)), 2) for n, v in per.items()}
 
     chunk_of = [i % n_chunks for i in range(args.steps)]
@@ -269,10 +308,21 @@ def main():
     value = total_bytes / (gpu_ms / 1000.0) / 1e9
     tflops = total_flops / (gpu_ms / 1000.0) / 1e12
 
-    gu_s = np.array(per["grouped_gemm_gate_up"]) / 1000.0
+    gu_s = np.array(per[gu_name]) / 1000.0
+    dn_s = np.array(per["grouped_gemm_down"]) / 1000.0
     gu_alg = np.array([gu_bytes_alg[c] for c in chunk_of])
     achieved = float(np.mean(gu_alg) / np.mean(gu_s) / 1e9)
-    roofline = {"kernel": "moe_w4a16_grouped_gemm (gate_up)", "bound": "hbm",
+
+    def gemm_line(wb, fl, secs):
+        t = float(np.mean(secs))
+        return {"us": round(t * 1e6, 2),
+                "weight_GBps": round(float(np.mean([wb[c] for c in chunk_of])) / t / 1e9, 1),
+                "TFLOPs": round(float(np.mean([fl[c] for c in chunk_of])) / t / 1e12, 2)}
+
+    per_gemm = {"gate_up": gemm_line(gu_w, gu_fl, gu_s), "down": gemm_line(dn_w, dn_fl, dn_s)}
+    kernel_label = ("moe_w4a16_grouped_gemm (gate_up)" if args.unfused
+                    else "moe_w4a16_grouped_gemm_swiglu (gate_up + SwiGLU)")
+    roofline = {"kernel": kernel_label, "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "avg_launch_us": round(float(np.mean(gu_s)) * 1e6, 2),
@@ -298,6 +348,10 @@ def main():
                    "routing": w.routing, "weight_format": "NVFP4 (E2M1 + E4M3/16 + FP32)",
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
+        "step_ms_p10_p90": [round(float(np.percentile(step_ms, 10)), 4),
+                            round(float(np.percentile(step_ms, 90)), 4)],
+        "gemms": per_gemm,
+        "gate_up_fused_swiglu": not args.unfused,
         "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
         "wall_s": round(wall, 4),
         "kernel_us": kern_us,

@@ -24,7 +24,7 @@ import os
 
 __all__ = [
     "load", "MoeError", "moe_align", "moe_w4a16_grouped_gemm", "swiglu_clamp", "moe_combine",
-    "moe_w4a16_dequant_bf16", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
+    "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a1
 # Every symbol include/moe_w4a16.h declares.
 EXPORTS = (
     "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
-    "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
+    "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
 )
 
 _LIB = None
@@ -48,6 +48,9 @@ _SIGNATURES = {
     "moe_align": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_w4a16_grouped_gemm": (
         [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp],
+        ctypes.c_int),
+    "moe_w4a16_grouped_gemm_swiglu": (
+        [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _f32, _vp],
         ctypes.c_int),
     "swiglu_clamp": ([_vp, _vp, _i64, _vp, _i64, _i32, _i32, _f32, _vp], ctypes.c_int),
     "moe_combine": ([_vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
@@ -173,6 +176,35 @@ def moe_w4a16_grouped_gemm(a, table: "ExpertTable", expert_offsets, c, a_gather=
         table.k, _stream(stream)))
 
 
+def moe_w4a16_grouped_gemm_swiglu(a, table: "ExpertTable", expert_offsets, act, limit: float,
+                                  a_gather=None, max_rows: int | None = None,
+                                  stream=None) -> None:
+    """``act[s] = swiglu_clamp(gate, up)`` of ``a[g(s)] @ W_e^T`` for a fused gate_up table
+    (``table.n = 2 mi``), without storing the gate_up values."""
+    import torch
+
+    if table.n % 2:
+        raise ValueError("the fused gate_up table needs an even n")
+    mi = table.n // 2
+    a, lda = _bf16_matrix(a, "a")
+    act, ld_act = _bf16_matrix(act, "act")
+    _want(expert_offsets, torch.int32, "expert_offsets")
+    _want(a_gather, torch.int32, "a_gather")
+    if expert_offsets.numel() < table.num_experts + 1:
+        raise ValueError("expert_offsets: needs num_experts + 1 elements")
+    rows = act.shape[0] if max_rows is None else max_rows
+    if rows > act.shape[0] or (a_gather is not None and a_gather.numel() < rows):
+        raise ValueError("max_rows exceeds act or a_gather")
+    if a_gather is None and rows > a.shape[0]:
+        raise ValueError("without a_gather, a needs max_rows rows")
+    if a.shape[1] < table.k or act.shape[1] < mi:
+        raise ValueError("a or act too narrow for the table's k, n / 2")
+    _check("moe_w4a16_grouped_gemm_swiglu", load().moe_w4a16_grouped_gemm_swiglu(
+        _p(a), lda, a.shape[0], _p(a_gather), _p(table.packed_ptrs), _p(table.scale_ptrs),
+        _p(table.scale2), _p(expert_offsets), table.num_experts, _p(act), ld_act, rows, mi,
+        table.k, float(limit), _stream(stream)))
+
+
 def swiglu_clamp(gate, up, out, limit: float, stream=None) -> None:
     """``out = silu(min(gate, L)) * clamp(up, -L, L)`` over ``[rows, n]`` views."""
     if gate.shape != up.shape or gate.stride() != up.stride():
@@ -292,10 +324,12 @@ class Workspace:
 
 def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable,
               moe_intermediate: int, limit: float, ws: Workspace, out, shared=None,
-              stream=None) -> None:
+              stream=None, fused: bool = True) -> None:
     """One routed MoE layer over the rows of ``x``, all on the device, in the order of the
     grouped-prefill arm: align -> zero expert_out -> grouped GEMM gate_up (rows gathered
-    through sorted_token_ids) -> SwiGLU clamp -> grouped GEMM down -> indexed combine.
+    through sorted_token_ids) with the SwiGLU clamp fused into its epilogue -> grouped GEMM
+    down -> indexed combine. ``fused=False`` runs the gate_up GEMM and swiglu_clamp as two
+    calls (same bits).
     ``ws.expert_out`` is zeroed first so experts that are not present add zero. When every
     down-projection entry is present the down GEMM writes every row the combine reads
     (each valid slot's row lies in its expert's segment), so the zeroing is skipped."""
@@ -306,9 +340,13 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     if not all(down.present):
         ws.expert_out[:s].zero_()
     mi = moe_intermediate
-    moe_w4a16_grouped_gemm(x, gate_up, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
-                           max_rows=s, stream=stream)
-    swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], limit, stream)
+    if fused:
+        moe_w4a16_grouped_gemm_swiglu(x, gate_up, ws.expert_offsets, ws.act, limit,
+                                      ws.sorted_token_ids, max_rows=s, stream=stream)
+    else:
+        moe_w4a16_grouped_gemm(x, gate_up, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
+                               max_rows=s, stream=stream)
+        swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], limit, stream)
     moe_w4a16_grouped_gemm(ws.act, down, ws.expert_offsets, ws.expert_out, None, max_rows=s,
                            stream=stream)
     moe_combine(ws.expert_out[:s], ws.token_to_perm, topk_weights, out, shared, stream)

@@ -8,6 +8,7 @@
 // Both kernels move 16 bytes (8 BF16) per thread per operand with 128-bit loads and
 // stores and compute in FP32; a block of 256 threads covers 2048 columns of one row.
 #include "common.h"
+#include "swiglu.h"
 
 namespace {
 
@@ -45,11 +46,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_clamp_kernel(
   unpack8(*reinterpret_cast<const uint4 *>(gate + in_off), g);
   unpack8(*reinterpret_cast<const uint4 *>(up + in_off), u);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float gc = fminf(g[i], limit);
-    const float uc = fminf(fmaxf(u[i], -limit), limit);
-    o[i] = gc / (1.0f + __expf(-gc)) * uc;
-  }
+  for (int i = 0; i < 8; ++i) o[i] = moe::swiglu_clamp1(g[i], u[i], limit);
   *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(o);
 }
 

@@ -1,4 +1,5 @@
-// moe_w4a16_grouped_gemm: one launch over all experts of a routed MoE layer.
+// moe_w4a16_grouped_gemm (and its SwiGLU-fused form): one launch over all experts of a
+// routed MoE layer.
 //
 // What it computes follows "Module forward_prefill_gemm": the expert-sorted rows of
 // each expert (expert_offsets prefix sum, rows gathered in-kernel through
@@ -10,29 +11,39 @@
 // HBM once per launch.
 //
 // gfx950 design (the pages' mma.sync/shared-memory tiling is not used):
-//   - grid = (N / 128 weight-row tiles, experts); a block of 8 wave64s owns 128 weight
-//     rows of one expert (16 per wave) over the whole K, and loops over that expert's
-//     sorted rows 16 at a time (one MFMA tile), so its weight bytes are streamed once per
-//     16 rows (once per launch for an expert with at most 16 routed rows).
+//   - grid = (N / 128 weight-row tiles, experts); a block of 4 wave64s owns 128 weight
+//     rows of one expert over the whole K, and loops over that expert's sorted rows 16 at
+//     a time (one MFMA tile), so its weight bytes are streamed once per 16 rows (once per
+//     launch for an expert with at most 16 routed rows). Three blocks share a CU.
+//   - Each wave owns two MFMA tiles of 16 weight rows: block rows [16w, 16w + 16) and
+//     [64 + 16w, 64 + 16w + 16). Both tiles multiply the same activation operands, so a
+//     wave reads each staged activation once per 32 weight rows.
 //   - The weights are the MFMA A operand (v_mfma_f32_16x16x32_bf16, M = 16 weight rows):
-//     each lane reads 2 x 16 bytes of packed nibbles (64 k of one row) per 256-k step with
-//     raw buffer loads (16 rows x 64 contiguous bytes per wave instruction), one step
-//     ahead in a two-slot register ring, and decodes them in registers (nvfp4_decode.h)
-//     straight into A; no dequantised weight goes through LDS. The L1 can track only a
-//     step's worth of a CU's weight lines, so a deeper ring only leaves waves stalled at
-//     load issue instead of decoding; one step of lead time covers the latency. The
-//     decode takes a wave-uniform branch: the byte-table path when every block of the
-//     wave allows it, else the exact per-element path.
+//     each lane reads 2 x 16 bytes of packed nibbles (64 k of one row) per tile and
+//     256-k step with raw buffer loads (16 rows x 64 contiguous bytes per wave
+//     instruction), one step ahead in a two-slot register ring, and decodes them in
+//     registers (nvfp4_decode.h) straight into A; no dequantised weight goes through LDS.
+//     The L1 can track only about a step's worth of a CU's weight lines, so a deeper ring
+//     only leaves waves stalled at load issue instead of decoding. The decode takes a
+//     wave-uniform branch per tile: the byte-table path when every block of the tile
+//     allows it, else the exact per-element path.
 //   - The gathered activation rows are the B operand (16 rows per MFMA tile). They are
-//     loaded four steps ahead into a register ring and staged per 256-k step in LDS
-//     (double buffered, one barrier per step), shared by the 8 waves, with k permuted
+//     loaded two steps ahead into a register ring and staged per 256-k step in LDS
+//     (double buffered, one barrier per step), shared by the 4 waves, with k permuted
 //     inside each group of 8 to match the decoder's order.
-//   - Block scales are staged in LDS 8 steps (a whole 128-byte line per row) at a time;
-//     each block turns every E4M3 code into its decode tables once (a 256-entry LUT).
-//   - Output: each lane holds 4 consecutive weight rows of one sorted row -> one 8-byte
-//     store of BF16 (round-to-nearest-even).
+//   - Block scales are staged in LDS 4 steps at a time; each block turns every E4M3 code
+//     into its decode tables once (a 256-entry LUT).
+//   - Output: each lane holds 4 consecutive weight rows of one sorted row per tile -> one
+//     8-byte store of BF16 (round-to-nearest-even).
+//   - SwiGLU-fused form: the weight is the fused gate_up projection (gate rows [0, mi),
+//     up rows [mi, 2 mi)). A block owns gate rows [64 b, 64 b + 64) in its first tiles
+//     and the matching up rows in its second tiles, so each lane holds the gate and up
+//     sums of the same 4 columns; both are rounded to BF16 (the values the unfused path
+//     would store) and the clamped SwiGLU (swiglu.h) is applied in registers. The gate_up
+//     output never reaches memory.
 #include "common.h"
 #include "nvfp4_decode.h"
+#include "swiglu.h"
 
 namespace {
 
@@ -40,23 +51,30 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 16;
-constexpr int kBlockN = kWaves * kRowsPerWave;    // weight rows per block
+constexpr int kTiles = 2;                         // MFMA tiles of 16 weight rows per wave
+constexpr int kBlockN = kWaves * 16 * kTiles;     // weight rows per block
+constexpr int kHalfN = kBlockN / 2;               // block rows per tile index
 constexpr int kChunkK = 256;                      // k per main-loop step
 constexpr int kBlockM = 16;                       // sorted rows per pass: one MFMA tile
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
-constexpr int kStageSteps = 8;  // steps per staged block of scales: 128 bytes, a whole line
-constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 8 steps x 16 scale bytes, padded
+constexpr int kXPieces = kBlockM * kPiecesPerRow / kThreads;  // per thread per step
+constexpr int kXAhead = 2;                        // activation ring: steps in flight
+constexpr int kStageSteps = 4;                    // steps per staged block of scales
+constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 4 steps x 16 scale bytes, padded
 constexpr int kScaleBufBytes = kBlockN * kScaleRowBytes;
-static_assert(kBlockM * kPiecesPerRow == kThreads, "one activation piece per thread");
-static_assert(kBlockN * kStageSteps == 2 * kThreads, "two scale pieces per thread");
+constexpr int kSPieces = kBlockN * kStageSteps / kThreads;  // scale pieces per thread
+static_assert(kBlockM * kPiecesPerRow == kXPieces * kThreads, "whole activation pieces");
+static_assert(kBlockN * kStageSteps == kSPieces * kThreads, "whole scale pieces");
+static_assert(kSPieces == kTiles, "one scale piece per thread and tile half");
 
 // Raw buffer access (gfx9 resource word 3): offsets past num_records read as zero
-// without touching memory, which masks padded and invalid rows at no cost.
+// without touching memory, which masks padded and invalid rows at no cost. The range
+// check covers the vector offset, not the scalar one, so row offsets always go in the
+// vector offset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
                                            static_cast<int>(bytes), 0x00020000);
@@ -69,18 +87,21 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t vof
                                                      static_cast<int>(soff), 0));
 }
 
-// One lane's packed weights of a step: 64 k of one row as two 16-byte loads; the wave
-// reads 16 rows x 64 contiguous bytes per load.
+// One lane's packed weights of a step: per tile, 64 k of one row as two 16-byte loads;
+// the wave reads 16 rows x 64 contiguous bytes per load.
 struct WeightRegs {
-  u32x4_t a;  // k in [32 kb, 32 kb + 32) of the step
-  u32x4_t b;  // k in [128 + 32 kb, 128 + 32 kb + 32)
+  u32x4_t a[kTiles];  // k in [32 kb, 32 kb + 32) of the step
+  u32x4_t b[kTiles];  // k in [128 + 32 kb, 128 + 32 kb + 32)
 };
 
 __device__ __forceinline__ void load_weights(WeightRegs &w, __amdgpu_buffer_rsrc_t r,
-                                             uint32_t voff, int step) {
+                                             const uint32_t *voff, int step) {
   const uint32_t soff = static_cast<uint32_t>(step) * (kChunkK / 2);
-  w.a = load16(r, voff, soff);
-  w.b = load16(r, voff + 64, soff);
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    w.a[t] = load16(r, voff[t], soff);
+    w.b[t] = load16(r, voff[t] + 64, soff);
+  }
 }
 
 // 8 BF16 (k0..k7) -> order (k0,k2) (k4,k6) (k1,k3) (k5,k7), the decoder's order.
@@ -109,14 +130,11 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&w)[4]) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// Multiply four decoded words (j0 .. j0+3) into acc against B operands read from LDS.
+// Multiply four decoded words into acc against four B operands.
 template <bool kFast>
 __device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Block &b0,
-                                      const moe::Fp4Block &b1, const uint8_t *brow,
+                                      const moe::Fp4Block &b1, const bf16x8_t *B,
                                       float scale2, f32x4_t &acc) {
-  bf16x8_t B[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) B[j] = *reinterpret_cast<const bf16x8_t *>(brow + 16 * j);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t wd[4];
@@ -129,15 +147,9 @@ __device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Block
   }
 }
 
-// Decode this lane's 64 weights of the step and multiply them into acc against the
-// staged activation tile `xb` (rows = sorted rows of the pass, k permuted by 8s).
-// `sc` holds the lane's four scale codes (see permute_scales); `lut` maps a scale code to
-// the byte tables of its block (code_table_lut).
-__device__ __forceinline__ void compute_step(const WeightRegs &w, uint32_t sc,
-                                             const uint8_t *xb, const uint8_t *lut, int r16,
-                                             int kb, float scale2, f32x4_t &acc) {
-  const uint8_t *brow = xb + r16 * kLdsRowBytes + 64 * kb;
-  moe::Fp4Block blk[4];
+// The byte tables of the lane's four blocks (scale codes in the bytes of `sc`, see
+// permute_scales) from the per-block LUT.
+__device__ __forceinline__ void lut_blocks(uint32_t sc, const uint8_t *lut, moe::Fp4Block *blk) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const u32x4_t t =
@@ -147,44 +159,55 @@ __device__ __forceinline__ void compute_step(const WeightRegs &w, uint32_t sc,
     blk[g].hi03 = t[2];
     blk[g].hi47 = t[3];
   }
-  // Byte 0 of lo03 (the table entry of magnitude 0) is zero exactly for codes whose
-  // byte tables are valid; the LUT marks the others there.
-  const bool lane_fast = ((blk[0].lo03 | blk[1].lo03 | blk[2].lo03 | blk[3].lo03) & 0xFFu) == 0;
-  const uint32_t wa[4] = {w.a[0], w.a[1], w.a[2], w.a[3]};
-  const uint32_t wb[4] = {w.b[0], w.b[1], w.b[2], w.b[3]};
-  if (__all(lane_fast)) {
-    mfma4<true>(wa, blk[0], blk[1], brow, scale2, acc);
-    mfma4<true>(wb, blk[2], blk[3], brow + 256, scale2, acc);
-  } else {  // some block of the wave needs the exact per-element path
-    float d[4];
-    moe::e4m3x2_to_f32(sc, d[0], d[1]);
-    moe::e4m3x2_to_f32_hi(sc, d[2], d[3]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) blk[g] = moe::make_block(d[g], scale2);
-    mfma4<false>(wa, blk[0], blk[1], brow, scale2, acc);
-    mfma4<false>(wb, blk[2], blk[3], brow + 256, scale2, acc);
+}
+
+// Byte 0 of lo03 (the table entry of magnitude 0) is zero exactly for codes whose byte
+// tables are valid; the LUT marks the others there.
+__device__ __forceinline__ bool lut_fast(const moe::Fp4Block *blk) {
+  return ((blk[0].lo03 | blk[1].lo03 | blk[2].lo03 | blk[3].lo03) & 0xFFu) == 0;
+}
+
+// Half h of one tile's step (k in [128 h, 128 h + 128)) against the half's B operands.
+__device__ __forceinline__ void tile_half(const u32x4_t &w4, bool fast, uint32_t sc, int h,
+                                          const moe::Fp4Block *blk, const bf16x8_t *B,
+                                          float scale2, f32x4_t &acc) {
+  const uint32_t w[4] = {w4[0], w4[1], w4[2], w4[3]};
+  if (fast) {
+    mfma4<true>(w, blk[2 * h], blk[2 * h + 1], B, scale2, acc);
+  } else {  // some block of the tile needs the exact per-element path
+    float d0, d1;
+    if (h == 0) {
+      moe::e4m3x2_to_f32(sc, d0, d1);
+    } else {
+      moe::e4m3x2_to_f32_hi(sc, d0, d1);
+    }
+    mfma4<false>(w, moe::make_block(d0, scale2), moe::make_block(d1, scale2), B, scale2, acc);
   }
 }
 
 // The byte tables of every E4M3 scale code for this expert's scale2, one 16-byte entry
 // per code {lo03, lo47, hi03, hi47}; byte 0 of lo03 is set for codes that must take the
-// exact path. Built once per block by threads 0..255.
+// exact path. Built once per block.
 __device__ __forceinline__ void build_code_table_lut(uint8_t *lut, int tid, float scale2) {
-  if (tid < 256) {
+  for (int c = tid; c < 256; c += kThreads) {
     float d, unused;
-    moe::e4m3x2_to_f32(static_cast<uint32_t>(tid), d, unused);
+    moe::e4m3x2_to_f32(static_cast<uint32_t>(c), d, unused);
     const moe::Fp4Block b = moe::make_block(d, scale2);
     const u32x4_t t = {b.lo03 | (moe::fast_pq(b.pq) ? 0u : 1u), b.lo47, b.hi03, b.hi47};
-    *reinterpret_cast<u32x4_t *>(lut + tid * 16) = t;
+    *reinterpret_cast<u32x4_t *>(lut + c * 16) = t;
   }
 }
 
-__global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
+// kSwiglu = false: c[s, n] for the N weight rows.
+// kSwiglu = true: N = 2 mi; c[s, j] = swiglu(gate sum of row j, up sum of row mi + j) for
+// j < mi (c is the activation buffer, ldc its leading dimension).
+template <bool kSwiglu>
+__global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t a_rows,
     const int32_t *__restrict__ gather, const uint64_t *__restrict__ packed_ptrs,
     const uint64_t *__restrict__ scale_ptrs, const float *__restrict__ scale2s,
     const int32_t *__restrict__ offsets, uint16_t *__restrict__ c, int64_t ldc,
-    int32_t max_rows, int32_t N, int32_t K) {
+    int32_t max_rows, int32_t N, int32_t K, float limit) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kLdsBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
@@ -201,8 +224,16 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r16 = lane & 15, kb = lane >> 4;
-  const int n_wave0 = blockIdx.x * kBlockN + wave * kRowsPerWave;
-  const bool wave_on = n_wave0 < N;  // N % 16 == 0: a wave's 16 rows are all in or all out
+  // Weight rows of block row j: base[j / kHalfN] + j % kHalfN. Plain: the block's 128
+  // consecutive rows. Fused: 64 gate rows, then the matching 64 up rows.
+  const int mi = N / 2;
+  const int row_base0 = blockIdx.x * (kSwiglu ? kHalfN : kBlockN);
+  const int row_base1 = row_base0 + (kSwiglu ? mi : kHalfN);
+  const int row_end0 = kSwiglu ? mi : N;  // rows past it are out (N, mi multiples of 16)
+  // This wave's tiles: block rows 16 w + [0, 16) and kHalfN + 16 w + [0, 16).
+  const int n_tile0 = row_base0 + 16 * wave, n_tile1 = row_base1 + 16 * wave;
+  const bool tile0_on = n_tile0 < row_end0;
+  const bool tile1_on = n_tile1 < N && (!kSwiglu || tile0_on);
   const uint32_t row_bytes = static_cast<uint32_t>(K) / 2, srow_bytes = static_cast<uint32_t>(K) / 16;
   const int n_steps = K / kChunkK;
   const int n_stages = (n_steps + kStageSteps - 1) / kStageSteps;
@@ -212,80 +243,118 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
   const __amdgpu_buffer_rsrc_t x_rsrc =
       make_rsrc(a, static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(lda) * 2u);
 
-  // This lane's weight row. Rows past N lie past the buffer end and read zeros.
-  const uint32_t w_voff = static_cast<uint32_t>(n_wave0 + r16) * row_bytes + 16u * kb;
-  // Scale staging: thread -> rows (tid / 8) and 64 + (tid / 8) of the block, step tid % 8
-  // of the stage; eight threads read a row's 128 contiguous bytes.
-  // Rows past N lie past the buffer end and read zeros.
-  const int s_sub = tid & 7;
-  const uint32_t s_voff = static_cast<uint32_t>(blockIdx.x * kBlockN + (tid >> 3)) * srow_bytes;
-  // Second row of the thread. Every row offset goes into the vector offset: the buffer
-  // range check covers the vector offset, not the scalar one, so rows past N read zeros.
-  const uint32_t s_half = (kBlockN / 2) * srow_bytes;
-  const int s_lds = (tid >> 3) * kScaleRowBytes + s_sub * 16;
-  constexpr int kScaleHalfLds = (kBlockN / 2) * kScaleRowBytes;
-  const auto scale_voff = [&](int stage) {
-    return s_voff + static_cast<uint32_t>(min(stage * kStageSteps + s_sub, n_steps - 1)) * 16u;
+  // This lane's weight rows; rows past N lie past the buffer end and read zeros. A fused
+  // block's gate rows past mi would read real up rows: those tiles are off (no output),
+  // their loads are harmless.
+  const uint32_t w_voff[kTiles] = {
+      static_cast<uint32_t>(n_tile0 + r16) * row_bytes + 16u * kb,
+      static_cast<uint32_t>(n_tile1 + r16) * row_bytes + 16u * kb};
+  // Scale staging: thread -> block rows tid / 4 (tile-0 half) and kHalfN + tid / 4
+  // (tile-1 half), step tid % 4 of the stage; four threads read a row's 64 bytes.
+  const int s_sub = tid & (kStageSteps - 1);
+  const int s_row = tid / kStageSteps;
+  const uint32_t s_voff[kSPieces] = {
+      static_cast<uint32_t>(row_base0 + s_row) * srow_bytes,
+      static_cast<uint32_t>(row_base1 + s_row) * srow_bytes};
+  const int s_lds = s_row * kScaleRowBytes + s_sub * 16;
+  constexpr int kScaleHalfLds = kHalfN * kScaleRowBytes;
+  const auto scale_off = [&](int stage) {
+    return static_cast<uint32_t>(min(stage * kStageSteps + s_sub, n_steps - 1)) * 16u;
   };
-  // This lane's scale dword within a staged block: row of the wave's 16, lane's kb.
-  const int s_read = (wave * kRowsPerWave + r16) * kScaleRowBytes + 4 * kb;
-  // Activation staging: thread -> (row of the pass, 16-byte piece of a step).
-  const int piece_row = tid / kPiecesPerRow, piece_col = tid % kPiecesPerRow;
-  const int lds_off = piece_row * kLdsRowBytes + piece_col * 16;
+  // This lane's scale dword of tile 0 within a staged block (tile 1: + kScaleHalfLds).
+  const int s_read = (16 * wave + r16) * kScaleRowBytes + 4 * kb;
   build_code_table_lut(lut, tid, scale2);  // published by the first pass's barrier
 
   for (int m0 = lo; m0 < hi; m0 += kBlockM) {
     const int m_cnt = min(kBlockM, hi - m0);
-    // Rows past the pass and out-of-range gather indices read zeros (offset past the end).
-    int g = -1;
-    if (piece_row < m_cnt) {
-      const int srow = m0 + piece_row;
-      g = gather != nullptr ? gather[srow] : srow;
+    // Activation staging: thread -> (row of the pass, 16-byte piece of a step) for rows
+    // tid / 32 and 8 + tid / 32. Rows past the pass and out-of-range gather indices read
+    // zeros (offset past the end).
+    uint32_t x_voff[kXPieces];
+    int lds_off[kXPieces];
+#pragma unroll
+    for (int p = 0; p < kXPieces; ++p) {
+      const int piece = tid + p * kThreads;
+      const int piece_row = piece / kPiecesPerRow, piece_col = piece % kPiecesPerRow;
+      lds_off[p] = piece_row * kLdsRowBytes + piece_col * 16;
+      int g = -1;
+      if (piece_row < m_cnt) {
+        const int srow = m0 + piece_row;
+        g = gather != nullptr ? gather[srow] : srow;
+      }
+      x_voff[p] = (g >= 0 && g < a_rows)
+                      ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) + piece_col * 8u) * 2u
+                      : 0x80000000u;
     }
-    const uint32_t x_voff = (g >= 0 && g < a_rows)
-                                ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) +
-                                   piece_col * 8u) * 2u
-                                : 0x80000000u;
 
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     WeightRegs w0, w1;
     load_weights(w0, w_rsrc, w_voff, 0);
-    *reinterpret_cast<u32x4_t *>(ss[0] + s_lds) =
-        permute_scales(load16(s_rsrc, scale_voff(0), 0));
-    *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + kScaleHalfLds) =
-        permute_scales(load16(s_rsrc, scale_voff(0) + s_half, 0));
-    *reinterpret_cast<u32x4_t *>(xs[0] + lds_off) = permute_k8(load16(x_rsrc, x_voff, 0));
-    // Activation chunks are prefetched kXAhead steps ahead in a register ring.
-    constexpr int kXAhead = 4;
-    u32x4_t xr[kXAhead];
+#pragma unroll
+    for (int p = 0; p < kSPieces; ++p)
+      *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + p * kScaleHalfLds) =
+          permute_scales(load16(s_rsrc, s_voff[p] + scale_off(0), 0));
+#pragma unroll
+    for (int p = 0; p < kXPieces; ++p)
+      *reinterpret_cast<u32x4_t *>(xs[0] + lds_off[p]) = permute_k8(load16(x_rsrc, x_voff[p], 0));
+    u32x4_t xr[kXAhead][kXPieces];
 #pragma unroll
     for (int d = 1; d < kXAhead; ++d)
-      xr[d] = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(d, n_steps - 1)) * (kChunkK * 2));
+#pragma unroll
+      for (int p = 0; p < kXPieces; ++p)
+        xr[d][p] = load16(x_rsrc, x_voff[p],
+                          static_cast<uint32_t>(min(d, n_steps - 1)) * (kChunkK * 2));
     __syncthreads();
 
     // Steps of one scale stage, weights prefetched one step ahead in a two-slot ring.
     // Every load here is unconditional (clamped indices): a load behind a branch leaves
     // the wait counters unknown at the join, and the compiler then drains all of them.
-    u32x4_t sc_next0, sc_next1;
+    u32x4_t sc_next[kSPieces];
     auto run_step = [&](int q, int i, WeightRegs &cur, WeightRegs &ahead) {
       const int step = q * kStageSteps + i;
       if (i == 0) {
-        sc_next0 = load16(s_rsrc, scale_voff(q + 1), 0);
-        sc_next1 = load16(s_rsrc, scale_voff(q + 1) + s_half, 0);
+#pragma unroll
+        for (int p = 0; p < kSPieces; ++p)
+          sc_next[p] = load16(s_rsrc, s_voff[p] + scale_off(q + 1), 0);
       }
-      xr[i % kXAhead] = load16(x_rsrc, x_voff, static_cast<uint32_t>(min(step + kXAhead, n_steps - 1)) *
-                                                  (kChunkK * 2));
+#pragma unroll
+      for (int p = 0; p < kXPieces; ++p)
+        xr[i % kXAhead][p] = load16(x_rsrc, x_voff[p],
+                                    static_cast<uint32_t>(min(step + kXAhead, n_steps - 1)) *
+                                        (kChunkK * 2));
       load_weights(ahead, w_rsrc, w_voff, min(step + 1, n_steps - 1));
-      if (wave_on) {
-        const uint32_t sc = *reinterpret_cast<const uint32_t *>(ss[q & 1] + s_read + 16 * i);
-        compute_step(cur, sc, xs[step & 1], lut, r16, kb, scale2, acc);
+      if (tile0_on) {
+        const uint8_t *srow = ss[q & 1] + s_read + 16 * i;
+        const uint32_t sc0 = *reinterpret_cast<const uint32_t *>(srow);
+        const uint32_t sc1 = *reinterpret_cast<const uint32_t *>(srow + kScaleHalfLds);
+        const uint8_t *brow = xs[step & 1] + r16 * kLdsRowBytes + 64 * kb;
+        moe::Fp4Block blk0[4], blk1[4];
+        lut_blocks(sc0, lut, blk0);
+        lut_blocks(sc1, lut, blk1);
+        const bool fast0 = __all(lut_fast(blk0)), fast1 = __all(lut_fast(blk1));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8_t B[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            B[j] = *reinterpret_cast<const bf16x8_t *>(brow + 256 * h + 16 * j);
+          tile_half(h ? cur.b[0] : cur.a[0], fast0, sc0, h, blk0, B, scale2, acc[0]);
+          if (tile1_on)
+            tile_half(h ? cur.b[1] : cur.a[1], fast1, sc1, h, blk1, B, scale2, acc[1]);
+        }
       }
-      *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off) = permute_k8(xr[(i + 1) % kXAhead]);
+#pragma unroll
+      for (int p = 0; p < kXPieces; ++p)
+        *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off[p]) =
+            permute_k8(xr[(i + 1) % kXAhead][p]);
       // The next stage's buffer was last read in the previous stage: fill it mid-stage.
-      if (i == 3) {
-        *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds) = permute_scales(sc_next0);
-        *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds + kScaleHalfLds) =
-            permute_scales(sc_next1);
+      if (i == 2) {
+#pragma unroll
+        for (int p = 0; p < kSPieces; ++p)
+          *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds + p * kScaleHalfLds) =
+              permute_scales(sc_next[p]);
       }
       __syncthreads();
     };
@@ -295,18 +364,37 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_gemm_kernel(
       if (s0 + 1 < n_steps) run_step(q, 1, w1, w0);
       if (s0 + 2 < n_steps) run_step(q, 2, w0, w1);
       if (s0 + 3 < n_steps) run_step(q, 3, w1, w0);
-      if (s0 + 4 < n_steps) run_step(q, 4, w0, w1);
-      if (s0 + 5 < n_steps) run_step(q, 5, w1, w0);
-      if (s0 + 6 < n_steps) run_step(q, 6, w0, w1);
-      if (s0 + 7 < n_steps) run_step(q, 7, w1, w0);
     }
 
-    // acc[i] = result for weight row n_wave0 + 4 kb + i and sorted row m0 + r16.
-    if (wave_on && r16 < m_cnt) {
-      uint2 o;
-      o.x = moe::pack_bf16x2(acc[0], acc[1]);
-      o.y = moe::pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<uint2 *>(c + static_cast<size_t>(m0 + r16) * ldc + n_wave0 + 4 * kb) = o;
+    // acc[t][i] = result for weight row n_tile_t + 4 kb + i and sorted row m0 + r16.
+    if (r16 < m_cnt) {
+      uint16_t *crow = c + static_cast<size_t>(m0 + r16) * ldc;
+      if (kSwiglu) {
+        if (tile0_on) {
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // the BF16 values the unfused path stores, then its SwiGLU
+            const uint32_t gu = moe::pack_bf16x2(acc[0][i], acc[1][i]);
+            o[i] = moe::swiglu_clamp1(__uint_as_float(gu << 16),
+                                      __uint_as_float(gu & 0xFFFF0000u), limit);
+          }
+          uint2 v;
+          v.x = moe::pack_bf16x2(o[0], o[1]);
+          v.y = moe::pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2 *>(crow + n_tile0 + 4 * kb) = v;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          if (t == 0 ? tile0_on : tile1_on) {
+            uint2 v;
+            v.x = moe::pack_bf16x2(acc[t][0], acc[t][1]);
+            v.y = moe::pack_bf16x2(acc[t][2], acc[t][3]);
+            *reinterpret_cast<uint2 *>(crow + (t == 0 ? n_tile0 : n_tile1) + 4 * kb) = v;
+          }
+        }
+      }
     }
   }
 }
@@ -344,6 +432,36 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
   }
 }
 
+// Shared argument checks of the two GEMM entry points (n = weight rows, n_out = columns
+// of c). Returns MOE_OK or MOE_EINVAL with the error recorded.
+int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_rows,
+                    const uint64_t *packed_ptrs, const uint64_t *scale_ptrs,
+                    const float *scale2, const int32_t *expert_offsets, int32_t num_experts,
+                    const uint16_t *c, int64_t ldc, int32_t max_rows, int32_t n,
+                    int32_t n_out, int32_t k) {
+  MOE_REQUIRE(k > 0 && k % kChunkK == 0, "%s: k must be a positive multiple of %d (got %d)",
+              name, kChunkK, k);
+  MOE_REQUIRE(lda >= k && lda % 8 == 0, "%s: lda must be >= k and a multiple of 8", name);
+  MOE_REQUIRE(ldc >= n_out && ldc % 8 == 0, "%s: ldc must be >= %d and a multiple of 8", name,
+              n_out);
+  MOE_REQUIRE(num_experts >= 1 && num_experts <= 65535,
+              "%s: num_experts must be in [1, 65535] (got %d)", name, num_experts);
+  MOE_REQUIRE(max_rows >= 0 && a_rows >= 0, "%s: max_rows and a_rows must be >= 0", name);
+  MOE_REQUIRE(a && packed_ptrs && scale_ptrs && scale2 && expert_offsets && c,
+              "%s: a required pointer is NULL", name);
+  MOE_REQUIRE(moe::aligned16(a) && moe::aligned16(c), "%s: a and c must be 16-byte aligned",
+              name);
+  if (max_rows == 0) return MOE_OK;
+  MOE_REQUIRE(a_rows >= 1, "%s: a_rows must be >= 1 when max_rows > 0", name);
+  // Buffer offsets are 32-bit: activations below 2 GiB, one expert's packed weights
+  // below 4 GiB.
+  MOE_REQUIRE(static_cast<uint64_t>(a_rows) * lda * 2 < (1ull << 31),
+              "%s: the activation buffer must be smaller than 2 GiB", name);
+  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 32),
+              "%s: one expert's packed weights must be smaller than 4 GiB", name);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -355,29 +473,36 @@ extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_
   moe::clear_error();
   MOE_REQUIRE(n > 0 && n % 16 == 0, "grouped_gemm: n must be a positive multiple of 16 (got %d)",
               n);
-  MOE_REQUIRE(k > 0 && k % kChunkK == 0,
-              "grouped_gemm: k must be a positive multiple of %d (got %d)", kChunkK, k);
-  MOE_REQUIRE(lda >= k && lda % 8 == 0, "grouped_gemm: lda must be >= k and a multiple of 8");
-  MOE_REQUIRE(ldc >= n && ldc % 8 == 0, "grouped_gemm: ldc must be >= n and a multiple of 8");
-  MOE_REQUIRE(num_experts >= 1 && num_experts <= 65535,
-              "grouped_gemm: num_experts must be in [1, 65535] (got %d)", num_experts);
-  MOE_REQUIRE(max_rows >= 0 && a_rows >= 0, "grouped_gemm: max_rows and a_rows must be >= 0");
-  MOE_REQUIRE(a && packed_ptrs && scale_ptrs && scale2 && expert_offsets && c,
-              "grouped_gemm: a required pointer is NULL");
-  MOE_REQUIRE(moe::aligned16(a) && moe::aligned16(c),
-              "grouped_gemm: a and c must be 16-byte aligned");
-  if (max_rows == 0) return MOE_OK;
-  MOE_REQUIRE(a_rows >= 1, "grouped_gemm: a_rows must be >= 1 when max_rows > 0");
-  // Buffer offsets are 32-bit: activations below 2 GiB, one expert's packed weights
-  // below 4 GiB.
-  MOE_REQUIRE(static_cast<uint64_t>(a_rows) * lda * 2 < (1ull << 31),
-              "grouped_gemm: the activation buffer must be smaller than 2 GiB");
-  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 32),
-              "grouped_gemm: one expert's packed weights must be smaller than 4 GiB");
+  const int rc = check_gemm_args("grouped_gemm", a, lda, a_rows, packed_ptrs, scale_ptrs, scale2,
+                                 expert_offsets, num_experts, c, ldc, max_rows, n, n, k);
+  if (rc != MOE_OK || max_rows == 0) return rc;
   const dim3 grid((n + kBlockN - 1) / kBlockN, num_experts);
-  return moe::launch("moe_w4a16_grouped_gemm", grouped_gemm_kernel, grid, dim3(kThreads), 0,
-                     stream, a, lda, a_rows, a_gather, packed_ptrs, scale_ptrs, scale2,
-                     expert_offsets, c, ldc, max_rows, n, k);
+  return moe::launch("moe_w4a16_grouped_gemm", grouped_gemm_kernel<false>, grid, dim3(kThreads),
+                     0, stream, a, lda, a_rows, a_gather, packed_ptrs, scale_ptrs, scale2,
+                     expert_offsets, c, ldc, max_rows, n, k, 0.0f);
+}
+
+extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
+                                             const int32_t *a_gather,
+                                             const uint64_t *packed_ptrs,
+                                             const uint64_t *scale_ptrs, const float *scale2,
+                                             const int32_t *expert_offsets, int32_t num_experts,
+                                             uint16_t *act, int64_t ld_act, int32_t max_rows,
+                                             int32_t mi, int32_t k, float limit, void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(mi > 0 && mi % 16 == 0,
+              "grouped_gemm_swiglu: mi must be a positive multiple of 16 (got %d)", mi);
+  MOE_REQUIRE(mi <= (1 << 29), "grouped_gemm_swiglu: mi too large (got %d)", mi);
+  MOE_REQUIRE(limit > 0.0f, "grouped_gemm_swiglu: limit must be > 0");
+  const int rc = check_gemm_args("grouped_gemm_swiglu", a, lda, a_rows, packed_ptrs, scale_ptrs,
+                                 scale2, expert_offsets, num_experts, act, ld_act, max_rows,
+                                 2 * mi, mi, k);
+  if (rc != MOE_OK || max_rows == 0) return rc;
+  const dim3 grid((mi + kHalfN - 1) / kHalfN, num_experts);
+  return moe::launch("moe_w4a16_grouped_gemm_swiglu", grouped_gemm_kernel<true>, grid,
+                     dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
+                     scale_ptrs, scale2, expert_offsets, act, ld_act, max_rows, 2 * mi, k,
+                     limit);
 }
 
 extern "C" int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales,

@@ -7,6 +7,8 @@
  *   moe_w4a16_grouped_gemm  one launch over all experts: gathered BF16 rows x NVFP4 weights
  *   swiglu_clamp            silu(min(gate, L)) * clamp(up, -L, L)
  *   moe_combine             top-k weighted sum of the expert-sorted rows per token
+ *   moe_w4a16_grouped_gemm_swiglu  the gate_up grouped GEMM with swiglu_clamp fused into
+ *                           its epilogue (same bits as the two calls in sequence)
  *
  * Sources (the pages this library follows, by title and section):
  *   [FPG]  "Module forward_prefill_gemm" (glm5next_mlp/forward_prefill_gemm), sections
@@ -129,6 +131,35 @@ int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
                            const uint64_t *scale_ptrs, const float *scale2,
                            const int32_t *expert_offsets, int32_t num_experts, uint16_t *c,
                            int64_t ldc, int32_t max_rows, int32_t n, int32_t k, void *stream);
+
+/*
+ * moe_w4a16_grouped_gemm_swiglu - moe_w4a16_grouped_gemm over a fused gate_up weight
+ * (n = 2 * mi rows: gate rows [0, mi), up rows [mi, 2 mi), the [FPG] fused gate_up
+ * layout) followed by swiglu_clamp, in one launch:
+ *
+ *   act[s, j] = bf16( swiglu(G, U) ),   j in [0, mi)
+ *   G = bf16(sum_k a[g(s), k] W_e[j, k]),   U = bf16(sum_k a[g(s), k] W_e[mi + j, k])
+ *   swiglu(G, U) = silu(min(G, limit)) * clamp(U, -limit, limit) in FP32, as swiglu_clamp
+ *
+ * The result is bit-identical to moe_w4a16_grouped_gemm into a [max_rows, 2 mi] buffer
+ * followed by swiglu_clamp on its two halves; the gate_up values are never stored. Rows,
+ * gathers, null entries and expert_offsets behave as in moe_w4a16_grouped_gemm (rows of a
+ * null expert are not written).
+ *
+ *   act      bf16 [max_rows, ld_act]  output
+ *   tables   packed_ptrs[e] -> uint8 [2 mi, k/2], scale_ptrs[e] -> uint8 [2 mi, k/16]
+ *
+ * Requirements (else MOE_EINVAL): mi > 0 and mi % 16 == 0; limit > 0; ld_act >= mi; the
+ * other requirements of moe_w4a16_grouped_gemm with n = 2 mi and c = act.
+ * Fusing the activation into the producing GEMM removes the gate_up buffer's write and
+ * read and one launch.
+ */
+int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
+                                  const int32_t *a_gather, const uint64_t *packed_ptrs,
+                                  const uint64_t *scale_ptrs, const float *scale2,
+                                  const int32_t *expert_offsets, int32_t num_experts,
+                                  uint16_t *act, int64_t ld_act, int32_t max_rows, int32_t mi,
+                                  int32_t k, float limit, void *stream);
 
 /*
  * swiglu_clamp - out[r, j] = bf16( silu(min(gate[r, j], limit)) * clamp(up[r, j], -limit,

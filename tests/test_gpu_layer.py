@@ -76,7 +76,7 @@ def _layer_inputs(w: wl.Workload, rows=None):
     return ids, wts, x_bits
 
 
-def _run_layer(hip, w, ids, wts, x_bits, gu_table, dn_table):
+def _run_layer(hip, w, ids, wts, x_bits, gu_table, dn_table, fused=True):
     rows, top_k = ids.shape
     ws = hip.Workspace(rows, top_k, w.num_experts, w.hidden, w.moe_intermediate)
     # NaN in every intermediate buffer: a row the path reads without writing it first
@@ -85,7 +85,7 @@ def _run_layer(hip, w, ids, wts, x_bits, gu_table, dn_table):
         t.view(torch.int16).fill_(-1)
     out = torch.empty((rows, w.hidden), dtype=torch.bfloat16, device="cuda")
     hip.moe_layer(bf16_dev(x_bits), dev(ids), dev(wts), gu_table, dn_table,
-                  w.moe_intermediate, w.limit, ws, out)
+                  w.moe_intermediate, w.limit, ws, out, fused=fused)
     torch.cuda.synchronize()
     return f64(out), ws
 
@@ -107,12 +107,14 @@ def _oracle_rows(w, ids, wts, x_bits, gu, dn, mode, null=()):
     return out
 
 
-def test_layer_e64_vs_oracle(hip):
-    """Full routed layer, 256 rows x 64 experts, every output against the oracle."""
+@pytest.mark.parametrize("fused", [True, False])
+def test_layer_e64_vs_oracle(hip, fused):
+    """Full routed layer, 256 rows x 64 experts, every output against the oracle, with the
+    SwiGLU fused into the gate_up GEMM and as its own call."""
     w = wl.WORKLOADS["layer_e64"]
     ids, wts, x_bits = _layer_inputs(w)
     gu, dn, gt, dt = _tables(hip, w)
-    got, ws = _run_layer(hip, w, ids, wts, x_bits, gt, dt)
+    got, ws = _run_layer(hip, w, ids, wts, x_bits, gt, dt, fused)
     ref = _oracle_rows(w, ids, wts, x_bits, gu, dn, "bf16w")
     r = rel_err(got, ref)
     exact = _oracle_rows(w, ids, wts, x_bits, gu, dn, "exact")
