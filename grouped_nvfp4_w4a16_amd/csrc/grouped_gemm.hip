@@ -31,8 +31,11 @@
 //     loaded two steps ahead into a register ring and staged per 256-k step in LDS
 //     (double buffered, one barrier per step), shared by the 4 waves, with k permuted
 //     inside each group of 8 to match the decoder's order.
-//   - Block scales are staged in LDS 4 steps at a time; each block turns every E4M3 code
-//     into its decode tables once (a 256-entry LUT).
+//   - Block scales are read a whole 128-byte line (8 steps) per row at a time and staged
+//     in LDS 4 steps at a time: the first half goes to LDS at once, the second half waits
+//     in registers for its stage (reading half lines lets L2 evict a line between its two
+//     halves, which doubles the scale traffic). Each block turns every E4M3 code into its
+//     decode tables once (a 256-entry LUT).
 //   - Output: each lane holds 4 consecutive weight rows of one sorted row per tile -> one
 //     8-byte store of BF16 (round-to-nearest-even).
 //   - SwiGLU-fused form: the weight is the fused gate_up projection (gate rows [0, mi),
@@ -64,6 +67,7 @@ constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged r
 constexpr int kXPieces = kBlockM * kPiecesPerRow / kThreads;  // per thread per step
 constexpr int kXAhead = 2;                        // activation ring: steps in flight
 constexpr int kStageSteps = 4;                    // steps per staged block of scales
+constexpr int kLineSteps = 2 * kStageSteps;       // steps per 128-byte line of scales
 constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 4 steps x 16 scale bytes, padded
 constexpr int kScaleBufBytes = kBlockN * kScaleRowBytes;
 constexpr int kSPieces = kBlockN * kStageSteps / kThreads;  // scale pieces per thread
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   const bool tile1_on = n_tile1 < N && (!kSwiglu || tile0_on);
   const uint32_t row_bytes = static_cast<uint32_t>(K) / 2, srow_bytes = static_cast<uint32_t>(K) / 16;
   const int n_steps = K / kChunkK;
-  const int n_stages = (n_steps + kStageSteps - 1) / kStageSteps;
+  const int n_groups = (n_steps + kLineSteps - 1) / kLineSteps;
 
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(packed, static_cast<uint32_t>(N) * row_bytes);
   const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(scales, static_cast<uint32_t>(N) * srow_bytes);
@@ -250,7 +254,8 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       static_cast<uint32_t>(n_tile0 + r16) * row_bytes + 16u * kb,
       static_cast<uint32_t>(n_tile1 + r16) * row_bytes + 16u * kb};
   // Scale staging: thread -> block rows tid / 4 (tile-0 half) and kHalfN + tid / 4
-  // (tile-1 half), step tid % 4 of the stage; four threads read a row's 64 bytes.
+  // (tile-1 half), step tid % 4 of each half line; four threads read a row's 128-byte
+  // line of 8 steps as two 16-byte pieces each.
   const int s_sub = tid & (kStageSteps - 1);
   const int s_row = tid / kStageSteps;
   const uint32_t s_voff[kSPieces] = {
@@ -258,8 +263,10 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       static_cast<uint32_t>(row_base1 + s_row) * srow_bytes};
   const int s_lds = s_row * kScaleRowBytes + s_sub * 16;
   constexpr int kScaleHalfLds = kHalfN * kScaleRowBytes;
-  const auto scale_off = [&](int stage) {
-    return static_cast<uint32_t>(min(stage * kStageSteps + s_sub, n_steps - 1)) * 16u;
+  // Offset of step (8 g + 4 h + s_sub) of a row's scales, clamped into the row.
+  const auto scale_off = [&](int g, int h) {
+    return static_cast<uint32_t>(min(g * kLineSteps + h * kStageSteps + s_sub, n_steps - 1)) *
+           16u;
   };
   // This lane's scale dword of tile 0 within a staged block (tile 1: + kScaleHalfLds).
   const int s_read = (16 * wave + r16) * kScaleRowBytes + 4 * kb;
@@ -292,10 +299,16 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     for (int t = 0; t < kTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     WeightRegs w0, w1;
     load_weights(w0, w_rsrc, w_voff, 0);
+    // Scales of steps 0-3 to LDS now; steps 4-7 wait in sc_keep.
+    u32x4_t sc_keep[kSPieces], sc_next[kSPieces];
+#pragma unroll
+    for (int p = 0; p < kSPieces; ++p) {
+      sc_next[p] = load16(s_rsrc, s_voff[p] + scale_off(0, 0), 0);
+      sc_keep[p] = load16(s_rsrc, s_voff[p] + scale_off(0, 1), 0);
+    }
 #pragma unroll
     for (int p = 0; p < kSPieces; ++p)
-      *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + p * kScaleHalfLds) =
-          permute_scales(load16(s_rsrc, s_voff[p] + scale_off(0), 0));
+      *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + p * kScaleHalfLds) = permute_scales(sc_next[p]);
 #pragma unroll
     for (int p = 0; p < kXPieces; ++p)
       *reinterpret_cast<u32x4_t *>(xs[0] + lds_off[p]) = permute_k8(load16(x_rsrc, x_voff[p], 0));
@@ -308,16 +321,18 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
                           static_cast<uint32_t>(min(d, n_steps - 1)) * (kChunkK * 2));
     __syncthreads();
 
-    // Steps of one scale stage, weights prefetched one step ahead in a two-slot ring.
-    // Every load here is unconditional (clamped indices): a load behind a branch leaves
-    // the wait counters unknown at the join, and the compiler then drains all of them.
-    u32x4_t sc_next[kSPieces];
-    auto run_step = [&](int q, int i, WeightRegs &cur, WeightRegs &ahead) {
-      const int step = q * kStageSteps + i;
-      if (i == 0) {
+    // Steps of one 8-step group of scales (LDS stage i / 4), weights prefetched one step
+    // ahead in a two-slot ring. Every load here is unconditional (clamped indices): a load
+    // behind a branch leaves the wait counters unknown at the join, and the compiler then
+    // drains all of them.
+    auto run_step = [&](int g, int i, WeightRegs &cur, WeightRegs &ahead) {
+      const int step = g * kLineSteps + i;
+      if (i == 4) {  // the next group's line, both halves in one go (sc_keep is free now)
 #pragma unroll
-        for (int p = 0; p < kSPieces; ++p)
-          sc_next[p] = load16(s_rsrc, s_voff[p] + scale_off(q + 1), 0);
+        for (int p = 0; p < kSPieces; ++p) {
+          sc_next[p] = load16(s_rsrc, s_voff[p] + scale_off(g + 1, 0), 0);
+          sc_keep[p] = load16(s_rsrc, s_voff[p] + scale_off(g + 1, 1), 0);
+        }
       }
 #pragma unroll
       for (int p = 0; p < kXPieces; ++p)
@@ -326,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
                                         (kChunkK * 2));
       load_weights(ahead, w_rsrc, w_voff, min(step + 1, n_steps - 1));
       if (tile0_on) {
-        const uint8_t *srow = ss[q & 1] + s_read + 16 * i;
+        const uint8_t *srow = ss[i / kStageSteps] + s_read + 16 * (i % kStageSteps);
         const uint32_t sc0 = *reinterpret_cast<const uint32_t *>(srow);
         const uint32_t sc1 = *reinterpret_cast<const uint32_t *>(srow + kScaleHalfLds);
         const uint8_t *brow = xs[step & 1] + r16 * kLdsRowBytes + 64 * kb;
@@ -349,21 +364,33 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       for (int p = 0; p < kXPieces; ++p)
         *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off[p]) =
             permute_k8(xr[(i + 1) % kXAhead][p]);
-      // The next stage's buffer was last read in the previous stage: fill it mid-stage.
+      // Each stage buffer is filled mid-way through the other stage (its last reads are
+      // a barrier behind): steps 4-7 of this group at step 2, steps 0-3 of the next
+      // group at step 6.
       if (i == 2) {
 #pragma unroll
         for (int p = 0; p < kSPieces; ++p)
-          *reinterpret_cast<u32x4_t *>(ss[(q + 1) & 1] + s_lds + p * kScaleHalfLds) =
+          *reinterpret_cast<u32x4_t *>(ss[1] + s_lds + p * kScaleHalfLds) =
+              permute_scales(sc_keep[p]);
+      }
+      if (i == 6) {
+#pragma unroll
+        for (int p = 0; p < kSPieces; ++p)
+          *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + p * kScaleHalfLds) =
               permute_scales(sc_next[p]);
       }
       __syncthreads();
     };
-    for (int q = 0; q < n_stages; ++q) {
-      const int s0 = q * kStageSteps;
-      run_step(q, 0, w0, w1);
-      if (s0 + 1 < n_steps) run_step(q, 1, w1, w0);
-      if (s0 + 2 < n_steps) run_step(q, 2, w0, w1);
-      if (s0 + 3 < n_steps) run_step(q, 3, w1, w0);
+    for (int g = 0; g < n_groups; ++g) {
+      const int s0 = g * kLineSteps;
+      run_step(g, 0, w0, w1);
+      if (s0 + 1 < n_steps) run_step(g, 1, w1, w0);
+      if (s0 + 2 < n_steps) run_step(g, 2, w0, w1);
+      if (s0 + 3 < n_steps) run_step(g, 3, w1, w0);
+      if (s0 + 4 < n_steps) run_step(g, 4, w0, w1);
+      if (s0 + 5 < n_steps) run_step(g, 5, w1, w0);
+      if (s0 + 6 < n_steps) run_step(g, 6, w0, w1);
+      if (s0 + 7 < n_steps) run_step(g, 7, w1, w0);
     }
 
     // acc[t][i] = result for weight row n_tile_t + 4 kb + i and sorted row m0 + r16.
