@@ -28,7 +28,7 @@
 //     wave-uniform branch per tile: the byte-table path when every block of the tile
 //     allows it, else the exact per-element path.
 //   - The gathered activation rows are the B operand (16 rows per MFMA tile). They are
-//     loaded two steps ahead into a register ring and staged per 256-k step in LDS
+//     loaded one step ahead into registers and staged per 256-k step in LDS
 //     (double buffered, one barrier per step), shared by the 4 waves, with k permuted
 //     inside each group of 8 to match the decoder's order.
 //   - Block scales are read a whole 128-byte line (8 steps) per row at a time and staged
@@ -65,7 +65,7 @@ constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padd
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
 constexpr int kXPieces = kBlockM * kPiecesPerRow / kThreads;  // per thread per step
-constexpr int kXAhead = 2;                        // activation ring: steps in flight
+constexpr int kXAhead = 1;                        // activation ring: steps in flight
 constexpr int kStageSteps = 4;                    // steps per staged block of scales
 constexpr int kLineSteps = 2 * kStageSteps;       // steps per 128-byte line of scales
 constexpr int kScaleRowBytes = kStageSteps * 16 + 16;  // 4 steps x 16 scale bytes, padded
@@ -98,13 +98,20 @@ struct WeightRegs {
   u32x4_t b[kTiles];  // k in [128 + 32 kb, 128 + 32 kb + 32)
 };
 
+// Past-the-end offset: the load returns zeros and moves no data.
+constexpr uint32_t kNoLoad = 0x80000000u;
+
+// Loads of a step past the last one get kNoLoad, so every load stays unconditional (see
+// the main loop) without re-reading data that L2 may already have evicted.
 __device__ __forceinline__ void load_weights(WeightRegs &w, __amdgpu_buffer_rsrc_t r,
-                                             const uint32_t *voff, int step) {
+                                             const uint32_t *voff, int step, int n_steps) {
   const uint32_t soff = static_cast<uint32_t>(step) * (kChunkK / 2);
+  const bool live = step < n_steps;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
-    w.a[t] = load16(r, voff[t], soff);
-    w.b[t] = load16(r, voff[t] + 64, soff);
+    const uint32_t v = live ? voff[t] : kNoLoad;
+    w.a[t] = load16(r, v, soff);
+    w.b[t] = load16(r, v + 64, soff);
   }
 }
 
@@ -263,10 +270,11 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       static_cast<uint32_t>(row_base1 + s_row) * srow_bytes};
   const int s_lds = s_row * kScaleRowBytes + s_sub * 16;
   constexpr int kScaleHalfLds = kHalfN * kScaleRowBytes;
-  // Offset of step (8 g + 4 h + s_sub) of a row's scales, clamped into the row.
-  const auto scale_off = [&](int g, int h) {
-    return static_cast<uint32_t>(min(g * kLineSteps + h * kStageSteps + s_sub, n_steps - 1)) *
-           16u;
+  // Vector offset of step (8 g + 4 h + s_sub) of piece p's scale row; kNoLoad past the
+  // row's last step.
+  const auto scale_voff = [&](int p, int g, int h) {
+    const int st = g * kLineSteps + h * kStageSteps + s_sub;
+    return st < n_steps ? s_voff[p] + static_cast<uint32_t>(st) * 16u : kNoLoad;
   };
   // This lane's scale dword of tile 0 within a staged block (tile 1: + kScaleHalfLds).
   const int s_read = (16 * wave + r16) * kScaleRowBytes + 4 * kb;
@@ -291,20 +299,20 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       }
       x_voff[p] = (g >= 0 && g < a_rows)
                       ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) + piece_col * 8u) * 2u
-                      : 0x80000000u;
+                      : kNoLoad;
     }
 
     f32x4_t acc[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     WeightRegs w0, w1;
-    load_weights(w0, w_rsrc, w_voff, 0);
+    load_weights(w0, w_rsrc, w_voff, 0, n_steps);
     // Scales of steps 0-3 to LDS now; steps 4-7 wait in sc_keep.
     u32x4_t sc_keep[kSPieces], sc_next[kSPieces];
 #pragma unroll
     for (int p = 0; p < kSPieces; ++p) {
-      sc_next[p] = load16(s_rsrc, s_voff[p] + scale_off(0, 0), 0);
-      sc_keep[p] = load16(s_rsrc, s_voff[p] + scale_off(0, 1), 0);
+      sc_next[p] = load16(s_rsrc, scale_voff(p, 0, 0), 0);
+      sc_keep[p] = load16(s_rsrc, scale_voff(p, 0, 1), 0);
     }
 #pragma unroll
     for (int p = 0; p < kSPieces; ++p)
@@ -317,29 +325,28 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     for (int d = 1; d < kXAhead; ++d)
 #pragma unroll
       for (int p = 0; p < kXPieces; ++p)
-        xr[d][p] = load16(x_rsrc, x_voff[p],
-                          static_cast<uint32_t>(min(d, n_steps - 1)) * (kChunkK * 2));
+        xr[d][p] = load16(x_rsrc, d < n_steps ? x_voff[p] : kNoLoad,
+                          static_cast<uint32_t>(d) * (kChunkK * 2));
     __syncthreads();
 
     // Steps of one 8-step group of scales (LDS stage i / 4), weights prefetched one step
-    // ahead in a two-slot ring. Every load here is unconditional (clamped indices): a load
-    // behind a branch leaves the wait counters unknown at the join, and the compiler then
-    // drains all of them.
+    // ahead in a two-slot ring. Every load here is unconditional (past the end it reads
+    // nothing): a load behind a branch leaves the wait counters unknown at the join, and
+    // the compiler then drains all of them.
     auto run_step = [&](int g, int i, WeightRegs &cur, WeightRegs &ahead) {
       const int step = g * kLineSteps + i;
       if (i == 4) {  // the next group's line, both halves in one go (sc_keep is free now)
 #pragma unroll
         for (int p = 0; p < kSPieces; ++p) {
-          sc_next[p] = load16(s_rsrc, s_voff[p] + scale_off(g + 1, 0), 0);
-          sc_keep[p] = load16(s_rsrc, s_voff[p] + scale_off(g + 1, 1), 0);
+          sc_next[p] = load16(s_rsrc, scale_voff(p, g + 1, 0), 0);
+          sc_keep[p] = load16(s_rsrc, scale_voff(p, g + 1, 1), 0);
         }
       }
 #pragma unroll
       for (int p = 0; p < kXPieces; ++p)
-        xr[i % kXAhead][p] = load16(x_rsrc, x_voff[p],
-                                    static_cast<uint32_t>(min(step + kXAhead, n_steps - 1)) *
-                                        (kChunkK * 2));
-      load_weights(ahead, w_rsrc, w_voff, min(step + 1, n_steps - 1));
+        xr[i % kXAhead][p] = load16(x_rsrc, step + kXAhead < n_steps ? x_voff[p] : kNoLoad,
+                                    static_cast<uint32_t>(step + kXAhead) * (kChunkK * 2));
+      load_weights(ahead, w_rsrc, w_voff, step + 1, n_steps);
       if (tile0_on) {
         const uint8_t *srow = ss[i / kStageSteps] + s_read + 16 * (i % kStageSteps);
         const uint32_t sc0 = *reinterpret_cast<const uint32_t *>(srow);
