@@ -15,6 +15,10 @@
 //     rows of one expert over the whole K, and loops over that expert's sorted rows 16 at
 //     a time (one MFMA tile), so its weight bytes are streamed once per 16 rows (once per
 //     launch for an expert with at most 16 routed rows). Three blocks share a CU.
+//     Workgroups are dealt to the 8 XCDs round-robin by linear id; the block index is
+//     remapped so that each XCD runs whole experts, and an expert's activation rows are
+//     fetched into one L2 only (measured L2-to-memory reads then equal the algorithmic
+//     bytes).
 //   - Each wave owns two MFMA tiles of 16 weight rows: block rows [16w, 16w + 16) and
 //     [64 + 16w, 64 + 16w + 16). Both tiles multiply the same activation operands, so a
 //     wave reads each staged activation once per 32 weight rows.
@@ -223,7 +227,19 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
 
-  const int e = blockIdx.y;
+  // Workgroups go to the 8 XCDs round-robin by linear id. Remap (a bijection on the
+  // grid) so that each XCD runs whole experts: an expert's activation rows are then
+  // fetched into one L2 only.
+  int e = blockIdx.y, tile = blockIdx.x;
+  {
+    const int T = gridDim.x, total = T * gridDim.y;
+    if ((total & 7) == 0) {
+      const int lin = blockIdx.y * T + blockIdx.x;
+      const int r = (lin & 7) * (total >> 3) + (lin >> 3);
+      e = r / T;
+      tile = r - e * T;
+    }
+  }
   const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_ptrs[e]);
   if (packed == nullptr) return;  // expert not present: its rows keep the caller's values
   const int lo = max(offsets[e], 0);
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   // Weight rows of block row j: base[j / kHalfN] + j % kHalfN. Plain: the block's 128
   // consecutive rows. Fused: 64 gate rows, then the matching 64 up rows.
   const int mi = N / 2;
-  const int row_base0 = blockIdx.x * (kSwiglu ? kHalfN : kBlockN);
+  const int row_base0 = tile * (kSwiglu ? kHalfN : kBlockN);
   const int row_base1 = row_base0 + (kSwiglu ? mi : kHalfN);
   const int row_end0 = kSwiglu ? mi : N;  // rows past it are out (N, mi multiples of 16)
   // This wave's tiles: block rows 16 w + [0, 16) and kHalfN + 16 w + [0, 16).
