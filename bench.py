@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # Counter-measured HBM traffic of the gate_up GEMM, valid only for the kernel source it
 # was measured on (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated with a copy kernel).
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_prefill_subchunk_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                            "grouped_gemm_gate_up_swiglu_prefill_subchunk_hbm_traffic.md")
 KERNEL_SOURCES = ("grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip",
                   "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h",
                   "grouped_nvfp4_w4a16_amd/csrc/swiglu.h")
@@ -56,9 +57,9 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(kernel: str):
     """HBM bytes per gate_up launch from the committed counter summary, or None when the
-    summary is missing or was taken on a different kernel source."""
+    summary is missing, covers another kernel or was taken on a different kernel source."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -68,7 +69,7 @@ def measured_traffic():
         if ":" in line and line.strip().startswith("- `"):
             key, _, val = line.strip()[3:].partition("`:")
             fields[key.strip()] = val.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+    if fields.get("kernel_source_sha256") != kernel_source_sha256() or fields.get("kernel") != kernel:
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -324,7 +325,7 @@ def main():
                     else "moe_w4a16_grouped_gemm_swiglu (gate_up + SwiGLU)")
     roofline = {"kernel": kernel_label, "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel_label),
                 "avg_launch_us": round(float(np.mean(gu_s)) * 1e6, 2),
                 "alg_bytes_per_launch": int(np.mean(gu_alg))}
 
