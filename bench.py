@@ -235,9 +235,8 @@ def main():
         hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
                       ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
 
-    def st_zero(x, ids, wts):
-        if need_zero:  # null down entries: their rows must read as zero in the combine
-            ws.expert_out[:s].zero_()
+    def st_zero(x, ids, wts):  # null down entries: their rows must read as zero in the combine
+        ws.expert_out[:s].zero_()
 
     def st_gate_up(x, ids, wts):
         hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
@@ -257,15 +256,16 @@ def main():
     def st_combine(x, ids, wts):
         hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out)
 
+    stages = [("moe_align", st_align)]
+    if need_zero:
+        stages.append(("zero_expert_out", st_zero))
     if args.unfused:
-        stages = [("moe_align", st_align), ("zero_expert_out", st_zero),
-                  ("grouped_gemm_gate_up", st_gate_up), ("swiglu_clamp", st_swiglu),
-                  ("grouped_gemm_down", st_down), ("moe_combine", st_combine)]
+        stages += [("grouped_gemm_gate_up", st_gate_up), ("swiglu_clamp", st_swiglu)]
+        gu_name = "grouped_gemm_gate_up"
     else:
-        stages = [("moe_align", st_align), ("zero_expert_out", st_zero),
-                  ("grouped_gemm_gate_up_swiglu", st_gate_up_swiglu),
-                  ("grouped_gemm_down", st_down), ("moe_combine", st_combine)]
-    gu_name = stages[2][0]
+        stages.append(("grouped_gemm_gate_up_swiglu", st_gate_up_swiglu))
+        gu_name = "grouped_gemm_gate_up_swiglu"
+    stages += [("grouped_gemm_down", st_down), ("moe_combine", st_combine)]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
 
