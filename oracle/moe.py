@@ -16,6 +16,10 @@ Sources (the pages' own sections):
 - Combine: forward_moe (2026-09-25), the glm5next_moe_combine_indexed launch and the
   comment that the routed rows are expert-sorted and read back through token_to_perm;
   "Zero FIRST" comment of the older forward_moe for the skipped-slot zeros.
+- Router top-k: forward_moe (both pages), the router launch: FP32 logits [rows, E], an
+  optional per-expert bias, top_k, n_group = 1 (the only value accepted), routed_scale
+  and a renormalize flag; -1 marks an unfilled slot. The pages do not print the
+  kernel's arithmetic; router_topk takes the plainest reading (its docstring).
 """
 
 from __future__ import annotations
@@ -143,6 +147,42 @@ def align(topk_ids: np.ndarray, num_experts: int) -> dict:
         "token_to_perm": token_to_perm.reshape(rows, top_k).astype(np.int32),
         "n_invalid": int((~valid).sum()),
     }
+
+
+# ---------------------------------------------------------------------------------------
+# Router top-k
+# ---------------------------------------------------------------------------------------
+
+def router_topk(logits, top_k: int, bias=None, routed_scale: float = 1.0,
+                renormalize: bool = True):
+    """Top-k expert selection of each row of FP32 router logits ``[T, E]``.
+
+    Reading of the pages' router launch (forward_moe): scores are the softmax of the row's
+    logits; the selection key of expert e is its score plus ``bias[e]`` when a bias is
+    given, else the logit itself (softmax is increasing, so this is the same selection
+    without the ties that rounding the scores could create); the top_k largest keys are
+    taken in descending order, equal keys to the lower expert id. The weight of a
+    selected expert is its score, divided by the selected scores' sum when
+    ``renormalize``, times ``routed_scale``. If top_k exceeds E the extra slots are -1
+    with weight 0. Returns ``(ids int32 [T, top_k], weights float64 [T, top_k])``.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    rows, n_exp = lg.shape
+    ids = np.full((rows, top_k), -1, dtype=np.int32)
+    wts = np.zeros((rows, top_k), dtype=np.float64)
+    for r in range(rows):
+        z = np.exp(lg[r] - lg[r].max())
+        scores = z / z.sum()
+        key = scores + np.asarray(bias, dtype=np.float64) if bias is not None else lg[r]
+        # descending key, equal keys in ascending id: a stable sort of -key
+        order = sorted(range(n_exp), key=lambda e: (-key[e], e))
+        sel = order[:min(top_k, n_exp)]
+        w = scores[sel]
+        if renormalize:
+            w = w / w.sum()
+        ids[r, :len(sel)] = sel
+        wts[r, :len(sel)] = w * routed_scale
+    return ids, wts
 
 
 # ---------------------------------------------------------------------------------------

@@ -408,3 +408,77 @@ def test_pages_error_table_is_self_consistent():
     norms = [r["max_abs"] / r["max_abs_over_ref_inf"] for r in t["rows"]]
     assert max(norms) / min(norms) < 1.001
     assert 256 <= norms[0] < 512
+
+
+# ------------------------------------------------------------------------------- router
+
+def test_router_no_bias_is_argsort_of_logits_and_softmax_of_selected():
+    rng = np.random.default_rng(21)
+    lg = rng.standard_normal((40, 33)).astype(np.float32)
+    ids, wts = moe.router_topk(lg, 6)
+    want_ids = np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :6]
+    assert np.array_equal(ids, want_ids)
+    sel = np.take_along_axis(lg.astype(np.float64), want_ids, axis=1)
+    assert np.allclose(wts, scipy.special.softmax(sel, axis=1), rtol=1e-14, atol=0)
+
+
+def test_router_brute_force_small():
+    # every subset of size k of 6 experts: the selection maximises the summed key, and
+    # among equal sums takes the lexicographically smallest id set (ties to lower ids)
+    import itertools
+    rng = np.random.default_rng(22)
+    for trial in range(30):
+        lg = rng.integers(-3, 4, size=(1, 6)).astype(np.float32)  # many equal keys
+        k = int(rng.integers(1, 6))
+        ids, wts = moe.router_topk(lg, k)
+        best = None
+        for sub in itertools.combinations(range(6), k):
+            # rank by the sorted key vector, then by ids: what "k largest, ties to lower id" means
+            kv = sorted((-float(lg[0, e]), e) for e in sub)
+            if best is None or kv < best[0]:
+                best = (kv, sub)
+        assert list(ids[0]) == [e for _, e in best[0]], (lg, k)
+        z = [math.exp(float(lg[0, e])) for e in ids[0]]
+        assert np.allclose(wts[0], [v / sum(z) for v in z], rtol=1e-14)
+
+
+def test_router_equal_logits_ties_and_weights():
+    ids, wts = moe.router_topk(np.zeros((2, 8), np.float32), 3, routed_scale=2.5)
+    assert ids.tolist() == [[0, 1, 2], [0, 1, 2]]
+    assert np.allclose(wts, 2.5 / 3, rtol=1e-15)
+
+
+def test_router_bias_changes_selection_not_weights():
+    lg = np.array([[0.0, 0.0, 5.0, 1.0]], np.float32)
+    bias = np.array([10.0, 0.0, 0.0, 0.0])
+    ids, wts = moe.router_topk(lg, 1, bias=bias)
+    assert ids.tolist() == [[0]] and wts[0, 0] == 1.0  # renormalised over one expert
+    ids, wts = moe.router_topk(lg, 2, bias=bias, renormalize=False)
+    p = scipy.special.softmax(lg[0].astype(np.float64))
+    assert ids.tolist() == [[0, 2]]
+    assert np.allclose(wts[0], [p[0], p[2]], rtol=1e-14)  # scores, not scores + bias
+
+
+def test_router_no_renormalize_is_softmax_over_all_experts():
+    rng = np.random.default_rng(23)
+    lg = rng.standard_normal((5, 12)).astype(np.float32)
+    ids, wts = moe.router_topk(lg, 4, renormalize=False, routed_scale=1.5)
+    p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(wts, 1.5 * np.take_along_axis(p, ids.astype(np.int64), axis=1), rtol=1e-14)
+
+
+def test_router_top_k_beyond_experts_pads():
+    ids, wts = moe.router_topk(np.array([[1.0, 3.0]], np.float32), 4)
+    assert ids.tolist() == [[1, 0, -1, -1]] and wts[0, 2:].tolist() == [0.0, 0.0]
+    assert math.isclose(wts[0, :2].sum(), 1.0, rel_tol=1e-15)
+
+
+@pytest.mark.parametrize("name", ["single_gemm", "layer_e64", "long_prefill"])
+def test_router_matches_workload_routing_recipe(name):
+    # the workloads' FP32 routing recipe (top-k of logits, softmax over the selected ones)
+    # is an independent implementation of the no-bias, renormalised case
+    w = wl.WORKLOADS[name]
+    ids, wts = moe.router_topk(wl.router_logits(w), w.top_k)
+    want_ids, want_w = wl.routing(w)
+    assert np.array_equal(ids, want_ids)
+    assert np.allclose(wts, want_w, rtol=2e-6, atol=0)

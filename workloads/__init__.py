@@ -126,18 +126,23 @@ def softmax_topk_routing(logits: np.ndarray, top_k: int):
     return order.astype(np.int32), wts
 
 
-def routing(w: Workload):
-    """``(topk_ids int32 [T, top_k], topk_weights float32 [T, top_k])`` for all rows."""
+def router_logits(w: Workload) -> np.ndarray:
+    """FP32 router logits ``[T, E]`` of all rows: N(0, 1), or for Zipf routing
+    ``-s ln(rank_e) + Gumbel(0, 1)`` with a seeded rank permutation."""
     rng = _rng(w.seed, _TAG_ROUTE)
     if w.routing == "softmax":
-        logits = rng.standard_normal(size=(w.rows, w.num_experts), dtype=np.float32)
-    elif w.routing == "zipf":
+        return rng.standard_normal(size=(w.rows, w.num_experts), dtype=np.float32)
+    if w.routing == "zipf":
         ranks = _rng(w.seed, _TAG_ZIPF).permutation(w.num_experts) + 1
         gumbel = rng.gumbel(size=(w.rows, w.num_experts))
-        logits = (-w.zipf_s * np.log(ranks)[None, :] + gumbel).astype(np.float32)
-    else:
-        raise ValueError(w.routing)
-    return softmax_topk_routing(logits, w.top_k)
+        return (-w.zipf_s * np.log(ranks)[None, :] + gumbel).astype(np.float32)
+    raise ValueError(w.routing)
+
+
+def routing(w: Workload):
+    """``(topk_ids int32 [T, top_k], topk_weights float32 [T, top_k])`` for all rows: the
+    workload's routing recipe applied to router_logits(w)."""
+    return softmax_topk_routing(router_logits(w), w.top_k)
 
 
 def activations(w: Workload) -> np.ndarray:
