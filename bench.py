@@ -15,7 +15,7 @@ grouped GEMM), timed with HIP events on the stream it runs on. ``cpu_baseline`` 
 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--copy-probe] [--unfused]
+                       [--no-cpu-baseline] [--copy-probe] [--unfused] [--device-router]
 """
 
 from __future__ import annotations
@@ -88,6 +88,9 @@ def parse():
                     help="also run a 1 GiB device copy (counter calibration runs)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the gate_up GEMM and swiglu_clamp as two calls")
+    ap.add_argument("--device-router", action="store_true",
+                    help="start each step from FP32 router logits (moe_router_topk on the "
+                         "device) instead of precomputed top-k ids and weights")
     return ap.parse_args()
 
 
@@ -228,9 +231,16 @@ def main():
 
     stream = torch.cuda.current_stream()
     need_zero = not all(dt.present)
+    cur_chunk = [0]
+    logits_all = (torch.from_numpy(wl.router_logits(w)).cuda() if args.device_router else None)
     s = rows * w.top_k
 
     # The stages of one step, in order; each is timed with HIP events on the stream.
+    def st_router(x, ids, wts):
+        c = cur_chunk[0]
+        hip.moe_router_topk(logits_all[c * rows:(c + 1) * rows], w.top_k, ws.topk_ids,
+                            ws.topk_weights)
+
     def st_align(x, ids, wts):
         hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
                       ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
@@ -256,7 +266,8 @@ def main():
     def st_combine(x, ids, wts):
         hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out)
 
-    stages = [("moe_align", st_align)]
+    stages = [("moe_router_topk", st_router)] if args.device_router else []
+    stages.append(("moe_align", st_align))
     if need_zero:
         stages.append(("zero_expert_out", st_zero))
     if args.unfused:
@@ -271,8 +282,11 @@ def main():
 
     def step(i, events=None):
         c = i % n_chunks
+        cur_chunk[0] = c
         sl = slice(c * rows, (c + 1) * rows)
         ids, wts, x = ids_all[sl], wts_all[sl], x_all[sl]
+        if args.device_router:  # the router writes the workspace's ids and weights
+            ids, wts = ws.topk_ids, ws.topk_weights
         for j, (_, fn) in enumerate(stages):
             if events:
                 events[j].record(stream)
@@ -353,6 +367,7 @@ def main():
                             round(float(np.percentile(step_ms, 90)), 4)],
         "gemms": per_gemm,
         "gate_up_fused_swiglu": not args.unfused,
+        "device_router": bool(args.device_router),
         "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
         "wall_s": round(wall, 4),
         "kernel_us": kern_us,

@@ -24,7 +24,8 @@ import os
 
 __all__ = [
     "load", "MoeError", "moe_align", "moe_w4a16_grouped_gemm", "swiglu_clamp", "moe_combine",
-    "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
+    "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "moe_router_topk",
+    "moe_layer_from_logits", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -33,6 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a1
 EXPORTS = (
     "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
+    "moe_router_topk",
 )
 
 _LIB = None
@@ -56,6 +58,8 @@ _SIGNATURES = {
     "moe_combine": ([_vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
                     ctypes.c_int),
     "moe_w4a16_dequant_bf16": ([_vp, _vp, _f32, _vp, _i32, _i32, _vp], ctypes.c_int),
+    "moe_router_topk": ([_vp, _i64, _i32, _i32, _vp, _i32, _f32, _i32, _vp, _vp, _vp],
+                        ctypes.c_int),
 }
 
 
@@ -205,6 +209,30 @@ def moe_w4a16_grouped_gemm_swiglu(a, table: "ExpertTable", expert_offsets, act, 
         table.k, float(limit), _stream(stream)))
 
 
+def moe_router_topk(logits, top_k: int, topk_ids, topk_weights, bias=None,
+                    routed_scale: float = 1.0, renormalize: bool = True, stream=None) -> None:
+    """Top-k expert ids and weights of each row of FP32 ``logits`` ``[rows, E]`` into
+    ``topk_ids`` int32 and ``topk_weights`` float32, both ``[rows, top_k]`` contiguous."""
+    import torch
+
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda:
+        raise TypeError("logits: expected a 2-D float32 device tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits: rows must be contiguous")
+    rows, n_exp = logits.shape
+    for t, dt, name in ((topk_ids, torch.int32, "topk_ids"), (topk_weights, torch.float32,
+                                                                "topk_weights")):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.numel() < rows * top_k:
+            raise ValueError(f"{name}: expected a contiguous {dt} device tensor of rows * top_k")
+    if bias is not None:
+        _want(bias, torch.float32, "bias")
+        if bias.numel() < n_exp:
+            raise ValueError("bias: needs num_experts entries")
+    _check("moe_router_topk", load().moe_router_topk(
+        _p(logits), logits.stride(0), rows, n_exp, _p(bias), int(top_k), float(routed_scale),
+        1 if renormalize else 0, _p(topk_ids), _p(topk_weights), _stream(stream)))
+
+
 def swiglu_clamp(gate, up, out, limit: float, stream=None) -> None:
     """``out = silu(min(gate, L)) * clamp(up, -L, L)`` over ``[rows, n]`` views."""
     if gate.shape != up.shape or gate.stride() != up.stride():
@@ -317,6 +345,8 @@ class Workspace:
         self.token_to_perm = torch.empty(s, **i32)
         self.active_experts = torch.empty(num_experts, **i32)
         self.counters = torch.empty(2, **i32)
+        self.topk_ids = torch.empty(max_rows, top_k, **i32)  # the device router's output
+        self.topk_weights = torch.empty(max_rows, top_k, dtype=torch.float32, device=device)
         self.gate_up = torch.empty(s, 2 * moe_intermediate, **bf)
         self.act = torch.empty(s, moe_intermediate, **bf)
         self.expert_out = torch.empty(s, hidden, **bf)
@@ -350,3 +380,18 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     moe_w4a16_grouped_gemm(ws.act, down, ws.expert_offsets, ws.expert_out, None, max_rows=s,
                            stream=stream)
     moe_combine(ws.expert_out[:s], ws.token_to_perm, topk_weights, out, shared, stream)
+
+
+def moe_layer_from_logits(x, logits, top_k: int, gate_up: ExpertTable, down: ExpertTable,
+                          moe_intermediate: int, limit: float, ws: Workspace, out, bias=None,
+                          routed_scale: float = 1.0, renormalize: bool = True, shared=None,
+                          stream=None, fused: bool = True) -> None:
+    """The layer from FP32 router logits ``[rows, E]``: moe_router_topk into
+    ``ws.topk_ids`` / ``ws.topk_weights``, then moe_layer."""
+    rows = logits.shape[0]
+    ids, wts = ws.topk_ids[:rows], ws.topk_weights[:rows]
+    if ids.shape[1] != top_k:
+        raise ValueError("the workspace was made for another top_k")
+    moe_router_topk(logits, top_k, ids, wts, bias, routed_scale, renormalize, stream)
+    moe_layer(x, ids, wts, gate_up, down, moe_intermediate, limit, ws, out, shared, stream,
+              fused)

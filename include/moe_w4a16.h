@@ -9,6 +9,8 @@
  *   moe_combine             top-k weighted sum of the expert-sorted rows per token
  *   moe_w4a16_grouped_gemm_swiglu  the gate_up grouped GEMM with swiglu_clamp fused into
  *                           its epilogue (same bits as the two calls in sequence)
+ *   moe_router_topk         router logits -> top-k expert ids and weights (feeds moe_align
+ *                           and moe_combine)
  *
  * Sources (the pages this library follows, by title and section):
  *   [FPG]  "Module forward_prefill_gemm" (glm5next_mlp/forward_prefill_gemm), sections
@@ -59,6 +61,39 @@ const char *moe_w4a16_last_error(void);
 
 /* Largest expert count moe_align accepts (one workgroup holds the histograms). */
 #define MOE_ALIGN_MAX_EXPERTS 2048
+
+/* Limits of moe_router_topk (one wave per row holds the row's logits in registers). */
+#define MOE_ROUTER_MAX_EXPERTS 2048
+#define MOE_ROUTER_MAX_TOPK 64
+
+/*
+ * moe_router_topk - top-k expert selection per row ([FWD] forward_moe, the router launch:
+ * FP32 logits, optional per-expert bias, top_k, n_group 1, routed_scale, renormalize).
+ * The pages do not print the kernel's arithmetic; this is the reading the library takes:
+ *
+ *   scores[e] = softmax(logits[r, :])[e]                                  (FP32)
+ *   key[e]    = scores[e] + bias[e] if bias != NULL, else logits[r, e]
+ *   topk_ids[r, j], j = 0..top_k-1: the top_k largest keys, descending; equal keys go
+ *               to the lower expert id
+ *   topk_weights[r, j] = scores[id] / (renormalize ? sum of the selected scores : 1)
+ *                        * routed_scale
+ *
+ * Without a bias the selection is the top_k logits (softmax is increasing): the same
+ * experts as the top_k scores, without ties made by rounding. The bias shifts only the
+ * selection, never the weights. If top_k > num_experts the extra slots are -1 with
+ * weight 0 (moe_align excludes them). Logits must be finite.
+ *
+ *   logits        float [rows, ld_logits]   in
+ *   bias          float [num_experts] or NULL
+ *   topk_ids      int32 [rows * top_k]      out (row-major, slot j of row r at r*top_k+j)
+ *   topk_weights  float [rows * top_k]      out
+ * Requirements (else MOE_EINVAL): rows >= 0; 1 <= num_experts <= MOE_ROUTER_MAX_EXPERTS;
+ * 1 <= top_k <= MOE_ROUTER_MAX_TOPK; ld_logits >= num_experts; routed_scale finite;
+ * logits, topk_ids and topk_weights non-NULL when rows > 0. rows == 0 enqueues nothing.
+ */
+int moe_router_topk(const float *logits, int64_t ld_logits, int32_t rows, int32_t num_experts,
+                    const float *bias, int32_t top_k, float routed_scale, int32_t renormalize,
+                    int32_t *topk_ids, float *topk_weights, void *stream);
 
 /*
  * moe_align - sort the routed slots by expert ([FWD] Glm5NextMlpWorkspace field docs).

@@ -174,3 +174,23 @@ def test_full_size_layer_sampled_rows(hip, name, rows):
     local = [r - c * w.chunk for r in rows]
     ref = _oracle_rows(w, ids[rows], wts[rows], x_bits[rows], gu, dn, "bf16w")
     assert rel_err(got[local], ref) <= GATE
+
+
+def test_layer_from_router_logits_vs_oracle(hip):
+    """The layer from router logits (device router -> align -> GEMMs -> combine) against
+    the oracle's router feeding the oracle's layer."""
+    w = wl.WORKLOADS["layer_e64"]
+    lg = wl.router_logits(w)
+    x_bits = wl.activations(w)
+    gu, dn, gt, dt = _tables(hip, w)
+    ws = hip.Workspace(w.rows, w.top_k, w.num_experts, w.hidden, w.moe_intermediate)
+    for t in (ws.gate_up, ws.act, ws.expert_out):
+        t.view(torch.int16).fill_(-1)
+    out = torch.empty((w.rows, w.hidden), dtype=torch.bfloat16, device="cuda")
+    hip.moe_layer_from_logits(bf16_dev(x_bits), dev(lg), w.top_k, gt, dt, w.moe_intermediate,
+                              w.limit, ws, out, routed_scale=1.0)
+    torch.cuda.synchronize()
+    ids, wts = moe.router_topk(lg, w.top_k)
+    ref = _oracle_rows(w, ids, wts, x_bits, gu, dn, "bf16w")
+    assert np.array_equal(ws.topk_ids.cpu().numpy(), ids)
+    assert rel_err(f64(out), ref) <= GATE
