@@ -9,7 +9,8 @@ imports, calls or links anything here, and this package shares no code with it.
 Modules:
 - ``codecs``: E2M1 / E4M3FN decode, FP32 -> BF16 round-to-nearest-even.
 - ``moe``: dequant (exact and BF16-weight modes), align, grouped GEMM, SwiGLU clamp,
-  combine, and the whole routed layer.
+  combine, the whole routed layer, the router top-k, and the shared expert (a BF16
+  SwiGLU MLP).
 
 Every function is pinned by a ``-m "not gpu"`` test against something other than
 itself (library routines, closed forms, brute force in exact rationals, worked

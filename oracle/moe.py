@@ -20,6 +20,9 @@ Sources (the pages' own sections):
   optional per-expert bias, top_k, n_group = 1 (the only value accepted), routed_scale
   and a renormalize flag; -1 marks an unfilled slot. The pages do not print the
   kernel's arithmetic; router_topk takes the plainest reading (its docstring).
+- Shared expert: forward_dense (both glm5next_mlp forward.rs pages), a BF16 SwiGLU MLP
+  run once over all rows, and the gemm helper above it (C[M, N] = A[M, K] B[N, K]^T,
+  BF16 in and out); forward_moe passes its output to the combine unscaled.
 """
 
 from __future__ import annotations
@@ -284,3 +287,33 @@ def moe_layer(x, topk_ids, topk_weights, gate_up, down, scale2_gate_up, scale2_d
     expert_out = rnd(expert_out)
     out = combine(expert_out, al["token_to_perm"], topk_weights, shared)
     return out, {"align": al, "c": c, "act": act, "expert_out": expert_out}
+
+
+# ---------------------------------------------------------------------------------------
+# Shared expert
+# ---------------------------------------------------------------------------------------
+
+def dense_mlp(x, gate_w, up_w, down_w, limit: float, mode: str):
+    """The shared expert: ``down(swiglu_clamp(gate(x), up(x)))`` over the rows of ``x``.
+
+    ``x`` is ``[T, H]``; ``gate_w`` and ``up_w`` are ``[I, H]`` and ``down_w`` is ``[H, I]``,
+    each stored the way the pages' gemm takes its B operand (``C = A @ B^T``, B ``[N, K]``).
+    Products in FP64 of the given values::
+
+        gate = x @ gate_w^T,  up = x @ up_w^T,  act = swiglu_clamp(gate, up, limit)
+        out  = act @ down_w^T
+
+    In ``mode="bf16w"`` the buffers the pages keep in BF16 (gate, up, act, and the output
+    itself) are rounded to BF16; ``mode="exact"`` rounds nothing.
+    Returns ``(out, {"gate", "up", "act"})``.
+    """
+    if mode not in ("exact", "bf16w"):
+        raise ValueError(mode)
+    rnd = round_bf16 if mode == "bf16w" else (lambda v: v)
+    x = np.asarray(x, dtype=np.float64)
+    gate = rnd(x @ np.asarray(gate_w, dtype=np.float64).T)
+    up = rnd(x @ np.asarray(up_w, dtype=np.float64).T)
+    act = rnd(swiglu_clamp(gate, up, limit))
+    out = rnd(act @ np.asarray(down_w, dtype=np.float64).T)
+    return out, {"gate": gate, "up": up, "act": act}
+

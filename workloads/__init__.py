@@ -28,6 +28,9 @@ Value recipe (every workload):
 - Zipf routing: ``logit[r, e] = -s * ln(rank_e) + Gumbel(0, 1)`` with ranks a seeded
   permutation of 1..E, so top-k is sampling without replacement with probability
   proportional to ``rank**-s`` (s = 1.1).
+- Shared expert (layer workloads): one BF16 SwiGLU MLP of width ``mi``; gate and up
+  ``[mi, H]``, down ``[H, mi]``, each N(0, 1) / sqrt(fan-in) in FP32 rounded to BF16, so
+  the gate and up values of N(0, 1) rows are of order one (inside the clamp).
 
 Seeds: one ``SeedSequence`` per (workload base seed, tensor tag, index), so any single
 expert's weights can be regenerated on its own.
@@ -40,7 +43,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # tensor tags for spawn keys
-_TAG_X, _TAG_ROUTE, _TAG_GU, _TAG_DN, _TAG_S2GU, _TAG_S2DN, _TAG_ZIPF = range(7)
+_TAG_X, _TAG_ROUTE, _TAG_GU, _TAG_DN, _TAG_S2GU, _TAG_S2DN, _TAG_ZIPF, _TAG_SHARED = range(8)
 
 
 @dataclass(frozen=True)
@@ -179,6 +182,17 @@ def scale2_gate_up(w: Workload) -> np.ndarray:
 
 def scale2_down(w: Workload) -> np.ndarray:
     return _rng(w.seed, _TAG_S2DN).uniform(0.5, 2.0, size=w.num_experts).astype(np.float32)
+
+
+def shared_expert(w: Workload, scale: float = 1.0):
+    """BF16 bits of the shared expert's ``(gate [mi, H], up [mi, H], down [H, mi])``:
+    N(0, 1) * scale / sqrt(fan-in) FP32 draws rounded to BF16."""
+    mi, h = w.moe_intermediate, w.hidden
+    out = []
+    for i, (n, k) in enumerate(((mi, h), (mi, h), (h, mi))):
+        v = _rng(w.seed, _TAG_SHARED, i).standard_normal(size=(n, k), dtype=np.float32)
+        out.append(_to_bf16_bits(v * np.float32(scale / np.sqrt(k))))
+    return tuple(out)
 
 
 def custom(name: str, seed: int, **kw) -> Workload:
