@@ -14,8 +14,14 @@ reads (experts touched by the batch, both projections) divided by the step time;
 grouped GEMM), timed with HIP events on the stream it runs on. ``cpu_baseline`` times the
 CPU oracle on a bounded sample of the same workload.
 
+``shared_expert`` times the shared expert (a BF16 SwiGLU MLP of width moe_intermediate
+over the same rows: moe_dense_gate_up_swiglu_bf16 then moe_dense_gemm_bf16) after the
+timed steps, outside ``value``; ``--with-shared`` runs it inside each step instead and
+feeds its output to the combine.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe] [--unfused] [--device-router]
+                       [--with-shared] [--no-shared]
 """
 
 from __future__ import annotations
@@ -32,13 +38,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 # Counter-measured HBM traffic of the gate_up GEMM, valid only for the kernel source it
 # was measured on (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated with a copy kernel).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "grouped_gemm_gate_up_swiglu_prefill_subchunk_hbm_traffic.md")
 KERNEL_SOURCES = ("grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip",
                   "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h",
-                  "grouped_nvfp4_w4a16_amd/csrc/swiglu.h")
+                  "grouped_nvfp4_w4a16_amd/csrc/swiglu.h",
+                  "grouped_nvfp4_w4a16_amd/csrc/buffer_io.h")
 METRIC = "grouped MoE W4A16 GEMM: HBM GB/s on unique weights + TFLOP/s, 256-row prefill"
 
 
@@ -91,6 +99,11 @@ def parse():
     ap.add_argument("--device-router", action="store_true",
                     help="start each step from FP32 router logits (moe_router_topk on the "
                          "device) instead of precomputed top-k ids and weights")
+    ap.add_argument("--with-shared", action="store_true",
+                    help="run the shared expert inside each step (its output joins the "
+                         "combine)")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the separate shared-expert measurement")
     return ap.parse_args()
 
 
@@ -174,6 +187,54 @@ def cpu_baseline(w, ids_chunk, seconds_budget=15.0):
             "tflops": round(flops / dt / 1e12, 6)}
 
 
+def time_shared_expert(se, x, w, steps, torch, stream):
+    """The shared expert over one batch of rows: the gate/up GEMM with the SwiGLU, then the
+    down GEMM, each launched ``steps`` times back to back between two HIP events on the
+    stream (a pair of events around one launch of a few tens of microseconds would add
+    the event packets' own time to it). Each kernel's roofline bound is the larger of its
+    HBM time (weights + input rows + output rows, once) and its matrix-core time (dense
+    BF16 peak)."""
+    import grouped_nvfp4_w4a16_amd as hip
+
+    rows, hidden, inter = x.shape[0], w.hidden, w.moe_intermediate
+    act, outb = se.act[:rows], se.out[:rows]
+    launches = (lambda: hip.moe_dense_gate_up_swiglu_bf16(x, se.gate_w, se.up_w, act, w.limit),
+                lambda: hip.moe_dense_gemm_bf16(act, se.down_w, outb))
+    for _ in range(3):
+        se(x, w.limit)
+    torch.cuda.synchronize()
+    secs = []
+    for fn in launches:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        secs.append(e0.elapsed_time(e1) / 1000.0 / steps)
+    gu, dn = secs
+
+    def roof(name, secs, wbytes, in_bytes, out_bytes, flops):
+        nbytes = wbytes + in_bytes + out_bytes
+        t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        if t_hbm >= t_mfma:
+            ach, peak, unit, bound = nbytes / secs / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        else:
+            ach, peak, unit, bound = flops / secs / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        return {"kernel": name, "us": round(secs * 1e6, 2), "bound": bound,
+                "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "alg_bytes_per_launch": int(nbytes),
+                "TFLOPs": round(flops / secs / 1e12, 2)}
+
+    return {"rows": rows, "inter": inter, "hidden": hidden,
+            "gate_up_swiglu": roof("moe_dense_gate_up_swiglu_bf16", gu, 2 * inter * hidden * 2,
+                                   rows * hidden * 2, rows * inter * 2,
+                                   2.0 * rows * 2 * inter * hidden),
+            "down": roof("moe_dense_gemm_bf16", dn, hidden * inter * 2, rows * inter * 2,
+                         rows * hidden * 2, 2.0 * rows * hidden * inter),
+            "total_us": round((gu + dn) * 1e6, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -193,6 +254,9 @@ def main():
     hip.load()
     torch.cuda.set_device(0)
     w = wl.WORKLOADS[args.workload]
+    if args.with_shared and w.moe_intermediate == 0:
+        print(f"bench.py: {w.name} is a single GEMM; it has no shared expert", file=sys.stderr)
+        sys.exit(2)
     t_gen = time.perf_counter()
     gt, dt, ids_all, wts_all, x_all, ids_host = upload_workload(hip, w, torch)
     print(f"bench: uploaded {w.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
@@ -231,6 +295,12 @@ def main():
 
     stream = torch.cuda.current_stream()
     need_zero = not all(dt.present)
+    se = None
+    if (args.with_shared or not args.no_shared) and w.moe_intermediate > 0:
+        sg, su, sd = (torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+                      for b in wl.shared_expert(w))
+        se = hip.SharedExpert(sg, su, sd, rows)
+    shared_out = [None]
     cur_chunk = [0]
     logits_all = (torch.from_numpy(wl.router_logits(w)).cuda() if args.device_router else None)
     s = rows * w.top_k
@@ -263,8 +333,11 @@ def main():
         hip.moe_w4a16_grouped_gemm(ws.act, dt, ws.expert_offsets, ws.expert_out, None,
                                    max_rows=s)
 
+    def st_shared(x, ids, wts):
+        shared_out[0] = se(x, w.limit)
+
     def st_combine(x, ids, wts):
-        hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out)
+        hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out, shared_out[0])
 
     stages = [("moe_router_topk", st_router)] if args.device_router else []
     stages.append(("moe_align", st_align))
@@ -276,7 +349,14 @@ def main():
     else:
         stages.append(("grouped_gemm_gate_up_swiglu", st_gate_up_swiglu))
         gu_name = "grouped_gemm_gate_up_swiglu"
-    stages += [("grouped_gemm_down", st_down), ("moe_combine", st_combine)]
+    stages.append(("grouped_gemm_down", st_down))
+    if args.with_shared:
+        stages.append(("shared_expert", st_shared))
+        # its BF16 weights are unique weight bytes of the step too
+        for c in range(n_chunks):
+            step_bytes[c] += 3 * mi * hidden * 2
+            step_flops[c] += 2.0 * rows * 3 * mi * hidden
+    stages.append(("moe_combine", st_combine))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
 
@@ -343,6 +423,10 @@ def main():
                 "avg_launch_us": round(float(np.mean(gu_s)) * 1e6, 2),
                 "alg_bytes_per_launch": int(np.mean(gu_alg))}
 
+    shared = None
+    if se is not None and not args.with_shared:
+        shared = time_shared_expert(se, x_all[:rows], w, args.steps, torch, stream)
+
     if args.copy_probe:  # a plain copy of known size, for scaling HBM counters
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -368,6 +452,8 @@ def main():
         "gemms": per_gemm,
         "gate_up_fused_swiglu": not args.unfused,
         "device_router": bool(args.device_router),
+        "shared_expert_in_step": bool(args.with_shared),
+        "shared_expert": shared,
         "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
         "wall_s": round(wall, 4),
         "kernel_us": kern_us,

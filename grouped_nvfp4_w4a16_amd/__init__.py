@@ -11,10 +11,14 @@ Calls (same names as the C ABI):
 - ``moe_w4a16_grouped_gemm``: one launch over all experts.
 - ``swiglu_clamp``, ``moe_combine``.
 - ``moe_w4a16_dequant_bf16``: diagnostic, the BF16 weight operand the GEMM decodes.
+- ``moe_router_topk``: router logits -> top-k ids and weights.
+- ``moe_dense_gate_up_swiglu_bf16``, ``moe_dense_gemm_bf16``: the shared expert's BF16
+  GEMMs (gate/up with the SwiGLU in the epilogue, then down).
 
 Helpers: ``ExpertTable`` (device pointer table of per-expert NVFP4 weights),
-``Workspace`` (every buffer of one layer call, allocated once) and ``moe_layer`` (the
-calls of one routed layer in order).
+``Workspace`` (every buffer of one layer call, allocated once), ``SharedExpert`` (the
+shared expert's weights and buffers) and ``moe_layer`` (the calls of one routed layer in
+order).
 """
 
 from __future__ import annotations
@@ -26,6 +30,7 @@ __all__ = [
     "load", "MoeError", "moe_align", "moe_w4a16_grouped_gemm", "swiglu_clamp", "moe_combine",
     "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "moe_router_topk",
     "moe_layer_from_logits", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
+    "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "SharedExpert",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -34,7 +39,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a1
 EXPORTS = (
     "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
-    "moe_router_topk",
+    "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
 )
 
 _LIB = None
@@ -60,6 +65,10 @@ _SIGNATURES = {
     "moe_w4a16_dequant_bf16": ([_vp, _vp, _f32, _vp, _i32, _i32, _vp], ctypes.c_int),
     "moe_router_topk": ([_vp, _i64, _i32, _i32, _vp, _i32, _f32, _i32, _vp, _vp, _vp],
                         ctypes.c_int),
+    "moe_dense_gemm_bf16": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
+                            ctypes.c_int),
+    "moe_dense_gate_up_swiglu_bf16": (
+        [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp], ctypes.c_int),
 }
 
 
@@ -284,7 +293,67 @@ def moe_w4a16_dequant_bf16(packed, scales, scale2: float, out, stream=None) -> N
         _p(packed), _p(scales), float(scale2), _p(out), n, k, _stream(stream)))
 
 
+def moe_dense_gemm_bf16(a, b, c, stream=None) -> None:
+    """``c[m, n] = a[m, :] @ b[n, :]`` (BF16 in and out, FP32 accumulation) over
+    ``a [M, K]``, ``b [N, K]`` and ``c [M, N]`` row-major views."""
+    a, lda = _bf16_matrix(a, "a")
+    b, ldb = _bf16_matrix(b, "b")
+    c, ldc = _bf16_matrix(c, "c")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(c.shape) != (m, n):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    _check("moe_dense_gemm_bf16", load().moe_dense_gemm_bf16(
+        _p(a), lda, _p(b), ldb, _p(c), ldc, m, n, k, _stream(stream)))
+
+
+def moe_dense_gate_up_swiglu_bf16(a, gate_w, up_w, act, limit: float, stream=None) -> None:
+    """``act = swiglu_clamp(bf16(a @ gate_w^T), bf16(a @ up_w^T))`` in one launch over
+    ``a [M, K]``, ``gate_w`` and ``up_w [I, K]`` (same strides) and ``act [M, I]``."""
+    a, lda = _bf16_matrix(a, "a")
+    gate_w, ldw = _bf16_matrix(gate_w, "gate_w")
+    up_w, ldw_up = _bf16_matrix(up_w, "up_w")
+    act, ld_act = _bf16_matrix(act, "act")
+    m, k = a.shape
+    inter = gate_w.shape[0]
+    if tuple(up_w.shape) != tuple(gate_w.shape) or ldw_up != ldw:
+        raise ValueError("gate_w and up_w must have the same shape and strides")
+    if gate_w.shape[1] != k or tuple(act.shape) != (m, inter):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, gate_w {tuple(gate_w.shape)}, "
+                         f"act {tuple(act.shape)}")
+    _check("moe_dense_gate_up_swiglu_bf16", load().moe_dense_gate_up_swiglu_bf16(
+        _p(a), lda, _p(gate_w), _p(up_w), ldw, _p(act), ld_act, m, inter, k, float(limit),
+        _stream(stream)))
+
+
 # ----------------------------------------------------------------------------- helpers
+
+class SharedExpert:
+    """The shared expert: BF16 ``gate_w``, ``up_w`` ``[I, H]`` and ``down_w`` ``[H, I]``
+    device tensors, plus its activation and output buffers for up to ``max_rows`` rows.
+    Calling it runs moe_dense_gate_up_swiglu_bf16 then moe_dense_gemm_bf16 and returns the
+    ``[rows, H]`` output view (the combine's ``shared`` term)."""
+
+    def __init__(self, gate_w, up_w, down_w, max_rows: int):
+        import torch
+
+        inter, hidden = gate_w.shape
+        if tuple(up_w.shape) != (inter, hidden) or tuple(down_w.shape) != (hidden, inter):
+            raise ValueError("expected gate_w, up_w [I, H] and down_w [H, I]")
+        self.gate_w, self.up_w, self.down_w = gate_w, up_w, down_w
+        self.inter, self.hidden = inter, hidden
+        self.act = torch.empty(max_rows, inter, dtype=torch.bfloat16, device=gate_w.device)
+        self.out = torch.empty(max_rows, hidden, dtype=torch.bfloat16, device=gate_w.device)
+
+    def __call__(self, x, limit: float, stream=None):
+        rows = x.shape[0]
+        if rows > self.act.shape[0]:
+            raise ValueError(f"{rows} rows exceed the {self.act.shape[0]} the buffers hold")
+        act, out = self.act[:rows], self.out[:rows]
+        moe_dense_gate_up_swiglu_bf16(x, self.gate_w, self.up_w, act, limit, stream)
+        moe_dense_gemm_bf16(act, self.down_w, out, stream)
+        return out
+
 
 class ExpertTable:
     """Device pointer table of one NVFP4 projection for all experts.
@@ -362,7 +431,9 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     calls (same bits).
     ``ws.expert_out`` is zeroed first so experts that are not present add zero. When every
     down-projection entry is present the down GEMM writes every row the combine reads
-    (each valid slot's row lies in its expert's segment), so the zeroing is skipped."""
+    (each valid slot's row lies in its expert's segment), so the zeroing is skipped.
+    ``shared`` is the combine's shared term: a ``[rows, H]`` BF16 tensor, or a
+    ``SharedExpert``, which is then run over ``x`` after the routed experts."""
     rows, top_k = topk_ids.shape
     s = rows * top_k
     moe_align(topk_ids, gate_up.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
@@ -379,6 +450,8 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
         swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], limit, stream)
     moe_w4a16_grouped_gemm(ws.act, down, ws.expert_offsets, ws.expert_out, None, max_rows=s,
                            stream=stream)
+    if isinstance(shared, SharedExpert):
+        shared = shared(x, limit, stream)
     moe_combine(ws.expert_out[:s], ws.token_to_perm, topk_weights, out, shared, stream)
 
 

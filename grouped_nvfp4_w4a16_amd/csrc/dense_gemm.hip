@@ -1,0 +1,348 @@
+// moe_dense_gemm_bf16 and moe_dense_gate_up_swiglu_bf16: the shared expert's BF16 GEMMs.
+//
+// What they compute follows forward_dense and the gemm helper above it (both
+// glm5next_mlp forward.rs pages): C[M, N] = A[M, K] B[N, K]^T with BF16 operands and
+// output and FP32 accumulation, for the gate, up and down projections of the shared
+// expert, a BF16 SwiGLU MLP run once over all rows. The gate/up form applies the clamped
+// SwiGLU (swiglu.h) to the BF16-rounded gate and up sums in its epilogue, so its output
+// has the bits of the two GEMMs followed by swiglu_clamp.
+//
+// gfx950 design:
+//   - A block of 4 wave64s owns a tile of 16 kMT rows of A by 16 kNT rows of B (output
+//     columns) over the whole K. The waves split K, not the tile: wave w takes the 64-k
+//     chunks w, w + 4, w + 8, ..., so no operand is shared between waves and the main
+//     loop needs neither LDS nor barriers. Each lane loads its MFMA operands straight
+//     from memory with raw buffer loads (16 rows x 64 contiguous bytes per instruction),
+//     kRing chunks ahead in a register ring; the four waves together read 512
+//     contiguous bytes of every row at a time.
+//   - v_mfma_f32_16x16x32_bf16 with the B rows (weights) as the MFMA A operand and the A
+//     rows (tokens) as the MFMA B operand: a lane then holds 4 consecutive output
+//     columns of one row.
+//   - The four FP32 partial tiles are summed through LDS in wave order (the same order
+//     for every tile shape, so the gate/up form reproduces the plain GEMM's sums bit for
+//     bit) and written as BF16, 16 lanes per 128 bytes of an output row.
+//   - Rows of A past M and rows of B past N lie outside their buffer resource and read
+//     zeros; their outputs are not stored.
+//   - Block order: workgroups are dealt to the 8 XCDs round-robin by linear id. When the
+//     column tiles divide by 8, the blocks that share B rows (one column tile, all row
+//     tiles) are dealt to one XCD back to back, so each weight line is fetched into one
+//     L2 and hits there for the other row tiles.
+#include "buffer_io.h"
+#include "common.h"
+#include "nvfp4_decode.h"  // moe::pack_bf16x2
+#include "swiglu.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+using moe::kNoLoad;
+using moe::load16;
+using moe::make_rsrc;
+using moe::u32x4_t;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kChunkK = 64;            // k per chunk: two MFMA k-steps of 32
+constexpr int kChunkBytes = kChunkK * 2;
+constexpr int kPad = 4;                // floats of padding per partial-tile row in LDS
+
+// One lane's operands of one chunk: per 16-row tile, 2 x 8 BF16 (k 8 kb + [0, 8) of each
+// 32-k half).
+template <int kMT, int kNT>
+struct Chunk {
+  u32x4_t w[kNT][2];  // B rows (weights)
+  u32x4_t x[kMT][2];  // A rows (tokens)
+};
+
+// Loads the wave's j-th chunk (k chunk `c`); past the wave's last chunk (`live` false)
+// every offset is kNoLoad: zeros, no traffic. B tiles [0, kSplit) read through `w_lo`,
+// the others through `w_hi` (the gate and up weights of the gate/up form).
+template <int kMT, int kNT, int kSplit>
+__device__ __forceinline__ void load_chunk(Chunk<kMT, kNT> &ch, __amdgpu_buffer_rsrc_t w_lo,
+                                           __amdgpu_buffer_rsrc_t w_hi, const uint32_t *w_voff,
+                                           __amdgpu_buffer_rsrc_t xr, const uint32_t *x_voff,
+                                           int c, bool live) {
+  const uint32_t soff = live ? static_cast<uint32_t>(c) * kChunkBytes : 0u;
+  // Offsets stay below 2^30, so setting bit 31 moves them past the end (no branch).
+  const uint32_t dead = live ? 0u : kNoLoad;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    const uint32_t v = w_voff[t] | dead;
+    ch.w[t][0] = load16(t < kSplit ? w_lo : w_hi, v, soff);
+    ch.w[t][1] = load16(t < kSplit ? w_lo : w_hi, v + 64, soff);
+  }
+#pragma unroll
+  for (int t = 0; t < kMT; ++t) {
+    const uint32_t v = x_voff[t] | dead;
+    ch.x[t][0] = load16(xr, v, soff);
+    ch.x[t][1] = load16(xr, v + 64, soff);
+  }
+}
+
+template <int kMT, int kNT>
+__device__ __forceinline__ void mma_chunk(const Chunk<kMT, kNT> &ch, f32x4_t (&acc)[kMT][kNT]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, ch.w[nt][h]), __builtin_bit_cast(bf16x8_t, ch.x[mt][h]),
+            acc[mt][nt], 0, 0, 0);
+}
+
+// kSwiglu = false: c[m, n] = sum_k a[m, k] b0[n, k] for n < N.
+// kSwiglu = true: N = inter; the block's first 8 kNT tile rows are gate rows of b0, the
+// other 8 kNT the same rows of b1 (up), and c[m, j] = swiglu(gate sum, up sum) of row j.
+template <int kMT, int kNT, int kRing, bool kSwiglu>
+__global__ __launch_bounds__(kThreads, 2) void dense_gemm_kernel(
+    const uint16_t *__restrict__ a, int64_t lda, int32_t M, const uint16_t *__restrict__ b0,
+    const uint16_t *__restrict__ b1, int64_t ldb, uint16_t *__restrict__ c, int64_t ldc,
+    int32_t N, int32_t K, float limit) {
+  constexpr int BM = 16 * kMT, BN = 16 * kNT;
+  constexpr int kRowF = BN + kPad;
+  static_assert(!kSwiglu || kNT % 2 == 0, "gate and up halves");
+  __shared__ __attribute__((aligned(16))) float red[kWaves][BM][kRowF];
+
+  // Block -> (row tile, column tile). Column tiles of one XCD: xcd, xcd + 8, ...
+  const int MT = gridDim.y, NT = gridDim.x;
+  int mt_blk, nt_blk;
+  {
+    const int lin = blockIdx.y * NT + blockIdx.x;
+    if ((NT & 7) == 0) {
+      const int xcd = lin & 7, seq = lin >> 3;
+      mt_blk = seq % MT;
+      nt_blk = (seq / MT) * 8 + xcd;
+    } else {
+      mt_blk = lin % MT;
+      nt_blk = lin / MT;
+    }
+  }
+  const int m0 = mt_blk * BM;
+  // First B row of the block (kSwiglu: in b0 and b1 each).
+  const int n0 = nt_blk * (kSwiglu ? BN / 2 : BN);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kb = lane >> 4;
+  const uint32_t xrow_bytes = static_cast<uint32_t>(lda) * 2u;
+  const uint32_t wrow_bytes = static_cast<uint32_t>(ldb) * 2u;
+
+  // Resources start at the tile's first row and end after its last valid row.
+  const int m_valid = min(BM, M - m0);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(a + static_cast<int64_t>(m0) * lda, static_cast<uint32_t>(m_valid) * xrow_bytes);
+  __amdgpu_buffer_rsrc_t wr, wr_up;
+  uint32_t w_voff[kNT];
+  {
+    const int rows_b = kSwiglu ? BN / 2 : BN;
+    const int n_valid = min(rows_b, N - n0);
+    wr = make_rsrc(b0 + static_cast<int64_t>(n0) * ldb, static_cast<uint32_t>(n_valid) * wrow_bytes);
+    wr_up = kSwiglu ? make_rsrc(b1 + static_cast<int64_t>(n0) * ldb,
+                                static_cast<uint32_t>(n_valid) * wrow_bytes)
+                    : wr;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      const int row = kSwiglu ? (t % (kNT / 2)) * 16 + r16 : t * 16 + r16;
+      w_voff[t] = static_cast<uint32_t>(row) * wrow_bytes + 16u * kb;
+    }
+  }
+  uint32_t x_voff[kMT];
+#pragma unroll
+  for (int t = 0; t < kMT; ++t) x_voff[t] = static_cast<uint32_t>(t * 16 + r16) * xrow_bytes + 16u * kb;
+
+  f32x4_t acc[kMT][kNT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // This wave's chunks: k chunk wave + 4 j for j < n_w.
+  const int n_chunks = K / kChunkK;
+  const int n_w = wave < n_chunks ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
+  constexpr int kSplit = kSwiglu ? kNT / 2 : kNT;
+
+  Chunk<kMT, kNT> ring[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r)
+    load_chunk<kMT, kNT, kSplit>(ring[r], wr, wr_up, w_voff, xr, x_voff, wave + kWaves * r,
+                                 r < n_w);
+  int j = 0;
+  // Every load in the loop is unconditional (past the wave's last chunk it reads
+  // nothing): a load behind a branch leaves the wait counters unknown at the join and
+  // the compiler then drains them all.
+  for (; j + kRing <= n_w; j += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      mma_chunk<kMT, kNT>(ring[r], acc);
+      const int jn = j + r + kRing;
+      load_chunk<kMT, kNT, kSplit>(ring[r], wr, wr_up, w_voff, xr, x_voff, wave + kWaves * jn,
+                                   jn < n_w);
+      // Keep the refill here: scheduled after the next slot's products, it would make
+      // them wait for every load in flight.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // The last n_w - j < kRing chunks are already in ring[0 .. n_w - j).
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r)
+    if (j + r < n_w) mma_chunk<kMT, kNT>(ring[r], acc);
+
+  // acc[mt][nt][i]: row m0 + 16 mt + r16, B row (tile column) 16 nt + 4 kb + i.
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+      *reinterpret_cast<f32x4_t *>(&red[wave][16 * mt + r16][16 * nt + 4 * kb]) = acc[mt][nt];
+  __syncthreads();
+
+  // Sum the partials in wave order; one unit = 4 consecutive output columns of one row.
+  constexpr int kOutCols = kSwiglu ? BN / 2 : BN;
+  constexpr int kUnitsPerRow = kOutCols / 4;
+  for (int u = tid; u < BM * kUnitsPerRow; u += kThreads) {
+    const int m = u / kUnitsPerRow, q = u % kUnitsPerRow;
+    const int row = m0 + m, col = n0 + 4 * q;
+    if (row >= M || col >= N) continue;
+    f32x4_t s = *reinterpret_cast<const f32x4_t *>(&red[0][m][4 * q]);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += *reinterpret_cast<const f32x4_t *>(&red[w][m][4 * q]);
+    uint2 v;
+    if (kSwiglu) {
+      f32x4_t su = *reinterpret_cast<const f32x4_t *>(&red[0][m][BN / 2 + 4 * q]);
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w)
+        su += *reinterpret_cast<const f32x4_t *>(&red[w][m][BN / 2 + 4 * q]);
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // the BF16 values the two plain GEMMs store, then the SwiGLU
+        const uint32_t gu = moe::pack_bf16x2(s[i], su[i]);
+        o[i] = moe::swiglu_clamp1(__uint_as_float(gu << 16), __uint_as_float(gu & 0xFFFF0000u),
+                                  limit);
+      }
+      v.x = moe::pack_bf16x2(o[0], o[1]);
+      v.y = moe::pack_bf16x2(o[2], o[3]);
+    } else {
+      v.x = moe::pack_bf16x2(s[0], s[1]);
+      v.y = moe::pack_bf16x2(s[2], s[3]);
+    }
+    *reinterpret_cast<uint2 *>(c + static_cast<int64_t>(row) * ldc + col) = v;
+  }
+}
+
+struct Tile {
+  int mt, nt;
+};
+
+// Tile shape for an M x N problem. Each CU streams its blocks' operands through its L1
+// at a roughly fixed rate (limited by the misses it can keep in flight), so the time goes
+// with the rows of A and B one CU loads: (blocks per CU, rounded up) x (16 kMT + 16 kNT)
+// rows of K. The shape with the fewest such rows wins; ties go to the larger tile.
+Tile pick_tile(int M, int N, bool swiglu, int cus) {
+  static const Tile kTiles[] = {{4, 4}, {4, 2}, {2, 4}, {2, 2}, {1, 4}, {1, 2}};
+  Tile best = kTiles[0];
+  long long best_cost = -1;
+  for (const Tile &t : kTiles) {
+    if (t.mt > 1 && M <= 16 * (t.mt / 2)) continue;  // a row tile mostly empty
+    const int out_cols = (swiglu ? 8 : 16) * t.nt;
+    const long long blocks = static_cast<long long>((M + 16 * t.mt - 1) / (16 * t.mt)) *
+                             ((N + out_cols - 1) / out_cols);
+    const long long cost = (blocks + cus - 1) / cus * (16 * t.mt + 16 * t.nt);
+    if (best_cost < 0 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus > 0 ? cus : 256;
+}
+
+template <int kMT, int kNT, bool kSwiglu>
+int launch_tile(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0, const uint16_t *b1,
+                int64_t ldb, uint16_t *c, int64_t ldc, int32_t n, int32_t k, float limit,
+                void *stream) {
+  const int bm = 16 * kMT, bn = (kSwiglu ? 8 : 16) * kNT;
+  const dim3 grid(static_cast<unsigned>((n + bn - 1) / bn), static_cast<unsigned>((m + bm - 1) / bm));
+  return moe::launch(kSwiglu ? "moe_dense_gate_up_swiglu_bf16" : "moe_dense_gemm_bf16",
+                     dense_gemm_kernel<kMT, kNT, 2, kSwiglu>, grid, dim3(kThreads), 0, stream, a,
+                     lda, m, b0, b1, ldb, c, ldc, n, k, limit);
+}
+
+template <bool kSwiglu>
+int dispatch(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0, const uint16_t *b1,
+             int64_t ldb, uint16_t *c, int64_t ldc, int32_t n, int32_t k, float limit,
+             void *stream) {
+  const Tile t = pick_tile(m, n, kSwiglu, device_cus());
+#define MOE_DENSE_TILE(MT_, NT_)                                                        \
+  if (t.mt == MT_ && t.nt == NT_)                                                       \
+    return launch_tile<MT_, NT_, kSwiglu>(a, lda, m, b0, b1, ldb, c, ldc, n, k, limit, \
+                                          stream);
+  MOE_DENSE_TILE(4, 4)
+  MOE_DENSE_TILE(4, 2)
+  MOE_DENSE_TILE(2, 4)
+  MOE_DENSE_TILE(2, 2)
+  MOE_DENSE_TILE(1, 4)
+  MOE_DENSE_TILE(1, 2)
+#undef MOE_DENSE_TILE
+  moe::set_error("dense gemm: no kernel for tile %dx%d", t.mt, t.nt);
+  return MOE_EINVAL;
+}
+
+// Shared argument checks: sizes, strides, alignment and the 32-bit buffer ranges.
+int check_dense_args(const char *name, const void *a, int64_t lda, const void *b0,
+                     const void *b1, int64_t ldb, const void *c, int64_t ldc, int32_t m,
+                     int32_t n, int32_t k) {
+  MOE_REQUIRE(m >= 0 && n >= 0 && k >= 0, "%s: negative size", name);
+  MOE_REQUIRE(n % 16 == 0, "%s: the output width must be a multiple of 16 (got %d)", name, n);
+  MOE_REQUIRE(k % kChunkK == 0, "%s: K must be a multiple of %d (got %d)", name, kChunkK, k);
+  MOE_REQUIRE(lda >= k && ldb >= k && ldc >= n, "%s: a leading dimension is below its width",
+              name);
+  MOE_REQUIRE(lda % 8 == 0 && ldb % 8 == 0 && ldc % 4 == 0,
+              "%s: lda and ldb must be multiples of 8, ldc of 4", name);
+  // A block's resource spans at most 64 rows of A or B.
+  MOE_REQUIRE(lda <= (1LL << 23) && ldb <= (1LL << 23),
+              "%s: lda and ldb must be at most 2^23 elements", name);
+  if (m == 0 || n == 0) return MOE_OK;
+  MOE_REQUIRE(c != nullptr, "%s: c is NULL", name);
+  if (k == 0) return MOE_OK;  // the empty sum: a and b are not read
+  MOE_REQUIRE(a && b0 && b1, "%s: a required pointer is NULL", name);
+  MOE_REQUIRE(moe::aligned16(a) && moe::aligned16(b0) && moe::aligned16(b1),
+              "%s: a and b must be 16-byte aligned", name);
+  MOE_REQUIRE((reinterpret_cast<uintptr_t>(c) & 7u) == 0, "%s: c must be 8-byte aligned", name);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_dense_gemm_bf16(const uint16_t *a, int64_t lda, const uint16_t *b,
+                                   int64_t ldb, uint16_t *c, int64_t ldc, int32_t m, int32_t n,
+                                   int32_t k, void *stream) {
+  moe::clear_error();
+  const int rc = check_dense_args("moe_dense_gemm_bf16", a, lda, b, b, ldb, c, ldc, m, n, k);
+  if (rc != MOE_OK || m == 0 || n == 0) return rc;
+  return dispatch<false>(a, lda, m, b, b, ldb, c, ldc, n, k, 0.f, stream);
+}
+
+extern "C" int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda,
+                                             const uint16_t *gate_w, const uint16_t *up_w,
+                                             int64_t ldw, uint16_t *act, int64_t ld_act,
+                                             int32_t m, int32_t inter, int32_t k, float limit,
+                                             void *stream) {
+  moe::clear_error();
+  const int rc = check_dense_args("moe_dense_gate_up_swiglu_bf16", a, lda, gate_w, up_w, ldw, act,
+                                  ld_act, m, inter, k);
+  if (rc != MOE_OK) return rc;
+  MOE_REQUIRE(limit == limit && limit > 0.f,
+              "moe_dense_gate_up_swiglu_bf16: limit must be positive (got %g)",
+              static_cast<double>(limit));
+  if (m == 0 || inter == 0) return MOE_OK;
+  return dispatch<true>(a, lda, m, gate_w, up_w, ldw, act, ld_act, inter, k, limit, stream);
+}

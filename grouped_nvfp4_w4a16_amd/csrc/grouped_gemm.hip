@@ -48,6 +48,7 @@
 //     sums of the same 4 columns; both are rounded to BF16 (the values the unfused path
 //     would store) and the clamped SwiGLU (swiglu.h) is applied in registers. The gate_up
 //     output never reaches memory.
+#include "buffer_io.h"
 #include "common.h"
 #include "nvfp4_decode.h"
 #include "swiglu.h"
@@ -56,7 +57,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+using moe::u32x4_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -79,21 +80,9 @@ static_assert(kBlockM * kPiecesPerRow == kXPieces * kThreads, "whole activation 
 static_assert(kBlockN * kStageSteps == kSPieces * kThreads, "whole scale pieces");
 static_assert(kSPieces == kTiles, "one scale piece per thread and tile half");
 
-// Raw buffer access (gfx9 resource word 3): offsets past num_records read as zero
-// without touching memory, which masks padded and invalid rows at no cost. The range
-// check covers the vector offset, not the scalar one, so row offsets always go in the
-// vector offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                          uint32_t soff) {
-  return __builtin_bit_cast(
-      u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
-                                                     static_cast<int>(soff), 0));
-}
+using moe::kNoLoad;
+using moe::load16;
+using moe::make_rsrc;
 
 // One lane's packed weights of a step: per tile, 64 k of one row as two 16-byte loads;
 // the wave reads 16 rows x 64 contiguous bytes per load.
@@ -101,9 +90,6 @@ struct WeightRegs {
   u32x4_t a[kTiles];  // k in [32 kb, 32 kb + 32) of the step
   u32x4_t b[kTiles];  // k in [128 + 32 kb, 128 + 32 kb + 32)
 };
-
-// Past-the-end offset: the load returns zeros and moves no data.
-constexpr uint32_t kNoLoad = 0x80000000u;
 
 // Loads of a step past the last one get kNoLoad, so every load stays unconditional (see
 // the main loop) without re-reading data that L2 may already have evicted.

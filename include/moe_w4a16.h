@@ -11,6 +11,9 @@
  *                           its epilogue (same bits as the two calls in sequence)
  *   moe_router_topk         router logits -> top-k expert ids and weights (feeds moe_align
  *                           and moe_combine)
+ *   moe_dense_gate_up_swiglu_bf16, moe_dense_gemm_bf16
+ *                           the shared expert (a BF16 SwiGLU MLP over all rows), whose
+ *                           output is moe_combine's `shared` term
  *
  * Sources (the pages this library follows, by title and section):
  *   [FPG]  "Module forward_prefill_gemm" (glm5next_mlp/forward_prefill_gemm), sections
@@ -20,7 +23,8 @@
  *   [FWD]  "glm5next_mlp/forward.rs" (the 2026-09-25 metrale_model_arch page): the
  *          Glm5NextMlpWorkspace field docs (sorted_token_ids, sorted_expert_ids,
  *          expert_offsets, token_to_perm, expert_out), swiglu_rows, and forward_moe's
- *          zero-first memset and glm5next_moe_combine_indexed launch.
+ *          zero-first memset and glm5next_moe_combine_indexed launch; forward_dense and
+ *          the gemm helper above it (C = A B^T, BF16 in and out) for the shared expert.
  *
  * Conventions shared by every call:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise. The caller
@@ -229,6 +233,44 @@ int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
                 const int32_t *token_to_perm, const float *topk_weights,
                 const uint16_t *shared, int64_t ld_s, uint16_t *out, int64_t ld_out,
                 int32_t rows, int32_t hidden, int32_t top_k, void *stream);
+
+/*
+ * moe_dense_gemm_bf16 - c[m, n] = bf16( sum_k a[m, k] * b[n, k] ), FP32 accumulation: the
+ * pages' BF16 gemm (C[M, N] = A[M, K] B[N, K]^T) as forward_dense uses it for the shared
+ * expert's down projection ([FWD] forward_dense).
+ *
+ *   a  bf16 [m, lda]   rows (tokens)
+ *   b  bf16 [n, ldb]   weight rows, K contiguous
+ *   c  bf16 [m, ldc]   output
+ * Requirements (else MOE_EINVAL): m, n, k >= 0; n % 16 == 0; k % 64 == 0; lda >= k and
+ * ldb >= k, multiples of 8 and at most 2^23; ldc >= n, a multiple of 4; c 8-byte aligned
+ * and non-NULL when m * n > 0; a and b 16-byte aligned and non-NULL when also k > 0.
+ * m == 0 or n == 0 enqueues nothing; k == 0 writes zeros (a and b are not read).
+ */
+int moe_dense_gemm_bf16(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+                        uint16_t *c, int64_t ldc, int32_t m, int32_t n, int32_t k, void *stream);
+
+/*
+ * moe_dense_gate_up_swiglu_bf16 - the gate and up projections of forward_dense and its
+ * SwiGLU in one launch ([FWD] forward_dense, swiglu_rows):
+ *
+ *   act[m, j] = bf16( swiglu(G, U) ),   j in [0, inter)
+ *   G = bf16(sum_k a[m, k] gate_w[j, k]),   U = bf16(sum_k a[m, k] up_w[j, k])
+ *   swiglu(G, U) = silu(min(G, limit)) * clamp(U, -limit, limit) in FP32, as swiglu_clamp
+ *
+ * Bit-identical to moe_dense_gemm_bf16 with gate_w and with up_w followed by
+ * swiglu_clamp; G and U are never stored.
+ *
+ *   a               bf16 [m, lda]
+ *   gate_w, up_w    bf16 [inter, ldw] each
+ *   act             bf16 [m, ld_act]
+ * Requirements (else MOE_EINVAL): limit > 0; inter % 16 == 0; the requirements of
+ * moe_dense_gemm_bf16 with n = inter, b = gate_w and up_w, c = act.
+ */
+int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda, const uint16_t *gate_w,
+                                  const uint16_t *up_w, int64_t ldw, uint16_t *act,
+                                  int64_t ld_act, int32_t m, int32_t inter, int32_t k,
+                                  float limit, void *stream);
 
 /*
  * moe_w4a16_dequant_bf16 - diagnostic: write the BF16 weight operand the grouped GEMM

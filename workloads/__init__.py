@@ -120,6 +120,11 @@ def bf16_normal(rng: np.random.Generator, shape) -> np.ndarray:
     return _to_bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
 
 
+def bf16_normal_scaled(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    """BF16 bit patterns (uint16) of N(0, 1) FP32 draws times ``std`` (in FP32)."""
+    return _to_bf16_bits(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std))
+
+
 def softmax_topk_routing(logits: np.ndarray, top_k: int):
     """Top-k ids by logit descending (ties to the lower id) and renormalised weights."""
     order = np.argsort(-logits.astype(np.float32), axis=1, kind="stable")[:, :top_k]
