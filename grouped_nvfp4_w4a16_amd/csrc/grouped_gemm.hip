@@ -16,9 +16,10 @@
 //     a time (one MFMA tile), so its weight bytes are streamed once per 16 rows (once per
 //     launch for an expert with at most 16 routed rows). Three blocks share a CU.
 //     Workgroups are dealt to the 8 XCDs round-robin by linear id; the block index is
-//     remapped so that each XCD runs whole experts, and an expert's activation rows are
-//     fetched into one L2 only (measured L2-to-memory reads then equal the algorithmic
-//     bytes).
+//     remapped so that each XCD runs whole experts (XCD x: experts x, x + 8, ...), and an
+//     expert's activation rows are fetched into one L2 only (measured L2-to-memory reads
+//     then equal the algorithmic bytes). Interleaving the experts keeps every XCD busy
+//     when a contiguous range of them is absent or idle.
 //   - Each wave owns two MFMA tiles of 16 weight rows: block rows [16w, 16w + 16) and
 //     [64 + 16w, 64 + 16w + 16). Both tiles multiply the same activation operands, so a
 //     wave reads each staged activation once per 32 weight rows.
@@ -214,14 +215,20 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
 
   // Workgroups go to the 8 XCDs round-robin by linear id. Remap (a bijection on the
-  // grid) so that each XCD runs whole experts: an expert's activation rows are then
-  // fetched into one L2 only.
+  // grid) so that each XCD runs whole experts, an expert's activation rows then being
+  // fetched into one L2 only; with E a multiple of 8, XCD x runs experts x, x + 8, ...,
+  // so a contiguous range of empty or absent experts (an expert-parallel rank's share,
+  // a cold part of the expert range) is spread over all XCDs instead of idling some.
   int e = blockIdx.y, tile = blockIdx.x;
   {
-    const int T = gridDim.x, total = T * gridDim.y;
-    if ((total & 7) == 0) {
-      const int lin = blockIdx.y * T + blockIdx.x;
-      const int r = (lin & 7) * (total >> 3) + (lin >> 3);
+    const int T = gridDim.x, E = gridDim.y;
+    const int lin = blockIdx.y * T + blockIdx.x;
+    if ((E & 7) == 0) {
+      const int q = lin >> 3, el = q / T;
+      tile = q - el * T;
+      e = el * 8 + (lin & 7);
+    } else if (((T * E) & 7) == 0) {
+      const int r = (lin & 7) * ((T * E) >> 3) + (lin >> 3);
       e = r / T;
       tile = r - e * T;
     }
