@@ -29,9 +29,8 @@
 //     instruction), one step ahead in a two-slot register ring, and decodes them in
 //     registers (nvfp4_decode.h) straight into A; no dequantised weight goes through LDS.
 //     The L1 can track only about a step's worth of a CU's weight lines, so a deeper ring
-//     only leaves waves stalled at load issue instead of decoding. The decode takes a
-//     wave-uniform branch per tile: the byte-table path when every block of the tile
-//     allows it, else the exact per-element path.
+//     only leaves waves stalled at load issue instead of decoding. The decode is one
+//     branch-free byte-table path for every scale code (nvfp4_decode.h).
 //   - The gathered activation rows are the B operand (16 rows per MFMA tile). They are
 //     loaded one step ahead into registers and staged per 256-k step in LDS
 //     (double buffered, one barrier per step), shared by the 4 waves, with k permuted
@@ -40,7 +39,7 @@
 //     in LDS 4 steps at a time: the first half goes to LDS at once, the second half waits
 //     in registers for its stage (reading half lines lets L2 evict a line between its two
 //     halves, which doubles the scale traffic). Each block turns every E4M3 code into its
-//     decode tables once (a 256-entry LUT).
+//     decode table once (a 256-entry LUT of the exact BF16 magnitudes for its scale2).
 //   - Output: each lane holds 4 consecutive weight rows of one sorted row per tile -> one
 //     8-byte store of BF16 (round-to-nearest-even).
 //   - SwiGLU-fused form: the weight is the fused gate_up projection (gate rows [0, mi),
@@ -133,25 +132,20 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&w)[4]) {
 }
 
 // Multiply four decoded words into acc against four B operands.
-template <bool kFast>
-__device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Block &b0,
-                                      const moe::Fp4Block &b1, const bf16x8_t *B,
-                                      float scale2, f32x4_t &acc) {
+__device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Table &b0,
+                                      const moe::Fp4Table &b1, const bf16x8_t *B,
+                                      f32x4_t &acc) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t wd[4];
-    if (kFast) {
-      moe::decode8_fast(words[j], j < 2 ? b0 : b1, wd);
-    } else {
-      moe::decode8(words[j], j < 2 ? b0 : b1, scale2, wd);
-    }
+    moe::decode8(words[j], j < 2 ? b0 : b1, wd);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wd), B[j], acc, 0, 0, 0);
   }
 }
 
 // The byte tables of the lane's four blocks (scale codes in the bytes of `sc`, see
 // permute_scales) from the per-block LUT.
-__device__ __forceinline__ void lut_blocks(uint32_t sc, const uint8_t *lut, moe::Fp4Block *blk) {
+__device__ __forceinline__ void lut_blocks(uint32_t sc, const uint8_t *lut, moe::Fp4Table *blk) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const u32x4_t t =
@@ -163,41 +157,16 @@ __device__ __forceinline__ void lut_blocks(uint32_t sc, const uint8_t *lut, moe:
   }
 }
 
-// Byte 0 of lo03 (the table entry of magnitude 0) is zero exactly for codes whose byte
-// tables are valid; the LUT marks the others there.
-__device__ __forceinline__ bool lut_fast(const moe::Fp4Block *blk) {
-  return ((blk[0].lo03 | blk[1].lo03 | blk[2].lo03 | blk[3].lo03) & 0xFFu) == 0;
-}
-
-// Half h of one tile's step (k in [128 h, 128 h + 128)) against the half's B operands.
-__device__ __forceinline__ void tile_half(const u32x4_t &w4, bool fast, uint32_t sc, int h,
-                                          const moe::Fp4Block *blk, const bf16x8_t *B,
-                                          float scale2, f32x4_t &acc) {
-  const uint32_t w[4] = {w4[0], w4[1], w4[2], w4[3]};
-  if (fast) {
-    mfma4<true>(w, blk[2 * h], blk[2 * h + 1], B, scale2, acc);
-  } else {  // some block of the tile needs the exact per-element path
-    float d0, d1;
-    if (h == 0) {
-      moe::e4m3x2_to_f32(sc, d0, d1);
-    } else {
-      moe::e4m3x2_to_f32_hi(sc, d0, d1);
-    }
-    mfma4<false>(w, moe::make_block(d0, scale2), moe::make_block(d1, scale2), B, scale2, acc);
-  }
-}
-
 // The byte tables of every E4M3 scale code for this expert's scale2, one 16-byte entry
-// per code {lo03, lo47, hi03, hi47}; byte 0 of lo03 is set for codes that must take the
-// exact path. Built once per block.
+// per code {lo03, lo47, hi03, hi47}. One code per thread, no loop, so that it is
+// scheduled behind the loads that precede it.
+static_assert(kThreads == 256, "one E4M3 code per thread");
 __device__ __forceinline__ void build_code_table_lut(uint8_t *lut, int tid, float scale2) {
-  for (int c = tid; c < 256; c += kThreads) {
-    float d, unused;
-    moe::e4m3x2_to_f32(static_cast<uint32_t>(c), d, unused);
-    const moe::Fp4Block b = moe::make_block(d, scale2);
-    const u32x4_t t = {b.lo03 | (moe::fast_pq(b.pq) ? 0u : 1u), b.lo47, b.hi03, b.hi47};
-    *reinterpret_cast<u32x4_t *>(lut + c * 16) = t;
-  }
+  float d, unused;
+  moe::e4m3x2_to_f32(static_cast<uint32_t>(tid), d, unused);
+  const moe::Fp4Table b = moe::make_table(d, scale2);
+  const u32x4_t t = {b.lo03, b.lo47, b.hi03, b.hi47};
+  *reinterpret_cast<u32x4_t *>(lut + tid * 16) = t;
 }
 
 // kSwiglu = false: c[s, n] for the N weight rows.
@@ -233,13 +202,19 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       tile = r - e * T;
     }
   }
-  const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_ptrs[e]);
-  if (packed == nullptr) return;  // expert not present: its rows keep the caller's values
-  const int lo = max(offsets[e], 0);
-  const int hi = min(offsets[e + 1], max_rows);
-  if (hi <= lo) return;
-  const uint8_t *scales = reinterpret_cast<const uint8_t *>(scale_ptrs[e]);
+  // All of the expert's metadata in one memory round trip: the empty asm needs every
+  // value before the early exits, so the five loads are issued together instead of one
+  // exit test at a time.
+  const uint64_t packed_u = packed_ptrs[e], scales_u = scale_ptrs[e];
   const float scale2 = scale2s[e];
+  const int off_lo = offsets[e], off_hi = offsets[e + 1];
+  asm volatile("" ::"s"(packed_u), "s"(scales_u), "s"(scale2), "s"(off_lo), "s"(off_hi));
+  const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_u);
+  if (packed == nullptr) return;  // expert not present: its rows keep the caller's values
+  const int lo = max(off_lo, 0);
+  const int hi = min(off_hi, max_rows);
+  if (hi <= lo) return;
+  const uint8_t *scales = reinterpret_cast<const uint8_t *>(scales_u);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -287,28 +262,27 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   };
   // This lane's scale dword of tile 0 within a staged block (tile 1: + kScaleHalfLds).
   const int s_read = (16 * wave + r16) * kScaleRowBytes + 4 * kb;
-  build_code_table_lut(lut, tid, scale2);  // published by the first pass's barrier
 
   for (int m0 = lo; m0 < hi; m0 += kBlockM) {
     const int m_cnt = min(kBlockM, hi - m0);
     // Activation staging: thread -> (row of the pass, 16-byte piece of a step) for rows
     // tid / 32 and 8 + tid / 32. Rows past the pass and out-of-range gather indices read
-    // zeros (offset past the end).
-    uint32_t x_voff[kXPieces];
-    int lds_off[kXPieces];
+    // zeros (offset past the end). The gather indices are loaded first, the step's
+    // weights and scales next, so that only the gather is waited for before the
+    // activation loads can be addressed.
+    int g_row[kXPieces], piece_col[kXPieces], lds_off[kXPieces];
 #pragma unroll
     for (int p = 0; p < kXPieces; ++p) {
       const int piece = tid + p * kThreads;
-      const int piece_row = piece / kPiecesPerRow, piece_col = piece % kPiecesPerRow;
-      lds_off[p] = piece_row * kLdsRowBytes + piece_col * 16;
+      const int piece_row = piece / kPiecesPerRow;
+      piece_col[p] = piece % kPiecesPerRow;
+      lds_off[p] = piece_row * kLdsRowBytes + piece_col[p] * 16;
       int g = -1;
       if (piece_row < m_cnt) {
         const int srow = m0 + piece_row;
         g = gather != nullptr ? gather[srow] : srow;
       }
-      x_voff[p] = (g >= 0 && g < a_rows)
-                      ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) + piece_col * 8u) * 2u
-                      : kNoLoad;
+      g_row[p] = g;
     }
 
     f32x4_t acc[kTiles];
@@ -322,6 +296,18 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     for (int p = 0; p < kSPieces; ++p) {
       sc_next[p] = load16(s_rsrc, scale_voff(p, 0, 0), 0);
       sc_keep[p] = load16(s_rsrc, scale_voff(p, 0, 1), 0);
+    }
+    // The decode tables, built while the first loads are in flight and published by the
+    // barrier below. Later passes write the same values again (every read of the previous
+    // pass is behind its last barrier), which costs less than a branch around it.
+    build_code_table_lut(lut, tid, scale2);
+    uint32_t x_voff[kXPieces];
+#pragma unroll
+    for (int p = 0; p < kXPieces; ++p) {
+      const int g = g_row[p];
+      x_voff[p] = (g >= 0 && g < a_rows)
+                      ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) + piece_col[p] * 8u) * 2u
+                      : kNoLoad;
     }
 #pragma unroll
     for (int p = 0; p < kSPieces; ++p)
@@ -361,19 +347,23 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
         const uint32_t sc0 = *reinterpret_cast<const uint32_t *>(srow);
         const uint32_t sc1 = *reinterpret_cast<const uint32_t *>(srow + kScaleHalfLds);
         const uint8_t *brow = xs[step & 1] + r16 * kLdsRowBytes + 64 * kb;
-        moe::Fp4Block blk0[4], blk1[4];
+        moe::Fp4Table blk0[4], blk1[4];
         lut_blocks(sc0, lut, blk0);
         lut_blocks(sc1, lut, blk1);
-        const bool fast0 = __all(lut_fast(blk0)), fast1 = __all(lut_fast(blk1));
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           bf16x8_t B[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             B[j] = *reinterpret_cast<const bf16x8_t *>(brow + 256 * h + 16 * j);
-          tile_half(h ? cur.b[0] : cur.a[0], fast0, sc0, h, blk0, B, scale2, acc[0]);
-          if (tile1_on)
-            tile_half(h ? cur.b[1] : cur.a[1], fast1, sc1, h, blk1, B, scale2, acc[1]);
+          const u32x4_t &x0 = h ? cur.b[0] : cur.a[0];
+          const uint32_t w0w[4] = {x0[0], x0[1], x0[2], x0[3]};
+          mfma4(w0w, blk0[2 * h], blk0[2 * h + 1], B, acc[0]);
+          if (tile1_on) {
+            const u32x4_t &x1 = h ? cur.b[1] : cur.a[1];
+            const uint32_t w1w[4] = {x1[0], x1[1], x1[2], x1[3]};
+            mfma4(w1w, blk1[2 * h], blk1[2 * h + 1], B, acc[1]);
+          }
         }
       }
 #pragma unroll
@@ -458,13 +448,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
                                                           2 * q);
   float d0, d1;
   moe::e4m3x2_to_f32(sc, d0, d1);
-  const moe::Fp4Block b0 = moe::make_block(d0, scale2), b1 = moe::make_block(d1, scale2);
+  const moe::Fp4Table b0 = moe::make_table(d0, scale2), b1 = moe::make_table(d1, scale2);
   const uint32_t words[4] = {v.x, v.y, v.z, v.w};
   uint4 *dst = reinterpret_cast<uint4 *>(out + static_cast<size_t>(n) * K + q * 32);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t wd[4];
-    moe::decode8(words[j], j < 2 ? b0 : b1, scale2, wd);
+    moe::decode8(words[j], j < 2 ? b0 : b1, wd);
     // (k0,k2) (k4,k6) (k1,k3) (k5,k7) -> (k0,k1) (k2,k3) (k4,k5) (k6,k7)
     uint4 o;
     o.x = moe::byte_perm(wd[2], wd[0], 0x05040100u);

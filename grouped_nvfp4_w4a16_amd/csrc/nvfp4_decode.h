@@ -7,20 +7,19 @@
 // Why not one multiply per element: at HBM speed the chip has only about three VALU
 // operations per weight element to spend, so the decode works on bit patterns.
 //
-// For a 16-k block with scale d (and the expert's scale2) every E2M1 magnitude is
-// m * 2^j with m in {1, 1.5}: {0, .5, 1, 1.5, 2, 3, 4, 6}. The first product v * d is
-// exact in FP32, and scaling by 2^j commutes with both roundings while the values stay
-// normal, so with
-//   P = bf16(fp32(d * scale2)),   Q = bf16(fp32(fp32(1.5 * d) * scale2))
-// the eight BF16 results are {0, P - 0x80, P, Q, P + 0x80, Q + 0x80, P + 0x100, Q + 0x100}
-// as bit patterns (0x80 is one step of the BF16 exponent). Their low and high bytes form
-// two 8-entry byte tables, and v_perm_b32 looks up four elements per instruction; the
-// nibble's sign bit is ORed into the high byte. About 1.75 VALU operations per element
-// plus about 12 per 16-element block for the tables.
+// Within one 16-k block every weight takes one of 16 values: the 8 E2M1 magnitudes
+// {0, .5, 1, 1.5, 2, 3, 4, 6} through the formula, each with either sign. IEEE
+// multiplication and round-to-nearest-even are symmetric in the sign of an operand, so
+// the BF16 value of nibble q is the value of its magnitude code (q & 7) with bit 15
+// flipped when q has its sign bit (bit 3) set. That holds for every block scale and
+// scale2, zero, negative, subnormal and NaN included, so one path serves every block.
 //
-// The identity needs P's exponent field >= 3 (so P - 0x80 and the FP32 value halved stay
-// normal) and Q + 0x100 finite; a zero, negative, subnormal-range, huge or NaN scale fails
-// that check and the block takes the exact per-element path instead.
+// The 8 BF16 magnitudes of a block, each computed by the formula itself, form a table
+// (Fp4Table). Its low and high bytes are two 8-entry byte tables; v_perm_b32 looks up
+// four elements per instruction, the nibble's sign is XORed into the high byte and the
+// bytes are interleaved into BF16 pairs: 14 VALU operations per 8 elements. The table
+// depends only on the scale code and scale2, so a caller that decodes many blocks builds
+// it once per code.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,100 +50,41 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t codes, float &d0, float &
   d1 = v[1];
 }
 
-// Two E4M3 codes in the high 16 bits of `codes` -> FP32 (exact).
-__device__ __forceinline__ void e4m3x2_to_f32_hi(uint32_t codes, float &d0, float &d1) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes), true);
-  d0 = v[0];
-  d1 = v[1];
-}
-
-struct Fp4Block {
-  uint32_t lo03, lo47;  // low bytes of the 8 BF16 magnitudes (codes 0-3, 4-7)
+// The BF16 values of the 8 E2M1 magnitude codes of one block, split into byte tables.
+struct Fp4Table {
+  uint32_t lo03, lo47;  // low bytes of the BF16 values of codes 0-3 and 4-7
   uint32_t hi03, hi47;  // high bytes
-  uint32_t pq;          // P in bits 0-15, Q in bits 16-31
-  float d;              // block scale value, for the exact path
 };
 
-// The bit-pattern identity holds for a block with these P (low half) and Q (high half).
-__device__ __forceinline__ bool fast_pq(uint32_t pq) {
-  return (pq & 0xFFFFu) >= 0x0180u && (pq >> 16) < 0x7E80u;
-}
-
-// Whether it holds for all four blocks: the smallest P and the largest Q decide
-// (packed 16-bit min/max).
-__device__ __forceinline__ bool fast_pq4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-  const u16x2 x = __builtin_bit_cast(u16x2, a), y = __builtin_bit_cast(u16x2, b);
-  const u16x2 z = __builtin_bit_cast(u16x2, c), w = __builtin_bit_cast(u16x2, d);
-  const u16x2 mn = __builtin_elementwise_min(__builtin_elementwise_min(x, y),
-                                             __builtin_elementwise_min(z, w));
-  const u16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(x, y),
-                                             __builtin_elementwise_max(z, w));
-  return mn[0] >= 0x0180u && mx[1] < 0x7E80u;
-}
-
-__device__ __forceinline__ Fp4Block make_block(float d, float scale2) {
-  Fp4Block b;
-  const float p = d * scale2;
-  const float q = (d * 1.5f) * scale2;  // 1.5 * d is exact: d has at most 4 significant bits
-  const uint32_t pq = pack_bf16x2(p, q);  // P in bits 0-15, Q in bits 16-31
-  b.pq = pq;
-  const uint32_t r0 = pq - 0x80u;         // P - 0x80 in the low half
-  const uint32_t r2 = pq + 0x00800080u;   // P + 0x80, Q + 0x80
-  const uint32_t r3 = pq + 0x01000100u;   // P + 0x100, Q + 0x100
-  // codes 0..3: {0, P - 0x80, P, Q};  codes 4..7: {P + 0x80, Q + 0x80, P + 0x100, Q + 0x100}
-  b.lo03 = byte_perm(pq, r0, 0x0604000Cu);
-  b.hi03 = byte_perm(pq, r0, 0x0705010Cu);
-  b.lo47 = byte_perm(r3, r2, 0x06040200u);
-  b.hi47 = byte_perm(r3, r2, 0x07050301u);
-  b.d = d;
-  return b;
-}
-
-// Exact per-element path: the formula itself, one FP32 product at a time.
-__device__ __forceinline__ uint32_t decode_one_exact(uint32_t nib, float d, float scale2) {
-  const uint32_t c = nib & 7u;
-  const float m = (c & 1u) ? 1.5f : 1.0f;
-  float mag = c == 0 ? 0.0f : (c == 1 ? 0.5f : ldexpf(m, static_cast<int>(c >> 1) - 1));
-  const float v = (nib & 8u) ? -mag : mag;
-  const float w = (v * d) * scale2;
-  return pack_bf16x2(w, 0.0f) & 0xFFFFu;
-}
-
-// Fast path of decode8 (fast_pq must hold for the block): 14 VALU operations.
-__device__ __forceinline__ void decode8_fast(uint32_t x, const Fp4Block &b, uint32_t out[4]) {
-  const uint32_t se = x & 0x07070707u;          // magnitude codes of k0, k2, k4, k6
-  const uint32_t so = (x >> 4) & 0x07070707u;   // magnitude codes of k1, k3, k5, k7
-  const uint32_t le = byte_perm(b.lo47, b.lo03, se);
-  const uint32_t he = byte_perm(b.hi47, b.hi03, se) | ((x << 4) & 0x80808080u);
-  const uint32_t lo = byte_perm(b.lo47, b.lo03, so);
-  const uint32_t ho = byte_perm(b.hi47, b.hi03, so) | (x & 0x80808080u);
-  out[0] = byte_perm(he, le, 0x05010400u);
-  out[1] = byte_perm(he, le, 0x07030602u);
-  out[2] = byte_perm(ho, lo, 0x05010400u);
-  out[3] = byte_perm(ho, lo, 0x07030602u);
-}
-
-// Exact path of decode8: the formula one element at a time.
-__device__ __forceinline__ void decode8_exact(uint32_t x, float d, float scale2, uint32_t out[4]) {
-  const auto e = [&](int i) { return decode_one_exact((x >> (4 * i)) & 15u, d, scale2); };
-  out[0] = e(0) | (e(2) << 16);
-  out[1] = e(4) | (e(6) << 16);
-  out[2] = e(1) | (e(3) << 16);
-  out[3] = e(5) | (e(7) << 16);
+// The table of a block with scale d, each entry by the formula: the first product is
+// exact in FP32 (a magnitude has at most 2 significant bits, d at most 4), the second is
+// rounded to FP32, then to BF16 by round-to-nearest-even.
+__device__ __forceinline__ Fp4Table make_table(float d, float scale2) {
+  const auto w = [&](float m) { return (m * d) * scale2; };
+  const uint32_t p01 = pack_bf16x2(w(0.0f), w(0.5f)), p23 = pack_bf16x2(w(1.0f), w(1.5f));
+  const uint32_t p45 = pack_bf16x2(w(2.0f), w(3.0f)), p67 = pack_bf16x2(w(4.0f), w(6.0f));
+  Fp4Table t;
+  t.lo03 = byte_perm(p23, p01, 0x06040200u);
+  t.hi03 = byte_perm(p23, p01, 0x07050301u);
+  t.lo47 = byte_perm(p67, p45, 0x06040200u);
+  t.hi47 = byte_perm(p67, p45, 0x07050301u);
+  return t;
 }
 
 // Decodes the 8 nibbles of x (k = 0..7, even k in the low nibble of each byte) into four
 // BF16 pairs in the order (k0,k2) (k4,k6) (k1,k3) (k5,k7). The matrix-core operand uses
-// this k order; the activations are staged in the same order.
-__device__ __forceinline__ void decode8(uint32_t x, const Fp4Block &b, float scale2,
-                                        uint32_t out[4]) {
-  if (fast_pq(b.pq)) {
-    decode8_fast(x, b, out);
-  } else {
-    decode8_exact(x, b.d, scale2, out);
-  }
+// this k order; the activations are staged in the same order. 14 VALU operations.
+__device__ __forceinline__ void decode8(uint32_t x, const Fp4Table &t, uint32_t out[4]) {
+  const uint32_t se = x & 0x07070707u;          // magnitude codes of k0, k2, k4, k6
+  const uint32_t so = (x >> 4) & 0x07070707u;   // magnitude codes of k1, k3, k5, k7
+  const uint32_t le = byte_perm(t.lo47, t.lo03, se);
+  const uint32_t he = byte_perm(t.hi47, t.hi03, se) ^ ((x << 4) & 0x80808080u);
+  const uint32_t lo = byte_perm(t.lo47, t.lo03, so);
+  const uint32_t ho = byte_perm(t.hi47, t.hi03, so) ^ (x & 0x80808080u);
+  out[0] = byte_perm(he, le, 0x05010400u);
+  out[1] = byte_perm(he, le, 0x07030602u);
+  out[2] = byte_perm(ho, lo, 0x05010400u);
+  out[3] = byte_perm(ho, lo, 0x07030602u);
 }
 
 }  // namespace moe
