@@ -23,6 +23,12 @@ Sources (the pages' own sections):
 - Shared expert: forward_dense (both glm5next_mlp forward.rs pages), a BF16 SwiGLU MLP
   run once over all rows, and the gemm helper above it (C[M, N] = A[M, K] B[N, K]^T,
   BF16 in and out); forward_moe passes its output to the combine unscaled.
+- Decode / verify (a few rows): forward.rs (2026-09-25), the workspace fields u_eid
+  ("union expert ids, -1 = entry unused") and u_slot ("slot per union entry per row, -1 =
+  row absent"), the doc of the row-batched GEMV (C[rows, top_k, N], the union of the rows'
+  selected experts, each expert swept once, the same per-(row, slot) result as one GEMV per
+  row) and the doc of moe_row_groups (which rows share a sweep never changes what a row
+  adds). row_union, union_gemv and moe_layer_decode follow those statements.
 """
 
 from __future__ import annotations
@@ -317,3 +323,109 @@ def dense_mlp(x, gate_w, up_w, down_w, limit: float, mode: str):
     out = rnd(act @ np.asarray(down_w, dtype=np.float64).T)
     return out, {"gate": gate, "up": up, "act": act}
 
+
+
+# ---------------------------------------------------------------------------------------
+# Decode / verify: the union of a few rows' experts, each swept once
+# ---------------------------------------------------------------------------------------
+
+def row_union(topk_ids: np.ndarray, num_experts: int) -> dict:
+    """The union of the experts the rows selected, with each row's slot per union entry.
+
+    Flat slot ``t = r * top_k + j``. A slot is covered when its id is in ``[0, E)`` and no
+    lower slot of the same row holds the same id (a proper top-k never repeats an expert
+    in a row; a repeat is treated like an invalid id). Returns:
+
+    - ``u_eid[rows * top_k]``: the distinct ids of the covered slots in order of first
+      appearance in the flat order, then -1.
+    - ``u_slot[rows * top_k, rows]``: ``u_slot[p, r] = j`` when row r's slot j is covered
+      and selects ``u_eid[p]``, else -1.
+    - ``slot_perm[rows, top_k]``: ``t`` for a covered slot, -1 otherwise (the combine's
+      ``token_to_perm`` over outputs laid out as ``[rows * top_k, N]``).
+    - ``n_union``, ``n_uncovered``.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    rows, top_k = ids.shape
+    n_ids = rows * top_k
+    u_eid = np.full(n_ids, -1, dtype=np.int64)
+    u_slot = np.full((n_ids, rows), -1, dtype=np.int64)
+    slot_perm = np.full((rows, top_k), -1, dtype=np.int64)
+    entry_of = {}  # expert id -> union entry
+    for r in range(rows):
+        for j in range(top_k):
+            e = int(ids[r, j])
+            if not 0 <= e < num_experts:
+                continue
+            if any(int(ids[r, jj]) == e for jj in range(j)):
+                continue  # repeated in this row
+            if e not in entry_of:
+                entry_of[e] = len(entry_of)
+                u_eid[entry_of[e]] = e
+            u_slot[entry_of[e], r] = j
+            slot_perm[r, j] = r * top_k + j
+    return {
+        "u_eid": u_eid.astype(np.int32),
+        "u_slot": u_slot.astype(np.int32),
+        "slot_perm": slot_perm.astype(np.int32),
+        "n_union": len(entry_of),
+        "n_uncovered": int((slot_perm < 0).sum()),
+    }
+
+
+def union_gemv(a, a_per_slot: bool, experts, scale2, u_eid, u_slot, top_k: int, out,
+               mode: str):
+    """W4A16 product over the union entries, written into ``out`` (float64 ``[rows*top_k, N]``).
+
+    For every entry p with ``e = u_eid[p] >= 0`` and a non-null table entry, and every row r
+    with ``j = u_slot[p, r] >= 0``::
+
+        out[r * top_k + j, n] = sum_k a[src, k] * w_e[n, k]
+
+    in FP64, ``src = r * top_k + j`` when ``a_per_slot`` (the down projection reads each
+    slot's own activation) else ``r`` (gate_up reads the row's input). Other rows of
+    ``out`` are left as they are.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    u_eid = np.asarray(u_eid, dtype=np.int64)
+    u_slot = np.asarray(u_slot, dtype=np.int64)
+    for p in range(u_eid.size):
+        e = int(u_eid[p])
+        if e < 0 or experts[e] is None:
+            continue
+        rs = [r for r in range(u_slot.shape[1]) if u_slot[p, r] >= 0]
+        if not rs:
+            continue
+        packed, scales = experts[e]
+        w = dequant(packed, scales, float(scale2[e]), mode)
+        dst = np.array([r * top_k + int(u_slot[p, r]) for r in rs])
+        src = dst if a_per_slot else np.array(rs)
+        out[dst, :] = a[src, :] @ w.T
+    return out
+
+
+def moe_layer_decode(x, topk_ids, topk_weights, gate_up, down, scale2_gate_up, scale2_down,
+                     moe_intermediate: int, limit: float, mode: str, shared=None):
+    """The routed layer for a few rows through the union of their experts.
+
+    row_union -> union_gemv gate_up (input: the row) -> SwiGLU clamp -> union_gemv down
+    (input: the slot's activation) -> combine through ``slot_perm``. Buffers and rounding
+    as :func:`moe_layer` (``mode="bf16w"`` rounds the gate_up output, the activation and the
+    down output to BF16); outputs are laid out ``[rows * top_k, N]`` by (row, slot) instead
+    of by expert. Returns ``(out, intermediates)``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    rows, top_k = ids.shape
+    hidden = x.shape[1]
+    un = row_union(ids, len(gate_up))
+    rnd = round_bf16 if mode == "bf16w" else (lambda v: v)
+    c = np.full((rows * top_k, 2 * moe_intermediate), np.nan)  # uncovered rows undefined
+    union_gemv(x, False, gate_up, scale2_gate_up, un["u_eid"], un["u_slot"], top_k, c, mode)
+    c = rnd(c)
+    act = rnd(swiglu_clamp(c[:, :moe_intermediate], c[:, moe_intermediate:], limit))
+    expert_out = np.zeros((rows * top_k, hidden))  # remote experts add exactly 0
+    union_gemv(act, True, down, scale2_down, un["u_eid"], un["u_slot"], top_k, expert_out,
+               mode)
+    expert_out = rnd(expert_out)
+    out = combine(expert_out, un["slot_perm"], topk_weights, shared)
+    return out, {"union": un, "c": c, "act": act, "expert_out": expert_out}
