@@ -14,11 +14,14 @@ Calls (same names as the C ABI):
 - ``moe_router_topk``: router logits -> top-k ids and weights.
 - ``moe_dense_gate_up_swiglu_bf16``, ``moe_dense_gemm_bf16``: the shared expert's BF16
   GEMMs (gate/up with the SwiGLU in the epilogue, then down).
+- ``moe_row_union``, ``moe_w4a16_gemv_union``, ``moe_w4a16_gemv_union_swiglu``: the
+  decode / verify path for a few rows (the union of their experts, each swept once).
 
 Helpers: ``ExpertTable`` (device pointer table of per-expert NVFP4 weights),
 ``Workspace`` (every buffer of one layer call, allocated once), ``SharedExpert`` (the
-shared expert's weights and buffers) and ``moe_layer`` (the calls of one routed layer in
-order).
+shared expert's weights and buffers), ``moe_layer`` (the calls of one routed layer in
+order), ``DecodeWorkspace`` and ``moe_layer_decode`` (the same layer for a few rows through
+the union path).
 """
 
 from __future__ import annotations
@@ -31,6 +34,8 @@ __all__ = [
     "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "moe_router_topk",
     "moe_layer_from_logits", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
     "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "SharedExpert",
+    "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
+    "moe_layer_decode", "UNION_MAX_ROWS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -40,7 +45,11 @@ EXPORTS = (
     "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
+    "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu",
 )
+
+UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
+UNION_MAX_ROWS = 16  # MOE_UNION_MAX_ROWS: rows of moe_w4a16_gemv_union
 
 _LIB = None
 
@@ -69,6 +78,13 @@ _SIGNATURES = {
                             ctypes.c_int),
     "moe_dense_gate_up_swiglu_bf16": (
         [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp], ctypes.c_int),
+    "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_w4a16_gemv_union": (
+        [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32,
+         _vp], ctypes.c_int),
+    "moe_w4a16_gemv_union_swiglu": (
+        [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32,
+         _f32, _vp], ctypes.c_int),
 }
 
 
@@ -217,6 +233,81 @@ def moe_w4a16_grouped_gemm_swiglu(a, table: "ExpertTable", expert_offsets, act, 
         _p(table.scale2), _p(expert_offsets), table.num_experts, _p(act), ld_act, rows, mi,
         table.k, float(limit), _stream(stream)))
 
+
+
+def moe_row_union(topk_ids, num_experts: int, u_eid, u_slot, slot_perm=None, counters=None,
+                  stream=None) -> None:
+    """The union of the experts the rows of ``topk_ids`` (int32 ``[rows, top_k]``) selected:
+    ``u_eid [rows*top_k]``, ``u_slot [rows*top_k, rows]``, optional ``slot_perm`` and
+    ``counters``; see the header."""
+    import torch
+
+    for t, n in ((topk_ids, "topk_ids"), (u_eid, "u_eid"), (u_slot, "u_slot"),
+                 (slot_perm, "slot_perm"), (counters, "counters")):
+        _want(t, torch.int32, n)
+    rows, top_k = topk_ids.shape
+    t_ids = rows * top_k
+    if not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be contiguous")
+    for t, need, n in ((u_eid, t_ids, "u_eid"), (u_slot, t_ids * rows, "u_slot"),
+                       (slot_perm, t_ids, "slot_perm"), (counters, 2, "counters")):
+        if t is not None and (t.numel() < need or not t.is_contiguous()):
+            raise ValueError(f"{n}: needs {need} contiguous elements")
+    _check("moe_row_union", load().moe_row_union(
+        _p(topk_ids), rows, top_k, num_experts, _p(u_eid), _p(u_slot), _p(slot_perm),
+        _p(counters), _stream(stream)))
+
+
+def _union_gemv_common(a, table, u_eid, u_slot, c, rows, top_k, a_per_slot):
+    import torch
+
+    a, lda = _bf16_matrix(a, "a")
+    c, ldc = _bf16_matrix(c, "c")
+    _want(u_eid, torch.int32, "u_eid")
+    _want(u_slot, torch.int32, "u_slot")
+    t_ids = rows * top_k
+    if u_eid.numel() < t_ids or u_slot.numel() < t_ids * rows:
+        raise ValueError("u_eid / u_slot too small for rows * top_k")
+    if not (u_eid.is_contiguous() and u_slot.is_contiguous()):
+        raise ValueError("u_eid and u_slot must be contiguous")
+    if c.shape[0] < t_ids:
+        raise ValueError("c needs rows * top_k rows")
+    if a.shape[0] < (t_ids if a_per_slot else rows):
+        raise ValueError("a needs rows (or rows * top_k with a_per_slot) rows")
+    if a.shape[1] < table.k:
+        raise ValueError("a too narrow for the table's k")
+    return a, lda, c, ldc
+
+
+def moe_w4a16_gemv_union(a, table: "ExpertTable", u_eid, u_slot, c, rows: int, top_k: int,
+                         a_per_slot: bool = False, stream=None) -> None:
+    """``c[r*top_k + j] = a[src] @ W_e^T`` for each union entry's rows (src = r, or the slot
+    r*top_k + j with ``a_per_slot``); each union expert's weights are swept once."""
+    a, lda, c, ldc = _union_gemv_common(a, table, u_eid, u_slot, c, rows, top_k, a_per_slot)
+    if c.shape[1] < table.n:
+        raise ValueError("c too narrow for the table's n")
+    _check("moe_w4a16_gemv_union", load().moe_w4a16_gemv_union(
+        _p(a), lda, a.shape[0], int(bool(a_per_slot)), _p(table.packed_ptrs),
+        _p(table.scale_ptrs), _p(table.scale2), _p(u_eid), _p(u_slot), rows, top_k,
+        table.num_experts, _p(c), ldc, table.n, table.k, _stream(stream)))
+
+
+def moe_w4a16_gemv_union_swiglu(a, table: "ExpertTable", u_eid, u_slot, act, limit: float,
+                                rows: int, top_k: int, a_per_slot: bool = False,
+                                stream=None) -> None:
+    """moe_w4a16_gemv_union over a fused gate_up table with the SwiGLU clamp in the
+    epilogue: ``act[r*top_k + j] = swiglu_clamp(gate, up)``."""
+    if table.n % 2:
+        raise ValueError("the fused gate_up table needs an even n")
+    mi = table.n // 2
+    a, lda, act, ld_act = _union_gemv_common(a, table, u_eid, u_slot, act, rows, top_k,
+                                             a_per_slot)
+    if act.shape[1] < mi:
+        raise ValueError("act too narrow for the table's n / 2")
+    _check("moe_w4a16_gemv_union_swiglu", load().moe_w4a16_gemv_union_swiglu(
+        _p(a), lda, a.shape[0], int(bool(a_per_slot)), _p(table.packed_ptrs),
+        _p(table.scale_ptrs), _p(table.scale2), _p(u_eid), _p(u_slot), rows, top_k,
+        table.num_experts, _p(act), ld_act, mi, table.k, float(limit), _stream(stream)))
 
 def moe_router_topk(logits, top_k: int, topk_ids, topk_weights, bias=None,
                     routed_scale: float = 1.0, renormalize: bool = True, stream=None) -> None:
@@ -468,3 +559,59 @@ def moe_layer_from_logits(x, logits, top_k: int, gate_up: ExpertTable, down: Exp
     moe_router_topk(logits, top_k, ids, wts, bias, routed_scale, renormalize, stream)
     moe_layer(x, ids, wts, gate_up, down, moe_intermediate, limit, ws, out, shared, stream,
               fused)
+
+
+class DecodeWorkspace:
+    """Every buffer one decode-path layer call needs, for up to ``max_rows`` (<= 16) rows."""
+
+    def __init__(self, max_rows: int, top_k: int, hidden: int, moe_intermediate: int,
+                 device="cuda"):
+        import torch
+
+        if not 1 <= max_rows <= UNION_MAX_ROWS or max_rows * top_k > UNION_MAX_IDS:
+            raise ValueError("the decode path takes 1..16 rows and rows * top_k <= 1024")
+        t = max_rows * top_k
+        i32 = dict(dtype=torch.int32, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.max_rows, self.top_k = max_rows, top_k
+        self.u_eid = torch.empty(t, **i32)
+        self.u_slot = torch.empty(t * max_rows, **i32)
+        self.slot_perm = torch.empty(t, **i32)
+        self.counters = torch.empty(2, **i32)
+        self.gate_up = torch.empty(t, 2 * moe_intermediate, **bf)
+        self.act = torch.empty(t, moe_intermediate, **bf)
+        self.expert_out = torch.empty(t, hidden, **bf)
+
+
+def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable,
+                     moe_intermediate: int, limit: float, ws: DecodeWorkspace, out,
+                     shared=None, stream=None, fused: bool = True) -> None:
+    """The routed layer for a few rows (<= 16) through the union of their experts:
+    moe_row_union -> union GEMV gate_up (each row's input) with the SwiGLU clamp fused ->
+    union GEMV down (each slot's activation) -> combine through ``slot_perm``. Outputs are
+    laid out by (row, slot), so no sort and no expert-sorted permutation are needed.
+    ``fused=False`` runs the gate_up GEMV and swiglu_clamp as two calls (same bits).
+    Slots of absent experts must read as zero in the combine, so ``ws.expert_out`` is
+    zeroed first unless every down entry is present."""
+    rows, top_k = topk_ids.shape
+    t = rows * top_k
+    if rows > ws.max_rows or top_k != ws.top_k:
+        raise ValueError("the workspace was made for fewer rows or another top_k")
+    u_slot = ws.u_slot[:t * rows]
+    moe_row_union(topk_ids, gate_up.num_experts, ws.u_eid, u_slot, ws.slot_perm, ws.counters,
+                  stream)
+    if not all(down.present):
+        ws.expert_out[:t].zero_()
+    mi = moe_intermediate
+    if fused:
+        moe_w4a16_gemv_union_swiglu(x, gate_up, ws.u_eid, u_slot, ws.act, limit, rows, top_k,
+                                    stream=stream)
+    else:
+        moe_w4a16_gemv_union(x, gate_up, ws.u_eid, u_slot, ws.gate_up, rows, top_k,
+                             stream=stream)
+        swiglu_clamp(ws.gate_up[:t, :mi], ws.gate_up[:t, mi:2 * mi], ws.act[:t], limit, stream)
+    moe_w4a16_gemv_union(ws.act, down, ws.u_eid, u_slot, ws.expert_out, rows, top_k,
+                         a_per_slot=True, stream=stream)
+    if isinstance(shared, SharedExpert):
+        shared = shared(x, limit, stream)
+    moe_combine(ws.expert_out[:t], ws.slot_perm[:t], topk_weights, out, shared, stream)

@@ -52,11 +52,12 @@
 #include "common.h"
 #include "nvfp4_decode.h"
 #include "swiglu.h"
+#include "w4a16_mma.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+using moe::bf16x8_t;
+using moe::f32x4_t;
 using moe::u32x4_t;
 
 constexpr int kWaves = 4;
@@ -80,9 +81,14 @@ static_assert(kBlockM * kPiecesPerRow == kXPieces * kThreads, "whole activation 
 static_assert(kBlockN * kStageSteps == kSPieces * kThreads, "whole scale pieces");
 static_assert(kSPieces == kTiles, "one scale piece per thread and tile half");
 
+using moe::build_code_table_lut;
 using moe::kNoLoad;
 using moe::load16;
+using moe::lut_blocks;
 using moe::make_rsrc;
+using moe::mfma4;
+using moe::permute_k8;
+static_assert(kThreads == 256, "build_code_table_lut: one E4M3 code per thread");
 
 // One lane's packed weights of a step: per tile, 64 k of one row as two 16-byte loads;
 // the wave reads 16 rows x 64 contiguous bytes per load.
@@ -105,16 +111,6 @@ __device__ __forceinline__ void load_weights(WeightRegs &w, __amdgpu_buffer_rsrc
   }
 }
 
-// 8 BF16 (k0..k7) -> order (k0,k2) (k4,k6) (k1,k3) (k5,k7), the decoder's order.
-__device__ __forceinline__ u32x4_t permute_k8(u32x4_t v) {
-  u32x4_t o;
-  o[0] = moe::byte_perm(v[1], v[0], 0x05040100u);
-  o[1] = moe::byte_perm(v[3], v[2], 0x05040100u);
-  o[2] = moe::byte_perm(v[1], v[0], 0x07060302u);
-  o[3] = moe::byte_perm(v[3], v[2], 0x07060302u);
-  return o;
-}
-
 // A row's 16 scale bytes of one step -> four dwords, dword kb holding the bytes lane kb
 // needs: groups 2kb, 2kb+1 (low half) and 8+2kb, 9+2kb (high half).
 __device__ __forceinline__ u32x4_t permute_scales(u32x4_t v) {
@@ -124,49 +120,6 @@ __device__ __forceinline__ u32x4_t permute_scales(u32x4_t v) {
   o[2] = moe::byte_perm(v[3], v[1], 0x05040100u);
   o[3] = moe::byte_perm(v[3], v[1], 0x07060302u);
   return o;
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&w)[4]) {
-  const u32x4_t u = {w[0], w[1], w[2], w[3]};
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// Multiply four decoded words into acc against four B operands.
-__device__ __forceinline__ void mfma4(const uint32_t *words, const moe::Fp4Table &b0,
-                                      const moe::Fp4Table &b1, const bf16x8_t *B,
-                                      f32x4_t &acc) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t wd[4];
-    moe::decode8(words[j], j < 2 ? b0 : b1, wd);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wd), B[j], acc, 0, 0, 0);
-  }
-}
-
-// The byte tables of the lane's four blocks (scale codes in the bytes of `sc`, see
-// permute_scales) from the per-block LUT.
-__device__ __forceinline__ void lut_blocks(uint32_t sc, const uint8_t *lut, moe::Fp4Table *blk) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const u32x4_t t =
-        *reinterpret_cast<const u32x4_t *>(lut + (((sc >> (8 * g)) & 0xFFu) << 4));
-    blk[g].lo03 = t[0];
-    blk[g].lo47 = t[1];
-    blk[g].hi03 = t[2];
-    blk[g].hi47 = t[3];
-  }
-}
-
-// The byte tables of every E4M3 scale code for this expert's scale2, one 16-byte entry
-// per code {lo03, lo47, hi03, hi47}. One code per thread, no loop, so that it is
-// scheduled behind the loads that precede it.
-static_assert(kThreads == 256, "one E4M3 code per thread");
-__device__ __forceinline__ void build_code_table_lut(uint8_t *lut, int tid, float scale2) {
-  float d, unused;
-  moe::e4m3x2_to_f32(static_cast<uint32_t>(tid), d, unused);
-  const moe::Fp4Table b = moe::make_table(d, scale2);
-  const u32x4_t t = {b.lo03, b.lo47, b.hi03, b.hi47};
-  *reinterpret_cast<u32x4_t *>(lut + tid * 16) = t;
 }
 
 // kSwiglu = false: c[s, n] for the N weight rows.

@@ -14,6 +14,10 @@
  *   moe_dense_gate_up_swiglu_bf16, moe_dense_gemm_bf16
  *                           the shared expert (a BF16 SwiGLU MLP over all rows), whose
  *                           output is moe_combine's `shared` term
+ *   moe_row_union, moe_w4a16_gemv_union, moe_w4a16_gemv_union_swiglu
+ *                           the decode / verify path for a few rows: the union of the
+ *                           rows' experts (no sort) and one sweep of each union expert,
+ *                           outputs laid out by (row, slot)
  *
  * Sources (the pages this library follows, by title and section):
  *   [FPG]  "Module forward_prefill_gemm" (glm5next_mlp/forward_prefill_gemm), sections
@@ -25,6 +29,9 @@
  *          expert_offsets, token_to_perm, expert_out), swiglu_rows, and forward_moe's
  *          zero-first memset and glm5next_moe_combine_indexed launch; forward_dense and
  *          the gemm helper above it (C = A B^T, BF16 in and out) for the shared expert.
+ *          For the decode path: the workspace fields u_eid and u_slot, the doc of the
+ *          row-batched GEMV (C[rows, top_k, N], each union expert swept once) and of
+ *          moe_row_groups (which rows share a sweep never changes what a row adds).
  *
  * Conventions shared by every call:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise. The caller
@@ -283,6 +290,86 @@ int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda, const uint16_t
  */
 int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales, float scale2,
                            uint16_t *out, int32_t n, int32_t k, void *stream);
+
+/* Limits of the decode / verify path. */
+#define MOE_UNION_MAX_IDS 1024 /* rows * top_k of moe_row_union (one workgroup) */
+#define MOE_UNION_MAX_ROWS 16  /* rows of moe_w4a16_gemv_union (one matrix-core tile) */
+
+/*
+ * moe_row_union - the union of the experts a few rows selected ([FWD] workspace fields
+ * u_eid, u_slot; the union is found by pairwise scans in one workgroup, no sort).
+ *
+ * Slot t = r * top_k + j is covered when topk_ids[t] is in [0, num_experts) and no lower
+ * slot of row r holds the same id (a proper top-k never repeats an expert in a row; a
+ * repeat is treated like an invalid id).
+ *
+ *   topk_ids   int32 [rows * top_k]          in
+ *   u_eid      int32 [rows * top_k]          out: the distinct ids of the covered slots in
+ *                                            order of first appearance in t, then -1
+ *   u_slot     int32 [rows * top_k, rows]    out: u_slot[p, r] = j when row r's slot j is
+ *                                            covered and selects u_eid[p], else -1
+ *   slot_perm  int32 [rows * top_k] or NULL  out: t for a covered slot, else -1 (the
+ *                                            combine's token_to_perm for outputs laid out
+ *                                            [rows * top_k, n] by slot)
+ *   counters   int32 [2] or NULL             out: {union size, uncovered slots}
+ *
+ * rows == 0 enqueues nothing. Errors: MOE_EINVAL if rows < 0, top_k < 1, num_experts < 1,
+ * rows * top_k > MOE_UNION_MAX_IDS, or a required pointer is NULL while rows > 0.
+ */
+int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                  int32_t *u_eid, int32_t *u_slot, int32_t *slot_perm, int32_t *counters,
+                  void *stream);
+
+/*
+ * moe_w4a16_gemv_union - the W4A16 product of each union expert's rows, each expert's
+ * weights swept once ([FWD] the row-batched GEMV: C[rows, top_k, N] over the union).
+ *
+ * For every entry p with e = u_eid[p] in [0, num_experts) and packed_ptrs[e] != 0, and
+ * every row r with j = u_slot[p, r] >= 0:
+ *
+ *   c[r * top_k + j, n] = bf16( sum_k a[src, k] * W_e[n, k] ),  src = a_per_slot ?
+ *                                                          r * top_k + j : r
+ *
+ * with W_e decoded exactly as in moe_w4a16_grouped_gemm (same tables, same BF16 operand)
+ * and FP32 accumulation. The sum's order does not depend on which rows share the sweep.
+ * Rows of c that no entry covers, and rows of absent experts, are not written.
+ *
+ *   a       bf16 [a_rows, lda]: the rows' inputs (a_per_slot = 0: a_rows >= rows) or one
+ *           input per slot (a_per_slot != 0: row r * top_k + j). A source row outside
+ *           [0, a_rows) reads zeros.
+ *   tables  as moe_w4a16_grouped_gemm (packed_ptrs, scale_ptrs, scale2 per global id)
+ *   u_eid, u_slot  as written by moe_row_union for the same rows and top_k
+ *   c       bf16 [rows * top_k, ldc] output, laid out by (row, slot)
+ *
+ * Requirements (else MOE_EINVAL): 0 <= rows <= MOE_UNION_MAX_ROWS; top_k >= 1 and
+ * rows * top_k <= MOE_UNION_MAX_IDS; n > 0, n % 16 == 0; k > 0, k % 256 == 0; lda >= k,
+ * a multiple of 8; ldc >= n, a multiple of 4; a 16-byte and c 8-byte aligned;
+ * num_experts >= 1; a_rows >= 1; required pointers non-NULL. rows == 0 enqueues nothing.
+ */
+int moe_w4a16_gemv_union(const uint16_t *a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
+                         const uint64_t *packed_ptrs, const uint64_t *scale_ptrs,
+                         const float *scale2, const int32_t *u_eid, const int32_t *u_slot,
+                         int32_t rows, int32_t top_k, int32_t num_experts, uint16_t *c,
+                         int64_t ldc, int32_t n, int32_t k, void *stream);
+
+/*
+ * moe_w4a16_gemv_union_swiglu - moe_w4a16_gemv_union over a fused gate_up weight (n = 2 mi
+ * rows, gate rows [0, mi), up rows [mi, 2 mi)) followed by swiglu_clamp in the epilogue:
+ *
+ *   act[r * top_k + j, i] = bf16( swiglu(G, U) ),  G = bf16(gate sum of row i),
+ *                           U = bf16(up sum of row mi + i)
+ *
+ * bit-identical to moe_w4a16_gemv_union into a [rows * top_k, 2 mi] buffer followed by
+ * swiglu_clamp. Requirements: mi > 0, mi % 16 == 0, limit > 0, ld_act >= mi, and those of
+ * moe_w4a16_gemv_union with n = 2 mi.
+ */
+int moe_w4a16_gemv_union_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
+                                int32_t a_per_slot, const uint64_t *packed_ptrs,
+                                const uint64_t *scale_ptrs, const float *scale2,
+                                const int32_t *u_eid, const int32_t *u_slot, int32_t rows,
+                                int32_t top_k, int32_t num_experts, uint16_t *act,
+                                int64_t ld_act, int32_t mi, int32_t k, float limit,
+                                void *stream);
 
 #ifdef __cplusplus
 }
