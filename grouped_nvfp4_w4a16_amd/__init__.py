@@ -50,6 +50,7 @@ EXPORTS = (
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
 UNION_MAX_ROWS = 16  # MOE_UNION_MAX_ROWS: rows of moe_w4a16_gemv_union
+UNION_GEMV_MAX_IDS = 512  # MOE_UNION_GEMV_MAX_IDS: rows * top_k of moe_w4a16_gemv_union
 
 _LIB = None
 
@@ -568,8 +569,8 @@ class DecodeWorkspace:
                  device="cuda"):
         import torch
 
-        if not 1 <= max_rows <= UNION_MAX_ROWS or max_rows * top_k > UNION_MAX_IDS:
-            raise ValueError("the decode path takes 1..16 rows and rows * top_k <= 1024")
+        if not 1 <= max_rows <= UNION_MAX_ROWS or max_rows * top_k > UNION_GEMV_MAX_IDS:
+            raise ValueError("the decode path takes 1..16 rows and rows * top_k <= 512")
         t = max_rows * top_k
         i32 = dict(dtype=torch.int32, device=device)
         bf = dict(dtype=torch.bfloat16, device=device)

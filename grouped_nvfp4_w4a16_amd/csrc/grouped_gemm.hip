@@ -439,12 +439,12 @@ int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_
               name);
   if (max_rows == 0) return MOE_OK;
   MOE_REQUIRE(a_rows >= 1, "%s: a_rows must be >= 1 when max_rows > 0", name);
-  // Buffer offsets are 32-bit: activations below 2 GiB, one expert's packed weights
-  // below 4 GiB.
+  // Buffer offsets are 32-bit and a skipped load uses offset 2^31, past any buffer below
+  // 2 GiB: activations and one expert's packed weights stay below 2 GiB.
   MOE_REQUIRE(static_cast<uint64_t>(a_rows) * lda * 2 < (1ull << 31),
               "%s: the activation buffer must be smaller than 2 GiB", name);
-  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 32),
-              "%s: one expert's packed weights must be smaller than 4 GiB", name);
+  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 31),
+              "%s: one expert's packed weights must be smaller than 2 GiB", name);
   return MOE_OK;
 }
 

@@ -128,6 +128,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kChunkK = 256;       // k per step
 constexpr int kMaxRows = 16;       // routed rows a launch may have: one MFMA tile of B
+constexpr int kSlotsPerCu = 3;     // resident blocks per CU (VGPR-limited)
+constexpr int kCus = 256;
+constexpr int kGemvMaxIds = 512;   // rows * top_k: the entries' metadata live in LDS
 static_assert(kThreads == 256, "build_code_table_lut: one E4M3 code per thread");
 
 // One lane's data of one step: packed weights of its two tiles (k in [64 kb, 64 kb + 32)
@@ -139,167 +142,279 @@ struct StepRegs {
   u32x4_t x[8];
 };
 
+// A live union entry (its expert present in the table), as the block's waves read it.
+struct LiveEntry {
+  uint64_t packed, scales;
+  float scale2;
+  int32_t p;  // union entry
+};
+// Dynamic LDS per union entry: the entry (if live) and the output row of each of its up
+// to 16 tokens (the entry's routed rows in order; -1 past the last).
+constexpr int kEntryLdsBytes = static_cast<int>(sizeof(LiveEntry)) + 16 * 2;
+
+// One work item as a wave sees it: the expert's buffers and scale2 (uniform), the rows of
+// the wave's two tiles as byte offsets into them (uniform: they ride in the scalar offset
+// of the buffer loads; a tile past the last row is off and loads nothing), and the lane's
+// activation row and output row (the entry's token r16).
+struct Item {
+  __amdgpu_buffer_rsrc_t w, s;
+  uint32_t w_base[2], s_base[2];
+  float scale2;
+  bool on[2];
+  uint32_t x_voff;  // per lane, kNoLoad if the lane has no token
+  int32_t dst_row;  // per lane, -1 if the lane has no token
+};
+
+// The work of a launch is (live entry, group of 32 * kGroups weight rows) items, dealt to
+// the persistent blocks round-robin. Items are alike (the same rows and K), so a static
+// deal is balanced, and a block streams its items back to back: the waves load the next
+// item's first step while computing the current item's last one, and each item's decode
+// table is built during the item before it (double-buffered), so no item pays a start-up.
 template <bool kSwiglu, int kKSplit>
-__global__ __launch_bounds__(kThreads, 3) void gemv_union_kernel(
+__global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
     const uint64_t *__restrict__ packed_ptrs, const uint64_t *__restrict__ scale_ptrs,
     const float *__restrict__ scale2s, const int32_t *__restrict__ u_eid,
     const int32_t *__restrict__ u_slot, int32_t rows, int32_t top_k, int32_t num_experts,
     uint16_t *__restrict__ c, int64_t ldc, int32_t N, int32_t K, float limit) {
-  constexpr int kGroups = kWaves / kKSplit;  // 32-row groups per block
-  __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
-  __shared__ __attribute__((aligned(16))) f32x4_t red[kWaves][2][64];
+  constexpr int kGroups = kWaves / kKSplit;  // 32-row groups per item
+  constexpr int kItemRows = kSwiglu ? 16 * kGroups : 32 * kGroups;  // gate rows if fused
+  __shared__ __attribute__((aligned(16))) uint8_t lut[2][256 * 16];
+  __shared__ __attribute__((aligned(16))) f32x4_t red[2][kWaves][2][64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  __shared__ int32_t n_live_s;
+  const int n_ids = rows * top_k;
+  LiveEntry *live = reinterpret_cast<LiveEntry *>(dyn_lds);
+  int16_t *tok = reinterpret_cast<int16_t *>(dyn_lds + n_ids * sizeof(LiveEntry));  // [n_ids][16]
 
-  const int p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kw = wave % kKSplit, nw = wave / kKSplit;
   const int r16 = lane & 15, kb = lane >> 4;
-
-  // The entry's expert and its rows: lane l < rows reads u_slot[p, l].
-  const int e = u_eid[p];
-  const int my_slot_of_lane = lane < rows ? u_slot[static_cast<int64_t>(p) * rows + lane] : -1;
-  if (e < 0 || e >= num_experts) return;
-  const uint64_t packed_u = packed_ptrs[e], scales_u = scale_ptrs[e];
-  const float scale2 = scale2s[e];
-  asm volatile("" ::"s"(packed_u), "s"(scales_u), "s"(scale2));
-  if (packed_u == 0) return;  // expert not present: its rows keep the caller's values
-  const uint64_t present = __ballot(my_slot_of_lane >= 0);
-  if (present == 0) return;
-  // Token r16 of the tile: the r16-th routed row present in the entry.
-  int tok_row = -1;
-  {
-    uint64_t m = present;
-    for (int i = 0; i < kMaxRows && m != 0; ++i) {
-      const int b = __builtin_ctzll(m);
-      if (i == r16) tok_row = b;
-      m &= m - 1;
-    }
-  }
-  const int tok_slot = __shfl(my_slot_of_lane, tok_row < 0 ? 0 : tok_row);
-  const bool tok_on = tok_row >= 0;
-  const int dst_row = tok_row * top_k + tok_slot;
-  const int src_row = a_per_slot ? dst_row : tok_row;
-
-  const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_u);
-  const uint8_t *scales = reinterpret_cast<const uint8_t *>(scales_u);
   const int mi = N / 2;
-  // This wave's two tiles of 16 weight rows. Plain: the group's 32 consecutive rows.
-  // Fused: 16 gate rows and the matching 16 up rows.
-  const int n_t0 = kSwiglu ? (blockIdx.x * kGroups + nw) * 16 : (blockIdx.x * kGroups + nw) * 32;
-  const int n_t1 = kSwiglu ? mi + n_t0 : n_t0 + 16;
   const int row_end0 = kSwiglu ? mi : N;
-  const bool t0_on = n_t0 < row_end0, t1_on = n_t1 < N && (!kSwiglu || t0_on);
-
+  const int items_per_entry = (row_end0 + kItemRows - 1) / kItemRows;
   const uint32_t row_bytes = static_cast<uint32_t>(K) / 2, srow_bytes = static_cast<uint32_t>(K) / 16;
   const int n_steps = K / kChunkK;
-  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(packed, static_cast<uint32_t>(N) * row_bytes);
-  const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(scales, static_cast<uint32_t>(N) * srow_bytes);
+  const int n_mine = n_steps > kw ? (n_steps - kw + kKSplit - 1) / kKSplit : 0;
+  // Lane parts of the weight and scale offsets (row r16 of a tile, bytes for k in
+  // [64 kb, 64 kb + 64) of a step); the tile's rows and the step go in the scalar offset.
+  const uint32_t w_lane = static_cast<uint32_t>(r16) * row_bytes + 32u * kb;
+  const uint32_t s_lane = static_cast<uint32_t>(r16) * srow_bytes + 4u * kb;
+
+  // The live entries, compacted in LDS by wave 0: an entry with an expert id in range and
+  // a non-null table address.
+  if (wave == 0) {
+    int n = 0;
+    for (int q0 = 0; q0 < n_ids; q0 += 64) {
+      const int q = q0 + lane;
+      const int e = q < n_ids ? u_eid[q] : -1;
+      const bool in = e >= 0 && e < num_experts;
+      const uint64_t pk = in ? packed_ptrs[e] : 0;
+      const bool ok = pk != 0;
+      const uint64_t m = __ballot(ok);
+      if (ok) {
+        LiveEntry le;
+        le.packed = pk;
+        le.scales = scale_ptrs[e];
+        le.scale2 = scale2s[e];
+        le.p = q;
+        live[n + __popcll(m & ((1ull << lane) - 1ull))] = le;
+      }
+      n += __popcll(m);
+    }
+    if (lane == 0) n_live_s = n;
+  }
+  __syncthreads();
+  const int n_live = n_live_s;
+  const int n_items = n_live * items_per_entry;
+  if (static_cast<int>(blockIdx.x) >= n_items) return;  // uniform: the whole block
+  // Each live entry's tokens: its routed rows (u_slot[p, r] >= 0) in order of r, as
+  // output rows r * top_k + slot. A wave reads the u_slot rows of 64 / rows entries at
+  // once, one lane per (entry, row); a present row's token index is its rank in its
+  // entry's lanes.
+  for (int q = tid; q < n_live * 16; q += kThreads) tok[q] = -1;
+  __syncthreads();
+  {
+    const int epw = 64 / rows;  // entries per wave and pass (rows >= 1 here)
+    const int le_lane = lane / rows, r = lane - le_lane * rows;
+    const int seg0 = le_lane * rows;
+    for (int base = wave * epw; base < n_live; base += kWaves * epw) {
+      const int li = base + le_lane;
+      const bool mine = le_lane < epw && li < n_live;
+      const int slot = mine ? u_slot[static_cast<int64_t>(live[li].p) * rows + r] : -1;
+      const uint64_t m = __ballot(slot >= 0);
+      if (slot >= 0) {
+        const uint64_t below = (1ull << lane) - 1ull, seg_below = (1ull << seg0) - 1ull;
+        const int rank = __popcll(m & below & ~seg_below);
+        tok[li * 16 + rank] = static_cast<int16_t>(r * top_k + slot);
+      }
+    }
+  }
+  __syncthreads();
+
+  // readfirstlane works on int: widen through uint32_t, so that a low word with its top
+  // bit set is not sign-extended into the high word of an address.
+  const auto rfl32 = [](uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+  };
+  const auto rfl64 = [&](uint64_t v) {
+    return (static_cast<uint64_t>(rfl32(static_cast<uint32_t>(v >> 32))) << 32) |
+           static_cast<uint64_t>(rfl32(static_cast<uint32_t>(v)));
+  };
   const __amdgpu_buffer_rsrc_t x_rsrc =
       make_rsrc(a, static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(lda) * 2u);
-  // Rows past N lie past the buffer end and read zeros; out-of-range inputs read zeros.
-  const uint32_t w_voff[2] = {static_cast<uint32_t>(n_t0 + r16) * row_bytes + 32u * kb,
-                              static_cast<uint32_t>(n_t1 + r16) * row_bytes + 32u * kb};
-  const uint32_t s_voff[2] = {static_cast<uint32_t>(n_t0 + r16) * srow_bytes + 4u * kb,
-                              static_cast<uint32_t>(n_t1 + r16) * srow_bytes + 4u * kb};
-  const bool x_on = tok_on && src_row >= 0 && src_row < a_rows;
-  const uint32_t x_voff =
-      x_on ? (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(lda) + 64u * kb) * 2u : kNoLoad;
-
-  // Step s of this wave's share (kw, kw + kKSplit, ...); past the last one the loads read
-  // nothing, so every load stays unconditional.
-  const int n_mine = n_steps > kw ? (n_steps - kw + kKSplit - 1) / kKSplit : 0;
-  const auto load_step = [&](StepRegs &st, int i) {
-    const bool live = i < n_mine;
+  // The whole Item of it: its entry's buffers (uniform), its rows, this lane's token.
+  const auto make_item = [&](int it) {
+    Item m;
+    const int li = it / items_per_entry, g = it - li * items_per_entry;
+    const LiveEntry &le = live[li];
+    m.w = make_rsrc(reinterpret_cast<const void *>(rfl64(le.packed)), static_cast<uint32_t>(N) * row_bytes);
+    m.s = make_rsrc(reinterpret_cast<const void *>(rfl64(le.scales)), static_cast<uint32_t>(N) * srow_bytes);
+    m.scale2 = __builtin_bit_cast(float, rfl32(__builtin_bit_cast(uint32_t, le.scale2)));
+    const int n_t0 = kSwiglu ? (g * kGroups + nw) * 16 : (g * kGroups + nw) * 32;
+    const int n_t1 = kSwiglu ? mi + n_t0 : n_t0 + 16;
+    m.on[0] = n_t0 < row_end0;
+    m.on[1] = n_t1 < N && (!kSwiglu || m.on[0]);
+    m.w_base[0] = static_cast<uint32_t>(n_t0) * row_bytes;
+    m.w_base[1] = static_cast<uint32_t>(n_t1) * row_bytes;
+    m.s_base[0] = static_cast<uint32_t>(n_t0) * srow_bytes;
+    m.s_base[1] = static_cast<uint32_t>(n_t1) * srow_bytes;
+    m.dst_row = tok[li * 16 + r16];
+    const int src = m.dst_row < 0 ? -1 : (a_per_slot ? m.dst_row : m.dst_row / top_k);
+    m.x_voff = (src >= 0 && src < a_rows)
+                   ? (static_cast<uint32_t>(src) * static_cast<uint32_t>(lda) + 64u * kb) * 2u
+                   : kNoLoad;
+    return m;
+  };
+  // Step i of this wave's share of an item (steps kw, kw + kKSplit, ...); live = false
+  // loads nothing, so every load stays unconditional.
+  const auto load_step = [&](StepRegs &st, const Item &m, int i, bool live_step) {
     const int step = kw + i * kKSplit;
-    const uint32_t wsoff = static_cast<uint32_t>(step) * (kChunkK / 2);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint32_t v = live ? w_voff[t] : kNoLoad;
-      st.wa[t] = load16(w_rsrc, v, wsoff);
-      st.wb[t] = load16(w_rsrc, v + 16, wsoff);
+      const bool on = live_step && m.on[t];
+      const uint32_t v = on ? w_lane : kNoLoad;
+      const uint32_t soff = m.w_base[t] + static_cast<uint32_t>(step) * (kChunkK / 2);
+      st.wa[t] = load16(m.w, v, soff);
+      st.wb[t] = load16(m.w, v + 16, soff);
       st.sc[t] = __builtin_amdgcn_raw_buffer_load_b32(
-          s_rsrc, static_cast<int>(live ? s_voff[t] : kNoLoad), static_cast<int>(step * 16), 0);
+          m.s, static_cast<int>(on ? s_lane : kNoLoad),
+          static_cast<int>(m.s_base[t] + static_cast<uint32_t>(step) * 16u), 0);
     }
-    const uint32_t xv = live ? x_voff : kNoLoad;
+    const uint32_t xv = live_step ? m.x_voff : kNoLoad;
     const uint32_t xsoff = static_cast<uint32_t>(step) * (kChunkK * 2);
 #pragma unroll
     for (int q = 0; q < 8; ++q) st.x[q] = load16(x_rsrc, xv + 16u * q, xsoff);
   };
 
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  const auto run_step = [&](const StepRegs &st) {
-    moe::Fp4Table blk0[4], blk1[4];
-    moe::lut_blocks(st.sc[0], lut, blk0);
-    moe::lut_blocks(st.sc[1], lut, blk1);
+  // The tables of blocks 2h, 2h + 1 (bytes of sc) are read per half, which keeps half of
+  // them out of the registers at a time.
+  const auto tables_of = [&](uint32_t sc, int h, const uint8_t *tab, moe::Fp4Table *blk) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const u32x4_t t = *reinterpret_cast<const u32x4_t *>(
+          tab + (((sc >> (8 * (2 * h + g))) & 0xFFu) << 4));
+      blk[g].lo03 = t[0];
+      blk[g].lo47 = t[1];
+      blk[g].hi03 = t[2];
+      blk[g].hi47 = t[3];
+    }
+  };
+  const auto run_step = [&](const StepRegs &st, const uint8_t *tab, bool t1_on) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      moe::Fp4Table blk0[2], blk1[2];
+      tables_of(st.sc[0], h, tab, blk0);
+      tables_of(st.sc[1], h, tab, blk1);
       bf16x8_t B[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) B[q] = __builtin_bit_cast(bf16x8_t, moe::permute_k8(st.x[4 * h + q]));
       const u32x4_t &x0 = h ? st.wb[0] : st.wa[0];
       const uint32_t w0w[4] = {x0[0], x0[1], x0[2], x0[3]};
-      moe::mfma4(w0w, blk0[2 * h], blk0[2 * h + 1], B, acc[0]);
+      moe::mfma4(w0w, blk0[0], blk0[1], B, acc[0]);
       if (t1_on) {
         const u32x4_t &x1 = h ? st.wb[1] : st.wa[1];
         const uint32_t w1w[4] = {x1[0], x1[1], x1[2], x1[3]};
-        moe::mfma4(w1w, blk1[2 * h], blk1[2 * h + 1], B, acc[1]);
+        moe::mfma4(w1w, blk1[0], blk1[1], B, acc[1]);
       }
     }
   };
 
-  StepRegs s0, s1;
-  load_step(s0, 0);
-  moe::build_code_table_lut(lut, tid, scale2);
-  __syncthreads();  // the LUT is complete
-  if (t0_on) {
-    for (int i = 0; i < n_mine; i += 2) {
-      load_step(s1, i + 1);
-      run_step(s0);
-      load_step(s0, i + 2);
-      if (i + 1 < n_mine) run_step(s1);
-    }
-  }
+  const int G = gridDim.x;
+  int item = blockIdx.x;
+  Item cur = make_item(item);
+  StepRegs sA, sB;
+  load_step(sA, cur, 0, true);
+  moe::build_code_table_lut(lut[0], tid, cur.scale2);
+  __syncthreads();  // table 0 is complete
 
-  // Sum the kKSplit partial tiles of each 32-row group in wave order.
-  if (kKSplit > 1) {
-    if (kw > 0) {
-      red[wave][0][lane] = acc[0];
-      red[wave][1][lane] = acc[1];
+  for (int j = 0;; ++j) {
+    const bool has_next = item + G < n_items;
+    const Item nxt = make_item(has_next ? item + G : item);
+    if (has_next) moe::build_code_table_lut(lut[(j + 1) & 1], tid, nxt.scale2);
+    const uint8_t *tab = lut[j & 1];
+
+    // This item's steps in pairs: slot A holds step i, slot B takes step i + 1; after an
+    // odd share, the pair's second step is empty. The step after this item's last is the
+    // next item's first, into slot A (a select, so the loads stay unconditional).
+    for (int i = 0; i < n_mine; i += 2) {
+      load_step(sB, cur, i + 1, i + 1 < n_mine);
+      if (cur.on[0]) run_step(sA, tab, cur.on[1]);
+      const bool last = i + 2 >= n_mine;
+      load_step(sA, last ? nxt : cur, last ? 0 : i + 2, last ? has_next : true);
+      if (i + 1 < n_mine && cur.on[0]) run_step(sB, tab, cur.on[1]);
     }
-    __syncthreads();
-    if (kw > 0) return;
-#pragma unroll
-    for (int q = 1; q < kKSplit; ++q) {
-      acc[0] += red[wave + q][0][lane];
-      acc[1] += red[wave + q][1][lane];
+
+    // Sum the kKSplit partial tiles of each 32-row group in wave order, store.
+    if (kKSplit > 1 && kw > 0) {
+      red[j & 1][wave][0][lane] = acc[0];
+      red[j & 1][wave][1][lane] = acc[1];
     }
-  }
-  // acc[t][i] = result for weight row n_t + 4 kb + i and the entry's row r16.
-  if (!tok_on || !t0_on) return;
-  uint16_t *crow = c + static_cast<size_t>(dst_row) * ldc;
-  if (kSwiglu) {
-    float o[4];
+    __syncthreads();  // the partials and the next table are complete
+    if (kw == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t gu = moe::pack_bf16x2(acc[0][i], acc[1][i]);
-      o[i] = moe::swiglu_clamp1(__uint_as_float(gu << 16), __uint_as_float(gu & 0xFFFF0000u),
-                                limit);
-    }
-    uint2 v;
-    v.x = moe::pack_bf16x2(o[0], o[1]);
-    v.y = moe::pack_bf16x2(o[2], o[3]);
-    *reinterpret_cast<uint2 *>(crow + n_t0 + 4 * kb) = v;
-  } else {
+      for (int q = 1; q < kKSplit; ++q) {
+        acc[0] += red[j & 1][wave + q][0][lane];
+        acc[1] += red[j & 1][wave + q][1][lane];
+      }
+      // acc[t][i] = result for weight row n_t + 4 kb + i and the entry's token r16.
+      if (cur.dst_row >= 0 && cur.on[0]) {
+        const int i0 = item / items_per_entry, g = item - i0 * items_per_entry;
+        const int n_t0 = kSwiglu ? (g * kGroups + nw) * 16 : (g * kGroups + nw) * 32;
+        const int n_t1 = kSwiglu ? mi + n_t0 : n_t0 + 16;
+        uint16_t *crow = c + static_cast<size_t>(cur.dst_row) * ldc;
+        if (kSwiglu) {
+          float o[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (t == 0 || t1_on) {
-        uint2 v;
-        v.x = moe::pack_bf16x2(acc[t][0], acc[t][1]);
-        v.y = moe::pack_bf16x2(acc[t][2], acc[t][3]);
-        *reinterpret_cast<uint2 *>(crow + (t == 0 ? n_t0 : n_t1) + 4 * kb) = v;
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t gu = moe::pack_bf16x2(acc[0][i], acc[1][i]);
+            o[i] = moe::swiglu_clamp1(__uint_as_float(gu << 16),
+                                      __uint_as_float(gu & 0xFFFF0000u), limit);
+          }
+          uint2 v;
+          v.x = moe::pack_bf16x2(o[0], o[1]);
+          v.y = moe::pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2 *>(crow + n_t0 + 4 * kb) = v;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (t == 0 || cur.on[1]) {
+              uint2 v;
+              v.x = moe::pack_bf16x2(acc[t][0], acc[t][1]);
+              v.y = moe::pack_bf16x2(acc[t][2], acc[t][3]);
+              *reinterpret_cast<uint2 *>(crow + (t == 0 ? n_t0 : n_t1) + 4 * kb) = v;
+            }
+          }
+        }
       }
     }
+    acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (!has_next) break;  // uniform
+    item += G;
+    cur = nxt;
   }
 }
 
@@ -310,14 +425,20 @@ int k_split(int32_t k) {
 }
 
 template <bool kSwiglu>
-int launch_gemv_union(const char *name, int split, dim3 grid, void *stream, const uint16_t *a,
-                      int64_t lda, int32_t a_rows, int32_t a_per_slot,
+int launch_gemv_union(const char *name, int split, int32_t item_rows, void *stream,
+                      const uint16_t *a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
                       const uint64_t *packed_ptrs, const uint64_t *scale_ptrs,
                       const float *scale2, const int32_t *u_eid, const int32_t *u_slot,
                       int32_t rows, int32_t top_k, int32_t num_experts, uint16_t *c,
                       int64_t ldc, int32_t n, int32_t k, float limit) {
+  // At most every union entry is live: one block per item up to a full chip of blocks.
+  const int64_t items =
+      static_cast<int64_t>(rows) * top_k * (((kSwiglu ? n / 2 : n) + item_rows - 1) / item_rows);
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(items, int64_t{kSlotsPerCu} * kCus)));
   const auto go = [&](auto kern) {
-    return moe::launch(name, kern, grid, dim3(kThreads), 0, stream, a, lda, a_rows, a_per_slot,
+    return moe::launch(name, kern, grid, dim3(kThreads),
+                       static_cast<size_t>(rows) * top_k * kEntryLdsBytes, stream, a, lda, a_rows,
+                       a_per_slot,
                        packed_ptrs, scale_ptrs, scale2, u_eid, u_slot, rows, top_k, num_experts,
                        c, ldc, n, k, limit);
   };
@@ -333,8 +454,8 @@ int check_union_gemv_args(const char *name, const uint16_t *a, int64_t lda, int3
                           int64_t ldc, int32_t n, int32_t n_out, int32_t k) {
   MOE_REQUIRE(rows >= 0 && rows <= kMaxRows, "%s: rows must be in [0, %d] (got %d)", name,
               kMaxRows, rows);
-  MOE_REQUIRE(top_k >= 1 && static_cast<int64_t>(rows) * top_k <= kUnionMaxIds,
-              "%s: need top_k >= 1 and rows * top_k <= %d", name, kUnionMaxIds);
+  MOE_REQUIRE(top_k >= 1 && static_cast<int64_t>(rows) * top_k <= kGemvMaxIds,
+              "%s: need top_k >= 1 and rows * top_k <= %d", name, kGemvMaxIds);
   MOE_REQUIRE(k > 0 && k % kChunkK == 0, "%s: k must be a positive multiple of %d (got %d)",
               name, kChunkK, k);
   MOE_REQUIRE(n > 0 && n % 16 == 0, "%s: n must be a positive multiple of 16 (got %d)", name, n);
@@ -348,8 +469,10 @@ int check_union_gemv_args(const char *name, const uint16_t *a, int64_t lda, int3
   MOE_REQUIRE((reinterpret_cast<uintptr_t>(c) & 7u) == 0, "%s: c must be 8-byte aligned", name);
   MOE_REQUIRE(a_rows >= 1 && static_cast<uint64_t>(a_rows) * lda * 2 < (1ull << 31),
               "%s: need a_rows >= 1 and an activation buffer smaller than 2 GiB", name);
-  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 32),
-              "%s: one expert's packed weights must be smaller than 4 GiB", name);
+  // Buffer offsets are 32-bit and a skipped load uses offset 2^31: one expert's packed
+  // weights stay below 2 GiB.
+  MOE_REQUIRE(static_cast<uint64_t>(n) * k / 2 < (1ull << 31),
+              "%s: one expert's packed weights must be smaller than 2 GiB", name);
   return MOE_OK;
 }
 
@@ -384,11 +507,10 @@ extern "C" int moe_w4a16_gemv_union(const uint16_t *a, int64_t lda, int32_t a_ro
                                        n, n, k);
   if (rc != MOE_OK || rows == 0) return rc;
   const int split = k_split(k);
-  const int rows_per_block = 32 * (kWaves / split);
-  const dim3 grid((n + rows_per_block - 1) / rows_per_block, rows * top_k);
-  return launch_gemv_union<false>("moe_w4a16_gemv_union", split, grid, stream, a, lda, a_rows,
-                                  a_per_slot != 0, packed_ptrs, scale_ptrs, scale2, u_eid, u_slot,
-                                  rows, top_k, num_experts, c, ldc, n, k, 0.0f);
+  return launch_gemv_union<false>("moe_w4a16_gemv_union", split, 32 * (kWaves / split), stream,
+                                  a, lda, a_rows, a_per_slot != 0, packed_ptrs, scale_ptrs,
+                                  scale2, u_eid, u_slot, rows, top_k, num_experts, c, ldc, n, k,
+                                  0.0f);
 }
 
 extern "C" int moe_w4a16_gemv_union_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -407,9 +529,8 @@ extern "C" int moe_w4a16_gemv_union_swiglu(const uint16_t *a, int64_t lda, int32
                                        num_experts, act, ld_act, 2 * mi, mi, k);
   if (rc != MOE_OK || rows == 0) return rc;
   const int split = k_split(k);
-  const int gate_rows_per_block = 16 * (kWaves / split);
-  const dim3 grid((mi + gate_rows_per_block - 1) / gate_rows_per_block, rows * top_k);
-  return launch_gemv_union<true>("moe_w4a16_gemv_union_swiglu", split, grid, stream, a, lda,
-                                 a_rows, a_per_slot != 0, packed_ptrs, scale_ptrs, scale2, u_eid,
-                                 u_slot, rows, top_k, num_experts, act, ld_act, 2 * mi, k, limit);
+  return launch_gemv_union<true>("moe_w4a16_gemv_union_swiglu", split, 16 * (kWaves / split),
+                                 stream, a, lda, a_rows, a_per_slot != 0, packed_ptrs, scale_ptrs,
+                                 scale2, u_eid, u_slot, rows, top_k, num_experts, act, ld_act,
+                                 2 * mi, k, limit);
 }

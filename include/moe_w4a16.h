@@ -169,8 +169,9 @@ int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_
  * Requirements (else MOE_EINVAL): n > 0 and n % 16 == 0; k > 0 and k % 256 == 0;
  * lda >= k and ldc >= n, both multiples of 8; a and c 16-byte aligned; num_experts >= 1;
  * max_rows >= 0; a_rows >= 1 when max_rows > 0; a, packed_ptrs, scale_ptrs, scale2,
- * expert_offsets and c non-NULL. Each table address must be 16-byte aligned (not checked:
- * device data). max_rows == 0 enqueues nothing.
+ * expert_offsets and c non-NULL; the activation buffer and one expert's packed weights
+ * below 2 GiB. Each table address must be 16-byte aligned (not checked: device data).
+ * max_rows == 0 enqueues nothing.
  */
 int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
                            const int32_t *a_gather, const uint64_t *packed_ptrs,
@@ -294,6 +295,7 @@ int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales, float s
 /* Limits of the decode / verify path. */
 #define MOE_UNION_MAX_IDS 1024 /* rows * top_k of moe_row_union (one workgroup) */
 #define MOE_UNION_MAX_ROWS 16  /* rows of moe_w4a16_gemv_union (one matrix-core tile) */
+#define MOE_UNION_GEMV_MAX_IDS 512 /* rows * top_k of moe_w4a16_gemv_union */
 
 /*
  * moe_row_union - the union of the experts a few rows selected ([FWD] workspace fields
@@ -342,9 +344,10 @@ int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t 
  *   c       bf16 [rows * top_k, ldc] output, laid out by (row, slot)
  *
  * Requirements (else MOE_EINVAL): 0 <= rows <= MOE_UNION_MAX_ROWS; top_k >= 1 and
- * rows * top_k <= MOE_UNION_MAX_IDS; n > 0, n % 16 == 0; k > 0, k % 256 == 0; lda >= k,
+ * rows * top_k <= MOE_UNION_GEMV_MAX_IDS; n > 0, n % 16 == 0; k > 0, k % 256 == 0; lda >= k,
  * a multiple of 8; ldc >= n, a multiple of 4; a 16-byte and c 8-byte aligned;
- * num_experts >= 1; a_rows >= 1; required pointers non-NULL. rows == 0 enqueues nothing.
+ * num_experts >= 1; a_rows >= 1; required pointers non-NULL; the activation buffer and one
+ * expert's packed weights below 2 GiB. rows == 0 enqueues nothing.
  */
 int moe_w4a16_gemv_union(const uint16_t *a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
                          const uint64_t *packed_ptrs, const uint64_t *scale_ptrs,
