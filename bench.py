@@ -19,9 +19,14 @@ over the same rows: moe_dense_gate_up_swiglu_bf16 then moe_dense_gemm_bf16) afte
 timed steps, outside ``value``; ``--with-shared`` runs it inside each step instead and
 feeds its output to the combine.
 
+``decode`` times the decode / verify path on the small-M workload (8 rows, 256 experts,
+half of them absent) after the timed steps, outside ``value``: the union path
+(moe_row_union -> union GEMVs -> combine) and the sorted path on the same rows.
+``--decode`` runs the main step itself through the union path (rows <= 16).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe] [--unfused] [--device-router]
-                       [--with-shared] [--no-shared]
+                       [--with-shared] [--no-shared] [--decode] [--no-decode]
 """
 
 from __future__ import annotations
@@ -104,6 +109,11 @@ def parse():
                          "combine)")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the separate shared-expert measurement")
+    ap.add_argument("--decode", action="store_true",
+                    help="run the step through the decode path (union of the rows' experts, "
+                         "each swept once; rows <= 16)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the separate decode-path measurement")
     return ap.parse_args()
 
 
@@ -235,6 +245,86 @@ def time_shared_expert(se, x, w, steps, torch, stream):
             "total_us": round((gu + dn) * 1e6, 2)}
 
 
+def time_decode_leg(hip, torch, steps):
+    """The decode / verify path on the small-M workload (8 rows over 256 experts, experts
+    [128, 256) absent), timed per stage with HIP events: the union path (moe_row_union ->
+    union GEMV gate_up with the SwiGLU -> union GEMV down -> combine) and the sorted path
+    (moe_align -> zero -> grouped GEMMs -> combine) on the same rows. GB/s is unique
+    weight bytes (live experts, both projections) per step."""
+    import workloads as wl
+
+    w = wl.WORKLOADS["small_m"]
+    gt, dt, ids, wts, x, ids_host = upload_workload(hip, w, torch)
+    rows, mi, hidden, top_k = w.rows, w.moe_intermediate, w.hidden, w.top_k
+    s = rows * top_k
+    ws = hip.Workspace(rows, top_k, w.num_experts, hidden, mi)
+    dws = hip.DecodeWorkspace(rows, top_k, hidden, mi)
+    out = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    u_slot = dws.u_slot[:s * rows]
+    n_gu, k_gu = wl.gate_up_shape(w)
+    n_dn, k_dn = wl.down_shape(w)
+    live = sorted({int(e) for e in ids_host.reshape(-1) if not w.is_null(int(e))})
+    wbytes = len(live) * (proj_bytes(n_gu, k_gu) + proj_bytes(n_dn, k_dn))
+    gu_alg = (len(live) * proj_bytes(n_gu, k_gu) + rows * hidden * 2
+              + int(sum(1 for e in ids_host.reshape(-1) if not w.is_null(int(e)))) * mi * 2)
+    paths = {
+        "union": [
+            ("moe_row_union", lambda: hip.moe_row_union(ids, w.num_experts, dws.u_eid, u_slot,
+                                                        dws.slot_perm, dws.counters)),
+            ("zero_expert_out", lambda: dws.expert_out[:s].zero_()),
+            ("gemv_union_gate_up_swiglu", lambda: hip.moe_w4a16_gemv_union_swiglu(
+                x, gt, dws.u_eid, u_slot, dws.act, w.limit, rows, top_k)),
+            ("gemv_union_down", lambda: hip.moe_w4a16_gemv_union(
+                dws.act, dt, dws.u_eid, u_slot, dws.expert_out, rows, top_k, a_per_slot=True)),
+            ("moe_combine", lambda: hip.moe_combine(dws.expert_out[:s], dws.slot_perm[:s], wts,
+                                                    out))],
+        "sorted": [
+            ("moe_align", lambda: hip.moe_align(ids, w.num_experts, ws.sorted_token_ids,
+                                                ws.sorted_expert_ids, ws.expert_offsets,
+                                                ws.token_to_perm, ws.active_experts,
+                                                ws.counters)),
+            ("zero_expert_out", lambda: ws.expert_out[:s].zero_()),
+            ("grouped_gemm_gate_up_swiglu", lambda: hip.moe_w4a16_grouped_gemm_swiglu(
+                x, gt, ws.expert_offsets, ws.act, w.limit, ws.sorted_token_ids, max_rows=s)),
+            ("grouped_gemm_down", lambda: hip.moe_w4a16_grouped_gemm(
+                ws.act, dt, ws.expert_offsets, ws.expert_out, None, max_rows=s)),
+            ("moe_combine", lambda: hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts,
+                                                    out))],
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, stages in paths.items():
+        for _ in range(3):
+            for _, fn in stages:
+                fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            for j, (_, fn) in enumerate(stages):
+                ev[i][j].record(stream)
+                fn()
+            ev[i][len(stages)].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        step_us = t0.elapsed_time(t1) * 1000.0 / steps
+        kus = {n: round(float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0
+                                       for i in range(steps)])), 2)
+               for j, (n, _) in enumerate(stages)}
+        res[name] = {"step_us": round(step_us, 2), "GBps": round(wbytes / step_us / 1e3, 1),
+                     "kernel_us": kus}
+    gu_us = res["union"]["kernel_us"]["gemv_union_gate_up_swiglu"]
+    achieved = gu_alg / gu_us / 1e3
+    return {"workload": w.name, "rows": rows, "live_experts": len(live),
+            "unique_weight_bytes": int(wbytes), **res,
+            "roofline": {"kernel": "moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)",
+                         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": int(gu_alg)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,6 +346,10 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.with_shared and w.moe_intermediate == 0:
         print(f"bench.py: {w.name} is a single GEMM; it has no shared expert", file=sys.stderr)
+        sys.exit(2)
+    if args.decode and (w.chunk > hip.UNION_MAX_ROWS or w.moe_intermediate == 0):
+        print(f"bench.py: the decode path takes layer workloads of at most "
+              f"{hip.UNION_MAX_ROWS} rows per step ({w.name} has {w.chunk})", file=sys.stderr)
         sys.exit(2)
     t_gen = time.perf_counter()
     gt, dt, ids_all, wts_all, x_all, ids_host = upload_workload(hip, w, torch)
@@ -339,24 +433,54 @@ def main():
     def st_combine(x, ids, wts):
         hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out, shared_out[0])
 
+    # The decode path: the union of the rows' experts, outputs by (row, slot).
+    dws = hip.DecodeWorkspace(rows, w.top_k, hidden, mi) if args.decode else None
+
+    def st_union(x, ids, wts):
+        hip.moe_row_union(ids, w.num_experts, dws.u_eid, dws.u_slot[:s * rows], dws.slot_perm,
+                          dws.counters)
+
+    def st_union_zero(x, ids, wts):
+        dws.expert_out[:s].zero_()
+
+    def st_union_gate_up(x, ids, wts):
+        hip.moe_w4a16_gemv_union_swiglu(x, gt, dws.u_eid, dws.u_slot[:s * rows], dws.act,
+                                        w.limit, rows, w.top_k)
+
+    def st_union_down(x, ids, wts):
+        hip.moe_w4a16_gemv_union(dws.act, dt, dws.u_eid, dws.u_slot[:s * rows],
+                                 dws.expert_out, rows, w.top_k, a_per_slot=True)
+
+    def st_union_combine(x, ids, wts):
+        hip.moe_combine(dws.expert_out[:s], dws.slot_perm[:s], wts, out, shared_out[0])
+
     stages = [("moe_router_topk", st_router)] if args.device_router else []
-    stages.append(("moe_align", st_align))
-    if need_zero:
-        stages.append(("zero_expert_out", st_zero))
-    if args.unfused:
-        stages += [("grouped_gemm_gate_up", st_gate_up), ("swiglu_clamp", st_swiglu)]
-        gu_name = "grouped_gemm_gate_up"
+    if args.decode:
+        stages.append(("moe_row_union", st_union))
+        if need_zero:
+            stages.append(("zero_expert_out", st_union_zero))
+        stages += [("gemv_union_gate_up_swiglu", st_union_gate_up),
+                   ("gemv_union_down", st_union_down)]
+        gu_name, dn_name = "gemv_union_gate_up_swiglu", "gemv_union_down"
     else:
-        stages.append(("grouped_gemm_gate_up_swiglu", st_gate_up_swiglu))
-        gu_name = "grouped_gemm_gate_up_swiglu"
-    stages.append(("grouped_gemm_down", st_down))
+        stages.append(("moe_align", st_align))
+        if need_zero:
+            stages.append(("zero_expert_out", st_zero))
+        if args.unfused:
+            stages += [("grouped_gemm_gate_up", st_gate_up), ("swiglu_clamp", st_swiglu)]
+            gu_name = "grouped_gemm_gate_up"
+        else:
+            stages.append(("grouped_gemm_gate_up_swiglu", st_gate_up_swiglu))
+            gu_name = "grouped_gemm_gate_up_swiglu"
+        stages.append(("grouped_gemm_down", st_down))
+        dn_name = "grouped_gemm_down"
     if args.with_shared:
         stages.append(("shared_expert", st_shared))
         # its BF16 weights are unique weight bytes of the step too
         for c in range(n_chunks):
             step_bytes[c] += 3 * mi * hidden * 2
             step_flops[c] += 2.0 * rows * 3 * mi * hidden
-    stages.append(("moe_combine", st_combine))
+    stages.append(("moe_combine", st_union_combine if args.decode else st_combine))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
 
@@ -404,7 +528,7 @@ def main():
     tflops = total_flops / (gpu_ms / 1000.0) / 1e12
 
     gu_s = np.array(per[gu_name]) / 1000.0
-    dn_s = np.array(per["grouped_gemm_down"]) / 1000.0
+    dn_s = np.array(per[dn_name]) / 1000.0
     gu_alg = np.array([gu_bytes_alg[c] for c in chunk_of])
     achieved = float(np.mean(gu_alg) / np.mean(gu_s) / 1e9)
 
@@ -415,7 +539,8 @@ def main():
                 "TFLOPs": round(float(np.mean([fl[c] for c in chunk_of])) / t / 1e12, 2)}
 
     per_gemm = {"gate_up": gemm_line(gu_w, gu_fl, gu_s), "down": gemm_line(dn_w, dn_fl, dn_s)}
-    kernel_label = ("moe_w4a16_grouped_gemm (gate_up)" if args.unfused
+    kernel_label = ("moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)" if args.decode
+                    else "moe_w4a16_grouped_gemm (gate_up)" if args.unfused
                     else "moe_w4a16_grouped_gemm_swiglu (gate_up + SwiGLU)")
     roofline = {"kernel": kernel_label, "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -426,6 +551,10 @@ def main():
     shared = None
     if se is not None and not args.with_shared:
         shared = time_shared_expert(se, x_all[:rows], w, args.steps, torch, stream)
+
+    decode = None
+    if w.name == "prefill_subchunk" and not args.no_decode and not args.decode:
+        decode = time_decode_leg(hip, torch, args.steps)
 
     if args.copy_probe:  # a plain copy of known size, for scaling HBM counters
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -454,6 +583,8 @@ def main():
         "device_router": bool(args.device_router),
         "shared_expert_in_step": bool(args.with_shared),
         "shared_expert": shared,
+        "decode_path": bool(args.decode),
+        "decode": decode,
         "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
         "wall_s": round(wall, 4),
         "kernel_us": kern_us,

@@ -267,3 +267,16 @@ def test_decode_layer_matches_sorted_layer_ragged(hip):
                                   w.limit, "bf16w")
     assert rel_err(got, ref) <= GATE
     assert rel_err(f64(out), ref) <= GATE
+
+
+def test_gemv_union_row_result_independent_of_sharing(hip):
+    """Which rows share a sweep never changes what a row gets: the same rows run as one
+    union and split into two unions give the same bits for every (row, slot)."""
+    rng, ids, experts, s2 = _problem(71, 8, 8, 24, 256, 2048)
+    a_bits = wl.bf16_normal(rng, (8, 2048))
+    whole, _, _, _ = _gemv_gpu(hip, a_bits, False, experts, s2, ids, 256, 2048)
+    lo, _, _, _ = _gemv_gpu(hip, a_bits[:3], False, experts, s2, ids[:3], 256, 2048)
+    hi, _, _, _ = _gemv_gpu(hip, a_bits[3:], False, experts, s2, ids[3:], 256, 2048)
+    split = np.concatenate([lo, hi])
+    assert np.array_equal(np.isnan(whole), np.isnan(split))
+    assert np.array_equal(whole, split)
