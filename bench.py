@@ -50,6 +50,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "grouped_gemm_gate_up_swiglu_prefill_subchunk_hbm_traffic.md")
 KERNEL_SOURCES = ("grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip",
                   "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h",
+                  "grouped_nvfp4_w4a16_amd/csrc/w4a16_mma.h",
                   "grouped_nvfp4_w4a16_amd/csrc/swiglu.h",
                   "grouped_nvfp4_w4a16_amd/csrc/buffer_io.h")
 METRIC = "grouped MoE W4A16 GEMM: HBM GB/s on unique weights + TFLOP/s, 256-row prefill"
