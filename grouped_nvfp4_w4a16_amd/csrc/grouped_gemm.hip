@@ -11,10 +11,13 @@
 // HBM once per launch.
 //
 // gfx950 design (the pages' mma.sync/shared-memory tiling is not used):
-//   - grid = (N / 128 weight-row tiles, experts); a block of 4 wave64s owns 128 weight
-//     rows of one expert over the whole K, and loops over that expert's sorted rows 16 at
-//     a time (one MFMA tile), so its weight bytes are streamed once per 16 rows (once per
-//     launch for an expert with at most 16 routed rows). Three blocks share a CU.
+//   - grid = (N / 128 weight-row tiles, experts + overflow chunks); a block of 4 wave64s
+//     owns 128 weight rows of one expert over the whole K, and loops over up to 64 of
+//     that expert's sorted rows 16 at a time (one MFMA tile), so its weight bytes are
+//     streamed once per 16 rows (once per launch for an expert with at most 16 routed
+//     rows). An expert's rows past its first 64 go to overflow blocks, 64 rows each, so
+//     a hot expert (skewed routing) is spread over several blocks instead of making one
+//     block run many passes while the rest of the chip idles. Three blocks share a CU.
 //     Workgroups are dealt to the 8 XCDs round-robin by linear id; the block index is
 //     remapped so that each XCD runs whole experts (XCD x: experts x, x + 8, ...), and an
 //     expert's activation rows are fetched into one L2 only (measured L2-to-memory reads
@@ -67,6 +70,7 @@ constexpr int kBlockN = kWaves * 16 * kTiles;     // weight rows per block
 constexpr int kHalfN = kBlockN / 2;               // block rows per tile index
 constexpr int kChunkK = 256;                      // k per main-loop step
 constexpr int kBlockM = 16;                       // sorted rows per pass: one MFMA tile
+constexpr int kChunkRows = 64;                    // sorted rows per block at most
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
@@ -122,6 +126,48 @@ __device__ __forceinline__ u32x4_t permute_scales(u32x4_t v) {
   return o;
 }
 
+// Rows of expert e the grouped GEMM covers: [max(off[e], 0), min(off[e + 1], max_rows)).
+// Beyond its first chunk_rows, an expert has overflow(e) = ceil(rows / chunk_rows) - 1
+// further chunks. Returns (expert, chunk index >= 1) of overflow chunk `oc` in expert
+// order, or (-1, 0) when there are at most `oc` overflow chunks. Every thread of the block
+// calls it (it holds barriers); all get the same answer.
+__device__ int2 find_overflow_chunk(const int32_t *__restrict__ offsets, int num_experts,
+                                    int chunk_rows, int max_rows, int oc) {
+  __shared__ int s_wave_sum[kWaves];
+  __shared__ int2 s_found;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_found = make_int2(-1, 0);
+  int carry = 0;
+  for (int base = 0; base < num_experts && carry <= oc; base += kThreads) {
+    const int x = base + tid;
+    int n_over = 0;
+    if (x < num_experts) {
+      const int rows = min(offsets[x + 1], max_rows) - max(offsets[x], 0);
+      n_over = rows > 0 ? (rows - 1) / chunk_rows : 0;
+    }
+    int incl = n_over;  // inclusive scan over the wave, then over the waves
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += t;
+    }
+    if (lane == 63) s_wave_sum[wave] = incl;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int ws = s_wave_sum[w];
+      if (w < wave) incl += ws;
+      total += ws;
+    }
+    const int excl = carry + incl - n_over;
+    if (n_over > 0 && excl <= oc && oc < excl + n_over) s_found = make_int2(x, oc - excl + 1);
+    carry += total;
+    __syncthreads();  // s_wave_sum is rewritten by the next round; s_found is published
+  }
+  return s_found;
+}
+
 // kSwiglu = false: c[s, n] for the N weight rows.
 // kSwiglu = true: N = 2 mi; c[s, j] = swiglu(gate sum of row j, up sum of row mi + j) for
 // j < mi (c is the activation buffer, ldc its leading dimension).
@@ -130,8 +176,9 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t a_rows,
     const int32_t *__restrict__ gather, const uint64_t *__restrict__ packed_ptrs,
     const uint64_t *__restrict__ scale_ptrs, const float *__restrict__ scale2s,
-    const int32_t *__restrict__ offsets, uint16_t *__restrict__ c, int64_t ldc,
-    int32_t max_rows, int32_t N, int32_t K, float limit) {
+    const int32_t *__restrict__ offsets, int32_t num_experts, int32_t chunk_rows,
+    uint16_t *__restrict__ c, int64_t ldc, int32_t max_rows, int32_t N, int32_t K,
+    float limit) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kLdsBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
@@ -141,19 +188,34 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   // fetched into one L2 only; with E a multiple of 8, XCD x runs experts x, x + 8, ...,
   // so a contiguous range of empty or absent experts (an expert-parallel rank's share,
   // a cold part of the expert range) is spread over all XCDs instead of idling some.
+  //
+  // Grid rows [0, num_experts) are the experts, each block taking the first chunk_rows of
+  // its expert's rows; rows past them are overflow chunks (the further chunk_rows-row
+  // pieces of heavily routed experts, in expert order), so that no block runs more than
+  // chunk_rows / 16 passes over its weights and a hot expert's rows spread over several
+  // blocks. The row order is reversed so that the overflow chunks are dispatched first.
   int e = blockIdx.y, tile = blockIdx.x;
   {
-    const int T = gridDim.x, E = gridDim.y;
+    const int T = gridDim.x, Y = gridDim.y;
     const int lin = blockIdx.y * T + blockIdx.x;
-    if ((E & 7) == 0) {
+    if ((Y & 7) == 0) {
       const int q = lin >> 3, el = q / T;
       tile = q - el * T;
       e = el * 8 + (lin & 7);
-    } else if (((T * E) & 7) == 0) {
-      const int r = (lin & 7) * ((T * E) >> 3) + (lin >> 3);
+    } else if (((T * Y) & 7) == 0) {
+      const int r = (lin & 7) * ((T * Y) >> 3) + (lin >> 3);
       e = r / T;
       tile = r - e * T;
     }
+    e = Y - 1 - e;
+  }
+  int chunk = 0;
+  if (e >= num_experts) {
+    const int2 found = find_overflow_chunk(offsets, num_experts, chunk_rows, max_rows,
+                                           e - num_experts);
+    if (found.x < 0) return;  // fewer overflow chunks than grid rows
+    e = found.x;
+    chunk = found.y;
   }
   // All of the expert's metadata in one memory round trip: the empty asm needs every
   // value before the early exits, so the five loads are issued together instead of one
@@ -164,8 +226,9 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   asm volatile("" ::"s"(packed_u), "s"(scales_u), "s"(scale2), "s"(off_lo), "s"(off_hi));
   const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_u);
   if (packed == nullptr) return;  // expert not present: its rows keep the caller's values
-  const int lo = max(off_lo, 0);
-  const int hi = min(off_hi, max_rows);
+  const int lo = max(off_lo, 0) + chunk * chunk_rows;
+  const int end = min(off_hi, max_rows);
+  const int hi = end - lo > chunk_rows ? lo + chunk_rows : end;  // no overflow at INT32_MAX
   if (hi <= lo) return;
   const uint8_t *scales = reinterpret_cast<const uint8_t *>(scales_u);
 
@@ -448,6 +511,23 @@ int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_
   return MOE_OK;
 }
 
+// Grid rows of a GEMM launch: the experts, then room for every overflow chunk. An expert
+// with r > 0 rows has ceil(r / kChunkRows) - 1 <= (r - 1) / kChunkRows overflow chunks, so
+// all experts together (at most max_rows rows) have fewer than max_rows / kChunkRows, i.e.
+// at most (max_rows - 1) / kChunkRows. The total is rounded up to a multiple of 8 (whole
+// experts per XCD). Where that would pass the grid's row limit, blocks take all of their
+// expert's rows (no overflow chunks).
+int grid_rows(int32_t num_experts, int32_t max_rows, int *chunk_rows) {
+  const int64_t rows = num_experts + static_cast<int64_t>(max_rows - 1) / kChunkRows;
+  const int64_t padded = (rows + 7) & ~static_cast<int64_t>(7);
+  if (padded <= 65535) {
+    *chunk_rows = kChunkRows;
+    return static_cast<int>(padded);
+  }
+  *chunk_rows = INT32_MAX;
+  return num_experts;
+}
+
 }  // namespace
 
 extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -462,10 +542,11 @@ extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_
   const int rc = check_gemm_args("grouped_gemm", a, lda, a_rows, packed_ptrs, scale_ptrs, scale2,
                                  expert_offsets, num_experts, c, ldc, max_rows, n, n, k);
   if (rc != MOE_OK || max_rows == 0) return rc;
-  const dim3 grid((n + kBlockN - 1) / kBlockN, num_experts);
+  int chunk_rows = 0;
+  const dim3 grid((n + kBlockN - 1) / kBlockN, grid_rows(num_experts, max_rows, &chunk_rows));
   return moe::launch("moe_w4a16_grouped_gemm", grouped_gemm_kernel<false>, grid, dim3(kThreads),
                      0, stream, a, lda, a_rows, a_gather, packed_ptrs, scale_ptrs, scale2,
-                     expert_offsets, c, ldc, max_rows, n, k, 0.0f);
+                     expert_offsets, num_experts, chunk_rows, c, ldc, max_rows, n, k, 0.0f);
 }
 
 extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -484,11 +565,12 @@ extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int
                                  scale2, expert_offsets, num_experts, act, ld_act, max_rows,
                                  2 * mi, mi, k);
   if (rc != MOE_OK || max_rows == 0) return rc;
-  const dim3 grid((mi + kHalfN - 1) / kHalfN, num_experts);
+  int chunk_rows = 0;
+  const dim3 grid((mi + kHalfN - 1) / kHalfN, grid_rows(num_experts, max_rows, &chunk_rows));
   return moe::launch("moe_w4a16_grouped_gemm_swiglu", grouped_gemm_kernel<true>, grid,
                      dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
-                     scale_ptrs, scale2, expert_offsets, act, ld_act, max_rows, 2 * mi, k,
-                     limit);
+                     scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows, act, ld_act,
+                     max_rows, 2 * mi, k, limit);
 }
 
 extern "C" int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales,

@@ -73,6 +73,7 @@ def _run_both(hip, experts, s2, offsets, x_bits, gather, mi, k, limit):
     (16, 768, [1, 33, 2], (), True, 3),                # one gate tile; three passes
     (192, 1024, [8, 8, 8, 8, 8, 8], (0, 5), False, 4),
     (48, 256, [40], (), True, 5),
+    (32, 512, [65, 0, 200, 64, 3], (3,), False, 6),  # experts past 64 rows: overflow blocks
 ])
 def test_fused_matches_two_calls_bitwise(hip, mi, k, counts, null, special, seed):
     experts, s2, offsets, x_bits, gather = _problem(seed, mi, k, counts, null, special)

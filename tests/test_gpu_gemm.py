@@ -208,6 +208,9 @@ def test_single_gemm_workload_vs_oracle(hip):
     (144, 768, [70, 1, 0, 15, 32, 9], (2,), 1),     # partial block of rows, long expert
     (400, 512, [5, 64, 0, 17], (0,), 2),            # ragged N tiles, exactly two passes
     (256, 2048, [129, 0, 2], (), 3),                # five passes
+    # experts past 64 rows: one block per 64 of them (64 fits one; 65, 128, 193 overflow),
+    # a null expert with overflow chunks keeps its rows
+    (48, 256, [64, 65, 0, 128, 193, 1, 130], (3,), 4),
 ])
 def test_ragged_shapes_and_nulls(hip, n, k, counts, null, seed):
     rng = np.random.default_rng(seed)
@@ -239,6 +242,23 @@ def test_no_gather_and_row_cut_off(hip):
     got = _gemm(hip, x_bits, experts, s2, offsets, n, k, rows=35, c_rows=60)
     assert np.all(got[35:] == -3.0)
     assert rel_err(got[:35], ref[:35]) <= GATE
+
+
+def test_row_cut_off_inside_an_overflow_chunk(hip):
+    """Experts of 150 and 100 rows (past 64: more blocks per expert), max_rows cutting the
+    second expert's rows inside its first chunk and the first expert's third chunk whole."""
+    rng = np.random.default_rng(8)
+    n, k = 32, 256
+    counts = [150, 100]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    x_bits = wl.bf16_normal(rng, (offsets[-1], k))
+    experts = [wl.random_nvfp4(rng, n, k) for _ in counts]
+    s2 = np.array([0.75, 1.5], np.float32)
+    ref = _oracle(x_bits, experts, s2, offsets, n, None, "bf16w")
+    for rows in (130, 180, 250):
+        got = _gemm(hip, x_bits, experts, s2, offsets, n, k, rows=rows, c_rows=250)
+        assert np.all(got[rows:] == -3.0)
+        assert rel_err(got[:rows], ref[:rows]) <= GATE
 
 
 def test_out_of_range_gather_reads_zeros(hip):
