@@ -122,6 +122,58 @@ __global__ __launch_bounds__(kUnionMaxIds) void row_union_kernel(
   }
 }
 
+// The same table for at most 64 ids, in one wave and without scans: lane t holds slot t.
+// The lanes holding the same valid id are found with one ballot per id bit; a slot is
+// covered when no lower lane of its row has its id, and opens an entry when no lower
+// covered lane has it. An entry's number is the count of openers below its opener.
+__global__ __launch_bounds__(64) void row_union_wave_kernel(
+    const int32_t *__restrict__ ids, int32_t rows, int32_t top_k, int32_t num_experts,
+    int32_t *__restrict__ u_eid, int32_t *__restrict__ u_slot, int32_t *__restrict__ slot_perm,
+    int32_t *__restrict__ counters) {
+  __shared__ int32_t s_slot[64 * 64];  // u_slot: [n_ids][rows], n_ids * rows <= 64 * 64
+  const int n_ids = rows * top_k;
+  const int t = threadIdx.x;
+  const int r = t / top_k, j = t - r * top_k;
+  int id = -1;
+  if (t < n_ids) {
+    const int v = ids[t];
+    if (v >= 0 && v < num_experts) id = v;
+  }
+  const bool valid = id >= 0;
+  const int bits = num_experts > 1 ? 32 - __clz(num_experts - 1) : 1;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {  // lanes whose valid id has the same bits as this one
+    const bool bit = (id >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    same &= bit ? ones : ~ones;
+  }
+  const uint64_t below = (1ull << t) - 1ull;
+  const uint64_t row_below = below & ~((1ull << (t - j)) - 1ull);  // lower lanes of the row
+  const bool covered = valid && (same & row_below) == 0;
+  const uint64_t cov = __ballot(covered);
+  const bool opens = covered && (same & cov & below) == 0;
+  const uint64_t openers = __ballot(opens);
+  const int n_union = __popcll(openers);
+  for (int q = t; q < n_ids * rows; q += 64) s_slot[q] = -1;
+  __syncthreads();
+  if (covered) {
+    const int first = __ffsll(static_cast<long long>(same & cov)) - 1;  // the entry's opener
+    const int p = __popcll(openers & ((1ull << first) - 1ull));
+    s_slot[p * rows + r] = j;
+  }
+  __syncthreads();
+  if (t < n_ids) {
+    if (opens) u_eid[__popcll(openers & below)] = id;
+    if (t >= n_union) u_eid[t] = -1;
+    if (slot_perm != nullptr) slot_perm[t] = covered ? t : -1;
+  }
+  for (int q = t; q < n_ids * rows; q += 64) u_slot[q] = s_slot[q];
+  if (counters != nullptr && t == 0) {
+    counters[0] = n_union;
+    counters[1] = n_ids - __popcll(cov);
+  }
+}
+
 // ------------------------------------------------------------------------- union GEMV
 
 constexpr int kWaves = 4;
@@ -490,6 +542,9 @@ extern "C" int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_
   if (rows == 0) return MOE_OK;
   MOE_REQUIRE(topk_ids && u_eid && u_slot, "row_union: a required pointer is NULL");
   const int n_ids = rows * top_k;
+  if (n_ids <= 64)
+    return moe::launch("moe_row_union", row_union_wave_kernel, dim3(1), dim3(64), 0, stream,
+                       topk_ids, rows, top_k, num_experts, u_eid, u_slot, slot_perm, counters);
   const int threads = (n_ids + 63) / 64 * 64;
   return moe::launch("moe_row_union", row_union_kernel, dim3(1), dim3(threads), 0, stream,
                      topk_ids, rows, top_k, num_experts, u_eid, u_slot, slot_perm, counters);

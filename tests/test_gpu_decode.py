@@ -32,7 +32,10 @@ def _union_gpu(hip, ids, num_experts):
 
 @pytest.mark.parametrize("rows,top_k,num_experts,seed", [
     (1, 8, 256, 0), (8, 8, 256, 1), (8, 8, 16, 2), (5, 3, 7, 3), (16, 8, 64, 4),
-    (128, 8, 256, 5), (1024, 1, 40, 6), (64, 16, 2048, 7)])
+    (128, 8, 256, 5), (1024, 1, 40, 6), (64, 16, 2048, 7),
+    # at most 64 ids (the one-wave kernel): one id per row, one row of 64, a single
+    # expert, heavy repeats, ids of 20 bits
+    (64, 1, 3, 8), (1, 64, 100, 9), (2, 32, 1, 10), (7, 9, 5, 11), (4, 16, 1 << 20, 12)])
 def test_row_union_bit_exact(hip, rows, top_k, num_experts, seed):
     rng = np.random.default_rng(seed)
     ids = rng.integers(-2, num_experts + 2, size=(rows, top_k)).astype(np.int32)
