@@ -15,9 +15,10 @@
 //     owns 128 weight rows of one expert over the whole K, and loops over up to 64 of
 //     that expert's sorted rows 16 at a time (one MFMA tile), so its weight bytes are
 //     streamed once per 16 rows (once per launch for an expert with at most 16 routed
-//     rows). An expert's rows past its first 64 go to overflow blocks, 64 rows each, so
-//     a hot expert (skewed routing) is spread over several blocks instead of making one
-//     block run many passes while the rest of the chip idles. Three blocks share a CU.
+//     rows). An expert with more than 64 rows is cut into 64-row chunks, each chunk an
+//     overflow block of its own, so a hot expert (skewed routing) is spread over several
+//     blocks instead of making one block run many passes while the rest of the chip
+//     idles. Three blocks share a CU.
 //     Workgroups are dealt to the 8 XCDs round-robin by linear id; the block index is
 //     remapped so that each XCD runs whole experts (XCD x: experts x, x + 8, ...), and an
 //     expert's activation rows are fetched into one L2 only (measured L2-to-memory reads
@@ -127,9 +128,10 @@ __device__ __forceinline__ u32x4_t permute_scales(u32x4_t v) {
 }
 
 // Rows of expert e the grouped GEMM covers: [max(off[e], 0), min(off[e + 1], max_rows)).
-// Beyond its first chunk_rows, an expert has overflow(e) = ceil(rows / chunk_rows) - 1
-// further chunks. Returns (expert, chunk index >= 1) of overflow chunk `oc` in expert
-// order, or (-1, 0) when there are at most `oc` overflow chunks. Every thread of the block
+// An expert with more than chunk_rows rows is done wholly by overflow blocks, one per
+// chunk_rows-row chunk: overflow(e) = ceil(rows / chunk_rows) chunks, else none. Returns
+// (expert, chunk index) of overflow chunk `oc` in expert order, or (-1, 0) when there are
+// at most `oc` overflow chunks. Every thread of the block
 // calls it (it holds barriers); all get the same answer.
 __device__ int2 find_overflow_chunk(const int32_t *__restrict__ offsets, int num_experts,
                                     int chunk_rows, int max_rows, int oc) {
@@ -143,7 +145,7 @@ __device__ int2 find_overflow_chunk(const int32_t *__restrict__ offsets, int num
     int n_over = 0;
     if (x < num_experts) {
       const int rows = min(offsets[x + 1], max_rows) - max(offsets[x], 0);
-      n_over = rows > 0 ? (rows - 1) / chunk_rows : 0;
+      n_over = rows > chunk_rows ? (rows + chunk_rows - 1) / chunk_rows : 0;
     }
     int incl = n_over;  // inclusive scan over the wave, then over the waves
 #pragma unroll
@@ -161,7 +163,7 @@ __device__ int2 find_overflow_chunk(const int32_t *__restrict__ offsets, int num
       total += ws;
     }
     const int excl = carry + incl - n_over;
-    if (n_over > 0 && excl <= oc && oc < excl + n_over) s_found = make_int2(x, oc - excl + 1);
+    if (n_over > 0 && excl <= oc && oc < excl + n_over) s_found = make_int2(x, oc - excl);
     carry += total;
     __syncthreads();  // s_wave_sum is rewritten by the next round; s_found is published
   }
@@ -189,11 +191,12 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   // so a contiguous range of empty or absent experts (an expert-parallel rank's share,
   // a cold part of the expert range) is spread over all XCDs instead of idling some.
   //
-  // Grid rows [0, num_experts) are the experts, each block taking the first chunk_rows of
-  // its expert's rows; rows past them are overflow chunks (the further chunk_rows-row
-  // pieces of heavily routed experts, in expert order), so that no block runs more than
-  // chunk_rows / 16 passes over its weights and a hot expert's rows spread over several
-  // blocks. The row order is reversed so that the overflow chunks are dispatched first.
+  // Grid rows [0, num_experts) are the experts with at most chunk_rows rows; rows past
+  // them are overflow chunks (the chunk_rows-row pieces of the more heavily routed
+  // experts, in expert order), so that no block runs more than chunk_rows / 16 passes
+  // over its weights and a hot expert's rows spread over several blocks. The row order is
+  // reversed so that the overflow chunks are dispatched first, the chunks of one expert
+  // next to each other (they read the same weights at about the same time).
   int e = blockIdx.y, tile = blockIdx.x;
   {
     const int T = gridDim.x, Y = gridDim.y;
@@ -210,7 +213,8 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     e = Y - 1 - e;
   }
   int chunk = 0;
-  if (e >= num_experts) {
+  const bool over = e >= num_experts;
+  if (over) {
     const int2 found = find_overflow_chunk(offsets, num_experts, chunk_rows, max_rows,
                                            e - num_experts);
     if (found.x < 0) return;  // fewer overflow chunks than grid rows
@@ -226,8 +230,9 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   asm volatile("" ::"s"(packed_u), "s"(scales_u), "s"(scale2), "s"(off_lo), "s"(off_hi));
   const uint8_t *packed = reinterpret_cast<const uint8_t *>(packed_u);
   if (packed == nullptr) return;  // expert not present: its rows keep the caller's values
-  const int lo = max(off_lo, 0) + chunk * chunk_rows;
   const int end = min(off_hi, max_rows);
+  if (!over && end - max(off_lo, 0) > chunk_rows) return;  // left to overflow blocks
+  const int lo = max(off_lo, 0) + chunk * chunk_rows;
   const int hi = end - lo > chunk_rows ? lo + chunk_rows : end;  // no overflow at INT32_MAX
   if (hi <= lo) return;
   const uint8_t *scales = reinterpret_cast<const uint8_t *>(scales_u);
@@ -512,13 +517,13 @@ int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_
 }
 
 // Grid rows of a GEMM launch: the experts, then room for every overflow chunk. An expert
-// with r > 0 rows has ceil(r / kChunkRows) - 1 <= (r - 1) / kChunkRows overflow chunks, so
-// all experts together (at most max_rows rows) have fewer than max_rows / kChunkRows, i.e.
-// at most (max_rows - 1) / kChunkRows. The total is rounded up to a multiple of 8 (whole
+// with r > C = kChunkRows rows has ceil(r / C) <= 2 r / (C + 1) chunks (the left side steps
+// to k + 1 at r = k C + 1, where 2 (k C + 1) >= (k + 1)(C + 1) because (k - 1)(C - 1) >= 0),
+// so all experts together (at most max_rows rows) have at most 2 max_rows / (C + 1). The total is rounded up to a multiple of 8 (whole
 // experts per XCD). Where that would pass the grid's row limit, blocks take all of their
 // expert's rows (no overflow chunks).
 int grid_rows(int32_t num_experts, int32_t max_rows, int *chunk_rows) {
-  const int64_t rows = num_experts + static_cast<int64_t>(max_rows - 1) / kChunkRows;
+  const int64_t rows = num_experts + 2 * static_cast<int64_t>(max_rows) / (kChunkRows + 1);
   const int64_t padded = (rows + 7) & ~static_cast<int64_t>(7);
   if (padded <= 65535) {
     *chunk_rows = kChunkRows;
