@@ -163,11 +163,14 @@ int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_
  *                   layout table row "remote expert (EP)").
  *   scale_ptrs      uint64 [num_experts] device addresses (non-zero where packed is).
  *   scale2          float  [num_experts]
- *   expert_offsets  int32  [num_experts + 1] as written by moe_align
+ *   expert_offsets  int32  [num_experts + 1] as written by moe_align: non-decreasing (a
+ *                   prefix sum). Other values are not checked (device data); each row the
+ *                   call writes still lies in [0, max_rows), but rows may then be missed.
  *   c               bf16   [max_rows, ldc] output rows in expert-sorted order
  *
  * Requirements (else MOE_EINVAL): n > 0 and n % 16 == 0; k > 0 and k % 256 == 0;
- * lda >= k and ldc >= n, both multiples of 8; a and c 16-byte aligned; num_experts >= 1;
+ * lda >= k and ldc >= n, both multiples of 8; a and c 16-byte aligned;
+ * 1 <= num_experts <= 65535;
  * max_rows >= 0; a_rows >= 1 when max_rows > 0; a, packed_ptrs, scale_ptrs, scale2,
  * expert_offsets and c non-NULL; the activation buffer and one expert's packed weights
  * below 2 GiB. Each table address must be 16-byte aligned (not checked: device data).
