@@ -72,6 +72,7 @@ constexpr int kHalfN = kBlockN / 2;               // block rows per tile index
 constexpr int kChunkK = 256;                      // k per main-loop step
 constexpr int kBlockM = 16;                       // sorted rows per pass: one MFMA tile
 constexpr int kChunkRows = 64;                    // sorted rows per block at most
+constexpr int kFrontChunks = 16;                  // overflow rows dispatched before experts
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
 constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
@@ -186,17 +187,23 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
 
   // Workgroups go to the 8 XCDs round-robin by linear id. Remap (a bijection on the
-  // grid) so that each XCD runs whole experts, an expert's activation rows then being
-  // fetched into one L2 only; with E a multiple of 8, XCD x runs experts x, x + 8, ...,
-  // so a contiguous range of empty or absent experts (an expert-parallel rank's share,
-  // a cold part of the expert range) is spread over all XCDs instead of idling some.
+  // grid) so that each XCD runs whole grid rows, an expert's activation rows then being
+  // fetched into one L2 only; with the row count a multiple of 8, an XCD runs every
+  // eighth row, so a contiguous range of empty or absent experts (an expert-parallel
+  // rank's share, a cold part of the expert range) is spread over all XCDs instead of
+  // idling some.
   //
   // Grid rows [0, num_experts) are the experts with at most chunk_rows rows; rows past
   // them are overflow chunks (the chunk_rows-row pieces of the more heavily routed
   // experts, in expert order), so that no block runs more than chunk_rows / 16 passes
-  // over its weights and a hot expert's rows spread over several blocks. The row order is
-  // reversed so that the overflow chunks are dispatched first, the chunks of one expert
-  // next to each other (they read the same weights at about the same time).
+  // over its weights and a hot expert's rows spread over several blocks. The first
+  // kFrontChunks overflow rows are dispatched first (the longest blocks start first, the
+  // chunks of one expert next to each other, reading the same weights at about the same
+  // time), then the experts in order (a contiguous range of absent ones, an
+  // expert-parallel rank's share, exits at the tail), then the remaining overflow rows.
+  // The room for overflow chunks is a worst-case bound; the rows past the actual chunks
+  // exit after one scan of the offsets, and dispatching only a few of them first keeps
+  // that cost off the start of a launch whose experts are all light.
   int e = blockIdx.y, tile = blockIdx.x;
   {
     const int T = gridDim.x, Y = gridDim.y;
@@ -210,7 +217,8 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       e = r / T;
       tile = r - e * T;
     }
-    e = Y - 1 - e;
+    const int front = min(Y - num_experts, kFrontChunks);
+    e = e < front ? num_experts + e : (e < front + num_experts ? e - front : e);
   }
   int chunk = 0;
   const bool over = e >= num_experts;
@@ -519,11 +527,14 @@ int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_
 // Grid rows of a GEMM launch: the experts, then room for every overflow chunk. An expert
 // with r > C = kChunkRows rows has ceil(r / C) <= 2 r / (C + 1) chunks (the left side steps
 // to k + 1 at r = k C + 1, where 2 (k C + 1) >= (k + 1)(C + 1) because (k - 1)(C - 1) >= 0),
-// so all experts together (at most max_rows rows) have at most 2 max_rows / (C + 1). The total is rounded up to a multiple of 8 (whole
-// experts per XCD). Where that would pass the grid's row limit, blocks take all of their
-// expert's rows (no overflow chunks).
+// so all experts together (at most max_rows rows) have at most 2 max_rows / (C + 1), and
+// none when max_rows <= C. The total is rounded up to a multiple of 8 (whole experts per
+// XCD). Where that would pass the grid's row limit, blocks take all of their expert's rows
+// (no overflow chunks).
 int grid_rows(int32_t num_experts, int32_t max_rows, int *chunk_rows) {
-  const int64_t rows = num_experts + 2 * static_cast<int64_t>(max_rows) / (kChunkRows + 1);
+  const int64_t chunks =
+      max_rows > kChunkRows ? 2 * static_cast<int64_t>(max_rows) / (kChunkRows + 1) : 0;
+  const int64_t rows = num_experts + chunks;
   const int64_t padded = (rows + 7) & ~static_cast<int64_t>(7);
   if (padded <= 65535) {
     *chunk_rows = kChunkRows;
