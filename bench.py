@@ -209,21 +209,30 @@ def time_shared_expert(se, x, w, steps, torch, stream):
 
     rows, hidden, inter = x.shape[0], w.hidden, w.moe_intermediate
     act, outb = se.act[:rows], se.out[:rows]
-    launches = (lambda: hip.moe_dense_gate_up_swiglu_bf16(x, se.gate_w, se.up_w, act, w.limit),
-                lambda: hip.moe_dense_gemm_bf16(act, se.down_w, outb))
-    for _ in range(3):
-        se(x, w.limit)
-    torch.cuda.synchronize()
-    secs = []
-    for fn in launches:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
+
+    def timed(ws):
+        launches = (lambda: hip.moe_dense_gate_up_swiglu_bf16(x, se.gate_w, se.up_w, act,
+                                                              w.limit, workspace=ws),
+                    lambda: hip.moe_dense_gemm_bf16(act, se.down_w, outb, workspace=ws))
+        for _ in range(3):
+            for fn in launches:
+                fn()
         torch.cuda.synchronize()
-        secs.append(e0.elapsed_time(e1) / 1000.0 / steps)
-    gu, dn = secs
+        secs = []
+        for fn in launches:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            secs.append(e0.elapsed_time(e1) / 1000.0 / steps)
+        return secs
+
+    # the split-K form (the shared expert's own, through its workspace), then the
+    # single-pass form for comparison
+    gu, dn = timed(se.workspace)
+    gu1, dn1 = timed(None)
 
     def roof(name, secs, wbytes, in_bytes, out_bytes, flops):
         nbytes = wbytes + in_bytes + out_bytes
@@ -243,7 +252,9 @@ def time_shared_expert(se, x, w, steps, torch, stream):
                                    2.0 * rows * 2 * inter * hidden),
             "down": roof("moe_dense_gemm_bf16", dn, hidden * inter * 2, rows * inter * 2,
                          rows * hidden * 2, 2.0 * rows * hidden * inter),
-            "total_us": round((gu + dn) * 1e6, 2)}
+            "total_us": round((gu + dn) * 1e6, 2), "form": "split-K (workspace)",
+            "single_pass_us": {"gate_up_swiglu": round(gu1 * 1e6, 2),
+                               "down": round(dn1 * 1e6, 2)}}
 
 
 def time_decode_leg(hip, torch, steps):

@@ -33,7 +33,8 @@ __all__ = [
     "load", "MoeError", "moe_align", "moe_w4a16_grouped_gemm", "swiglu_clamp", "moe_combine",
     "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "moe_router_topk",
     "moe_layer_from_logits", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
-    "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "SharedExpert",
+    "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "moe_dense_workspace_bytes",
+    "dense_workspace", "SharedExpert",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
     "moe_layer_decode", "UNION_MAX_ROWS",
 ]
@@ -45,7 +46,7 @@ EXPORTS = (
     "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
-    "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu",
+    "moe_dense_workspace_bytes", "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu",
 )
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
@@ -75,10 +76,12 @@ _SIGNATURES = {
     "moe_w4a16_dequant_bf16": ([_vp, _vp, _f32, _vp, _i32, _i32, _vp], ctypes.c_int),
     "moe_router_topk": ([_vp, _i64, _i32, _i32, _vp, _i32, _f32, _i32, _vp, _vp, _vp],
                         ctypes.c_int),
-    "moe_dense_gemm_bf16": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
-                            ctypes.c_int),
+    "moe_dense_gemm_bf16": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp, _i64,
+                             _vp], ctypes.c_int),
     "moe_dense_gate_up_swiglu_bf16": (
-        [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp], ctypes.c_int),
+        [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _i64, _vp],
+        ctypes.c_int),
+    "moe_dense_workspace_bytes": ([_i32, _i32, _i32, _i32], _i64),
     "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_w4a16_gemv_union": (
         [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32,
@@ -385,9 +388,35 @@ def moe_w4a16_dequant_bf16(packed, scales, scale2: float, out, stream=None) -> N
         _p(packed), _p(scales), float(scale2), _p(out), n, k, _stream(stream)))
 
 
-def moe_dense_gemm_bf16(a, b, c, stream=None) -> None:
+def moe_dense_workspace_bytes(m: int, n: int, k: int, swiglu: bool = False) -> int:
+    """Bytes of the split-K workspace of moe_dense_gemm_bf16 (``n`` = output width) or of
+    moe_dense_gate_up_swiglu_bf16 (``swiglu=True``, ``n`` = inter) at these sizes."""
+    return int(load().moe_dense_workspace_bytes(int(m), int(n), int(k), 1 if swiglu else 0))
+
+
+def dense_workspace(m: int, n: int, k: int, swiglu: bool = False, device="cuda"):
+    """A uint8 device tensor sized for the split-K form at these sizes."""
+    import torch
+
+    return torch.empty(max(moe_dense_workspace_bytes(m, n, k, swiglu), 1), dtype=torch.uint8,
+                       device=device)
+
+
+def _workspace(ws):
+    import torch
+
+    if ws is None:
+        return None, 0
+    _want(ws, torch.uint8, "workspace")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return _p(ws), ws.numel()
+
+
+def moe_dense_gemm_bf16(a, b, c, stream=None, workspace=None) -> None:
     """``c[m, n] = a[m, :] @ b[n, :]`` (BF16 in and out, FP32 accumulation) over
-    ``a [M, K]``, ``b [N, K]`` and ``c [M, N]`` row-major views."""
+    ``a [M, K]``, ``b [N, K]`` and ``c [M, N]`` row-major views. With ``workspace`` (see
+    ``dense_workspace``) it runs split over K with larger tiles."""
     a, lda = _bf16_matrix(a, "a")
     b, ldb = _bf16_matrix(b, "b")
     c, ldc = _bf16_matrix(c, "c")
@@ -395,13 +424,16 @@ def moe_dense_gemm_bf16(a, b, c, stream=None) -> None:
     n = b.shape[0]
     if b.shape[1] != k or tuple(c.shape) != (m, n):
         raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    wp, wb = _workspace(workspace)
     _check("moe_dense_gemm_bf16", load().moe_dense_gemm_bf16(
-        _p(a), lda, _p(b), ldb, _p(c), ldc, m, n, k, _stream(stream)))
+        _p(a), lda, _p(b), ldb, _p(c), ldc, m, n, k, wp, wb, _stream(stream)))
 
 
-def moe_dense_gate_up_swiglu_bf16(a, gate_w, up_w, act, limit: float, stream=None) -> None:
+def moe_dense_gate_up_swiglu_bf16(a, gate_w, up_w, act, limit: float, stream=None,
+                                  workspace=None) -> None:
     """``act = swiglu_clamp(bf16(a @ gate_w^T), bf16(a @ up_w^T))`` in one launch over
-    ``a [M, K]``, ``gate_w`` and ``up_w [I, K]`` (same strides) and ``act [M, I]``."""
+    ``a [M, K]``, ``gate_w`` and ``up_w [I, K]`` (same strides) and ``act [M, I]``. With
+    ``workspace`` it runs split over K with larger tiles."""
     a, lda = _bf16_matrix(a, "a")
     gate_w, ldw = _bf16_matrix(gate_w, "gate_w")
     up_w, ldw_up = _bf16_matrix(up_w, "up_w")
@@ -413,9 +445,10 @@ def moe_dense_gate_up_swiglu_bf16(a, gate_w, up_w, act, limit: float, stream=Non
     if gate_w.shape[1] != k or tuple(act.shape) != (m, inter):
         raise ValueError(f"shape mismatch: a {tuple(a.shape)}, gate_w {tuple(gate_w.shape)}, "
                          f"act {tuple(act.shape)}")
+    wp, wb = _workspace(workspace)
     _check("moe_dense_gate_up_swiglu_bf16", load().moe_dense_gate_up_swiglu_bf16(
         _p(a), lda, _p(gate_w), _p(up_w), ldw, _p(act), ld_act, m, inter, k, float(limit),
-        _stream(stream)))
+        wp, wb, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -424,9 +457,11 @@ class SharedExpert:
     """The shared expert: BF16 ``gate_w``, ``up_w`` ``[I, H]`` and ``down_w`` ``[H, I]``
     device tensors, plus its activation and output buffers for up to ``max_rows`` rows.
     Calling it runs moe_dense_gate_up_swiglu_bf16 then moe_dense_gemm_bf16 and returns the
-    ``[rows, H]`` output view (the combine's ``shared`` term)."""
+    ``[rows, H]`` output view (the combine's ``shared`` term). With ``split_k`` (default)
+    both run in their split-K form through one workspace (the two calls are ordered on
+    the stream, so they can share it)."""
 
-    def __init__(self, gate_w, up_w, down_w, max_rows: int):
+    def __init__(self, gate_w, up_w, down_w, max_rows: int, split_k: bool = True):
         import torch
 
         inter, hidden = gate_w.shape
@@ -436,14 +471,20 @@ class SharedExpert:
         self.inter, self.hidden = inter, hidden
         self.act = torch.empty(max_rows, inter, dtype=torch.bfloat16, device=gate_w.device)
         self.out = torch.empty(max_rows, hidden, dtype=torch.bfloat16, device=gate_w.device)
+        self.workspace = None
+        if split_k:  # the partial tiles grow with the rows: size for max_rows
+            nbytes = max(moe_dense_workspace_bytes(max_rows, inter, hidden, True),
+                         moe_dense_workspace_bytes(max_rows, hidden, inter, False), 1)
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=gate_w.device)
 
     def __call__(self, x, limit: float, stream=None):
         rows = x.shape[0]
         if rows > self.act.shape[0]:
             raise ValueError(f"{rows} rows exceed the {self.act.shape[0]} the buffers hold")
         act, out = self.act[:rows], self.out[:rows]
-        moe_dense_gate_up_swiglu_bf16(x, self.gate_w, self.up_w, act, limit, stream)
-        moe_dense_gemm_bf16(act, self.down_w, out, stream)
+        moe_dense_gate_up_swiglu_bf16(x, self.gate_w, self.up_w, act, limit, stream,
+                                      self.workspace)
+        moe_dense_gemm_bf16(act, self.down_w, out, stream, self.workspace)
         return out
 
 

@@ -27,6 +27,14 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
     }                                          \
   } while (0)
 
+#define MOE_REQUIRE_CODE(cond, code, ...)      \
+  do {                                         \
+    if (!(cond)) {                             \
+      ::moe::set_error(__VA_ARGS__);           \
+      return (code);                           \
+    }                                          \
+  } while (0)
+
 template <typename Tuple, size_t... I>
 void arg_pointers(Tuple &t, void **out, std::index_sequence<I...>) {
   ((out[I] = static_cast<void *>(&std::get<I>(t))), ...);

@@ -232,6 +232,276 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_kernel(
   }
 }
 
+// ------------------------------------------------------------------ split-K form
+//
+// With a workspace the GEMMs run split over K with larger tiles, in two launches. The
+// single-pass kernel above streams a 64-row tile of A and of B per block, so A is read
+// once per 64 output columns and B once per 64 rows; what bounds it is the bytes each CU
+// pulls through its L1 (misses in flight per CU, not HBM): about 400 MB for the shared
+// expert's gate/up at 256 rows. Tiles of 128 x 128 halve those bytes, and splitting K
+// S ways restores the block count (two blocks per CU at the shared expert's shapes).
+//   1. Partial GEMM. 4 waves as 2 x 2, each owning 64 A rows x 64 B rows (16 MFMA tiles,
+//      64 accumulator VGPRs). A and B tiles of 64 k are staged in LDS, double buffered,
+//      one barrier per step; the global loads run two steps ahead in registers. LDS rows
+//      are 128 bytes with the 16-byte pieces XOR-swizzled by the row (piece c of row r
+//      at c ^ (r & 7)), so the 16 rows x 4 pieces an MFMA operand read touches fall in
+//      distinct banks. Each block writes its FP32 partial tile to the workspace in
+//      fragment order (1 KB contiguous per wave and MFMA tile).
+//   2. Reduction. One thread per output fragment (4 columns of one row) sums the S
+//      partials in split order (deterministic), rounds to BF16 and, in the gate/up form,
+//      applies the SwiGLU to the BF16 gate and up sums; the whole chip reads the
+//      partials in parallel.
+//   The gate/up form puts 64 gate rows and the same 64 up rows in one B tile, so the gate
+//   and up sums of an output column sit in fragments f and f + 2048 of a tile. S depends
+//   on K only, so its G and U have the bits of the plain split-K GEMM's.
+constexpr int kLT = 128;                        // rows of A and of B per tile
+constexpr int kLK = 64;                         // k per LDS stage
+constexpr int kLRowBytes = kLK * 2;             // 128: staged rows are not padded
+constexpr int kLOperand = kLT * kLRowBytes;     // 16 KB: one operand's stage
+constexpr int kLStage = 2 * kLOperand;          // A and B
+constexpr int kLLds = 2 * kLStage;              // double buffered: 64 KB
+constexpr int kLPieces = kLT * (kLRowBytes / 16) / kThreads;  // 16-byte pieces per thread
+constexpr int kLFrags = kWaves * 16 * 64;       // f32x4 fragments per tile partial
+constexpr int kLMaxWays = 8;
+static_assert(kLPieces == 4, "four pieces of each operand per thread and step");
+
+// Split count for K: the largest power of two up to 8 that divides the 64-k steps evenly
+// and leaves each split at least 8 of them.
+int splitk_ways(int32_t k) {
+  const int steps = k / kLK;
+  for (int s = kLMaxWays; s > 1; s /= 2)
+    if (steps % s == 0 && steps / s >= 8) return s;
+  return 1;
+}
+
+struct SplitKShape {
+  int tiles_m, tiles_n, ways;
+  int64_t tiles, bytes;
+};
+
+SplitKShape splitk_shape(int32_t m, int32_t n, int32_t k, bool swiglu) {
+  SplitKShape sh;
+  sh.tiles_m = (m + kLT - 1) / kLT;
+  sh.tiles_n = (n + (swiglu ? kLT / 2 : kLT) - 1) / (swiglu ? kLT / 2 : kLT);
+  sh.ways = splitk_ways(k);
+  sh.tiles = static_cast<int64_t>(sh.tiles_m) * sh.tiles_n;
+  sh.bytes = sh.tiles * sh.ways * kLFrags * 16;
+  return sh;
+}
+
+// Phase 1: the partial tile of (row tile, column tile, split) for rows A and B rows over
+// the split's K range. Fused: B tile rows [0, 64) are gate rows n0 + r of b0 and [64, 128)
+// the same rows of b1 (up).
+template <bool kSwiglu>
+__global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
+    const uint16_t *__restrict__ a, int64_t lda, int32_t M, const uint16_t *__restrict__ b0,
+    const uint16_t *__restrict__ b1, int64_t ldb, int32_t N, int32_t K,
+    f32x4_t *__restrict__ partials) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int TN = gridDim.x, TM = gridDim.y, S = gridDim.z;
+
+  // Block -> (row tile, column tile, split). Blocks that read the same B rows (one column
+  // tile and split, every row tile) go to one XCD back to back.
+  int tm, tn, ks;
+  {
+    const int lin = (blockIdx.z * TM + blockIdx.y) * TN + blockIdx.x;
+    if (((TN * S) & 7) == 0) {
+      const int xcd = lin & 7, seq = lin >> 3;
+      tm = seq % TM;
+      const int g = (seq / TM) * 8 + xcd;
+      tn = g % TN;
+      ks = g / TN;
+    } else {
+      tn = blockIdx.x;
+      tm = blockIdx.y;
+      ks = blockIdx.z;
+    }
+  }
+  const int m0 = tm * kLT;
+  const int n0 = tn * (kSwiglu ? kLT / 2 : kLT);  // first B row (in b0 and b1 if fused)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, kb = lane >> 4;
+  const uint32_t arow = static_cast<uint32_t>(lda) * 2u, brow = static_cast<uint32_t>(ldb) * 2u;
+
+  // Resources from the tile's first row to its last valid row: rows past them read 0.
+  const __amdgpu_buffer_rsrc_t ar =
+      make_rsrc(a + static_cast<int64_t>(m0) * lda, static_cast<uint32_t>(min(kLT, M - m0)) * arow);
+  const int b_rows = kSwiglu ? kLT / 2 : kLT;
+  const uint32_t b_valid = static_cast<uint32_t>(min(b_rows, N - n0)) * brow;
+  const __amdgpu_buffer_rsrc_t br0 = make_rsrc(b0 + static_cast<int64_t>(n0) * ldb, b_valid);
+  const __amdgpu_buffer_rsrc_t br1 =
+      kSwiglu ? make_rsrc(b1 + static_cast<int64_t>(n0) * ldb, b_valid) : br0;
+
+  // This thread's staging pieces: piece p = tid + 256 i is row p / 8, 16-byte column p % 8.
+  uint32_t a_voff[kLPieces], b_voff[kLPieces], st_off[kLPieces];
+  bool b_up[kLPieces];
+#pragma unroll
+  for (int i = 0; i < kLPieces; ++i) {
+    const int p = tid + kThreads * i, row = p >> 3, col = p & 7;
+    a_voff[i] = static_cast<uint32_t>(row) * arow + 16u * col;
+    const int brow_i = kSwiglu ? (row & (kLT / 2 - 1)) : row;
+    b_up[i] = kSwiglu && row >= kLT / 2;
+    b_voff[i] = static_cast<uint32_t>(brow_i) * brow + 16u * col;
+    st_off[i] = static_cast<uint32_t>(row) * kLRowBytes + 16u * (col ^ (row & 7));
+  }
+
+  const int steps = K / kLK / S;
+  const int k_first = ks * steps;
+  struct Regs {
+    u32x4_t a[kLPieces], b[kLPieces];
+  };
+  const auto load_step = [&](Regs &r, int j) {  // j >= steps loads nothing
+    const uint32_t dead = j < steps ? 0u : kNoLoad;
+    const uint32_t soff = j < steps ? static_cast<uint32_t>(k_first + j) * kLRowBytes : 0u;
+#pragma unroll
+    for (int i = 0; i < kLPieces; ++i) {
+      r.a[i] = load16(ar, a_voff[i] | dead, soff);
+      r.b[i] = load16(b_up[i] ? br1 : br0, b_voff[i] | dead, soff);
+    }
+  };
+  const auto stage_step = [&](const Regs &r, int buf) {
+    uint8_t *sa = lds + buf * kLStage, *sb = sa + kLOperand;
+#pragma unroll
+    for (int i = 0; i < kLPieces; ++i) {
+      *reinterpret_cast<u32x4_t *>(sa + st_off[i]) = r.a[i];
+      *reinterpret_cast<u32x4_t *>(sb + st_off[i]) = r.b[i];
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const auto compute = [&](int buf) {
+    const uint8_t *sa = lds + buf * kLStage, *sb = sa + kLOperand;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int piece = 4 * h + kb;
+      bf16x8_t wf[4], xf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int rw = 64 * wn + 16 * t + r16, rx = 64 * wm + 16 * t + r16;
+        wf[t] = *reinterpret_cast<const bf16x8_t *>(sb + rw * kLRowBytes + 16 * (piece ^ (rw & 7)));
+        xf[t] = *reinterpret_cast<const bf16x8_t *>(sa + rx * kLRowBytes + 16 * (piece ^ (rx & 7)));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], xf[mt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+
+  // Steps j (LDS buffer j & 1) with the global loads two steps ahead in two register
+  // sets: set j & 1 is free once step j is staged, and takes step j + 2.
+  Regs r0, r1;
+  load_step(r0, 0);
+  load_step(r1, 1);
+  stage_step(r0, 0);
+  __syncthreads();
+  for (int j = 0; j < steps; j += 2) {
+    load_step(r0, j + 2);
+    compute(0);
+    if (j + 1 < steps) stage_step(r1, 1);
+    __syncthreads();
+    if (j + 1 >= steps) break;
+    load_step(r1, j + 3);
+    compute(1);
+    if (j + 2 < steps) stage_step(r0, 0);
+    __syncthreads();
+  }
+
+  // The partial tile in fragment order: [split][tile][wave][mt * 4 + nt][lane].
+  f32x4_t *mine = partials + (static_cast<int64_t>(ks) * TM * TN + tm * TN + tn) * kLFrags +
+                  wave * 1024;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) mine[(mt * 4 + nt) * 64 + lane] = acc[mt][nt];
+}
+
+// Phase 2: output fragment g of the tile grid (fragment f = g % kOutFrags of tile
+// g / kOutFrags). Fragment f: wave f / 1024, MFMA tile (f / 64) % 16, lane f % 64; its
+// element i is A row 64 (w & 1) + 16 mt + (lane & 15) and B row
+// 64 (w >> 1) + 16 nt + 4 (lane >> 4) + i.
+template <bool kSwiglu>
+__global__ __launch_bounds__(kThreads) void dense_reduce_kernel(
+    const f32x4_t *__restrict__ partials, int32_t tiles_n, int64_t n_tiles, int32_t ways,
+    uint16_t *__restrict__ c, int64_t ldc, int32_t M, int32_t N, float limit) {
+  constexpr int kOutFrags = kSwiglu ? kLFrags / 2 : kLFrags;  // fused: the gate fragments
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (g >= n_tiles * kOutFrags) return;
+  const int64_t tile = g / kOutFrags;
+  const int f = static_cast<int>(g - tile * kOutFrags);
+  const int tm = static_cast<int>(tile / tiles_n), tn = static_cast<int>(tile - static_cast<int64_t>(tm) * tiles_n);
+  const int w = f >> 10, q = (f >> 6) & 15, l = f & 63;
+  const int row = tm * kLT + 64 * (w & 1) + 16 * (q >> 2) + (l & 15);
+  const int col = tn * (kSwiglu ? kLT / 2 : kLT) + 64 * (w >> 1) + 16 * (q & 3) + 4 * (l >> 4);
+  if (row >= M || col >= N) return;
+  const int64_t stride = n_tiles * kLFrags;
+  const f32x4_t *p = partials + tile * kLFrags + f;
+  f32x4_t s = p[0];
+  for (int k = 1; k < ways; ++k) s += p[k * stride];
+  uint2 v;
+  if (kSwiglu) {
+    const f32x4_t *pu = p + kLFrags / 2;  // the up rows: waves 2, 3
+    f32x4_t su = pu[0];
+    for (int k = 1; k < ways; ++k) su += pu[k * stride];
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t gu = moe::pack_bf16x2(s[i], su[i]);
+      o[i] = moe::swiglu_clamp1(__uint_as_float(gu << 16), __uint_as_float(gu & 0xFFFF0000u),
+                                limit);
+    }
+    v.x = moe::pack_bf16x2(o[0], o[1]);
+    v.y = moe::pack_bf16x2(o[2], o[3]);
+  } else {
+    v.x = moe::pack_bf16x2(s[0], s[1]);
+    v.y = moe::pack_bf16x2(s[2], s[3]);
+  }
+  *reinterpret_cast<uint2 *>(c + static_cast<int64_t>(row) * ldc + col) = v;
+}
+
+template <bool kSwiglu>
+int launch_splitk(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0,
+                  const uint16_t *b1, int64_t ldb, uint16_t *c, int64_t ldc, int32_t n,
+                  int32_t k, float limit, void *workspace, int64_t workspace_bytes,
+                  void *stream) {
+  const char *name = kSwiglu ? "moe_dense_gate_up_swiglu_bf16" : "moe_dense_gemm_bf16";
+  const SplitKShape sh = splitk_shape(m, n, k, kSwiglu);
+  MOE_REQUIRE_CODE(workspace_bytes >= sh.bytes, MOE_ECAPACITY,
+                   "%s: the workspace holds %lld bytes, the split-K form needs %lld", name,
+                   static_cast<long long>(workspace_bytes), static_cast<long long>(sh.bytes));
+  MOE_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+              "%s: the workspace must be 256-byte aligned", name);
+  MOE_REQUIRE(sh.tiles_n <= 65535 && sh.tiles_m <= 65535,
+              "%s: too many tiles for the split-K form", name);
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(dense_partial_kernel<kSwiglu>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLLds);
+  if (attr_err != hipSuccess) {
+    moe::set_error("%s: cannot raise the LDS limit: %s", name, hipGetErrorString(attr_err));
+    return MOE_ELAUNCH;
+  }
+  f32x4_t *partials = static_cast<f32x4_t *>(workspace);
+  const dim3 grid(static_cast<unsigned>(sh.tiles_n), static_cast<unsigned>(sh.tiles_m),
+                  static_cast<unsigned>(sh.ways));
+  const int rc = moe::launch(name, dense_partial_kernel<kSwiglu>, grid, dim3(kThreads), kLLds,
+                             stream, a, lda, m, b0, b1, ldb, n, k, partials);
+  if (rc != MOE_OK) return rc;
+  const int64_t frags = sh.tiles * (kSwiglu ? kLFrags / 2 : kLFrags);
+  return moe::launch(name, dense_reduce_kernel<kSwiglu>,
+                     dim3(static_cast<unsigned>((frags + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, partials, sh.tiles_n, sh.tiles, sh.ways, c, ldc,
+                     m, n, limit);
+}
+
 struct Tile {
   int mt, nt;
 };
@@ -322,12 +592,21 @@ int check_dense_args(const char *name, const void *a, int64_t lda, const void *b
 
 }  // namespace
 
+extern "C" int64_t moe_dense_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t swiglu) {
+  if (m <= 0 || n <= 0 || k < 0) return 0;
+  return splitk_shape(m, n, k, swiglu != 0).bytes;
+}
+
 extern "C" int moe_dense_gemm_bf16(const uint16_t *a, int64_t lda, const uint16_t *b,
                                    int64_t ldb, uint16_t *c, int64_t ldc, int32_t m, int32_t n,
-                                   int32_t k, void *stream) {
+                                   int32_t k, void *workspace, int64_t workspace_bytes,
+                                   void *stream) {
   moe::clear_error();
   const int rc = check_dense_args("moe_dense_gemm_bf16", a, lda, b, b, ldb, c, ldc, m, n, k);
   if (rc != MOE_OK || m == 0 || n == 0) return rc;
+  if (workspace != nullptr)
+    return launch_splitk<false>(a, lda, m, b, b, ldb, c, ldc, n, k, 0.f, workspace,
+                                workspace_bytes, stream);
   return dispatch<false>(a, lda, m, b, b, ldb, c, ldc, n, k, 0.f, stream);
 }
 
@@ -335,6 +614,7 @@ extern "C" int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda,
                                              const uint16_t *gate_w, const uint16_t *up_w,
                                              int64_t ldw, uint16_t *act, int64_t ld_act,
                                              int32_t m, int32_t inter, int32_t k, float limit,
+                                             void *workspace, int64_t workspace_bytes,
                                              void *stream) {
   moe::clear_error();
   const int rc = check_dense_args("moe_dense_gate_up_swiglu_bf16", a, lda, gate_w, up_w, ldw, act,
@@ -344,5 +624,8 @@ extern "C" int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda,
               "moe_dense_gate_up_swiglu_bf16: limit must be positive (got %g)",
               static_cast<double>(limit));
   if (m == 0 || inter == 0) return MOE_OK;
+  if (workspace != nullptr)
+    return launch_splitk<true>(a, lda, m, gate_w, up_w, ldw, act, ld_act, inter, k, limit,
+                               workspace, workspace_bytes, stream);
   return dispatch<true>(a, lda, m, gate_w, up_w, ldw, act, ld_act, inter, k, limit, stream);
 }

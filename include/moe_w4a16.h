@@ -250,16 +250,37 @@ int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
  * pages' BF16 gemm (C[M, N] = A[M, K] B[N, K]^T) as forward_dense uses it for the shared
  * expert's down projection ([FWD] forward_dense).
  *
- *   a  bf16 [m, lda]   rows (tokens)
- *   b  bf16 [n, ldb]   weight rows, K contiguous
- *   c  bf16 [m, ldc]   output
+ *   a          bf16 [m, lda]   rows (tokens)
+ *   b          bf16 [n, ldb]   weight rows, K contiguous
+ *   c          bf16 [m, ldc]   output
+ *   workspace  NULL, or device memory of at least moe_dense_workspace_bytes(m, n, k, 0)
+ *              bytes, 256-byte aligned (no initial contents needed). With it the GEMM
+ *              runs split over K with 128 x 128 tiles in two launches (FP32 partial tiles
+ *              into the workspace, then a reduction in split order): fewer bytes through
+ *              each CU's cache at the prefill shapes. Calls that share a workspace must not
+ *              run concurrently (stream-ordered calls may share one). Without it, a single
+ *              pass with 64 x 64 tiles. The two forms sum in different orders: each is
+ *              deterministic, their bits differ.
  * Requirements (else MOE_EINVAL): m, n, k >= 0; n % 16 == 0; k % 64 == 0; lda >= k and
  * ldb >= k, multiples of 8 and at most 2^23; ldc >= n, a multiple of 4; c 8-byte aligned
- * and non-NULL when m * n > 0; a and b 16-byte aligned and non-NULL when also k > 0.
- * m == 0 or n == 0 enqueues nothing; k == 0 writes zeros (a and b are not read).
+ * and non-NULL when m * n > 0; a and b 16-byte aligned and non-NULL when also k > 0; a
+ * workspace 256-byte aligned. MOE_ECAPACITY if workspace_bytes is below what the
+ * split-K form needs. m == 0 or n == 0 enqueues nothing; k == 0 writes zeros (a and b
+ * are not read).
  */
 int moe_dense_gemm_bf16(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
-                        uint16_t *c, int64_t ldc, int32_t m, int32_t n, int32_t k, void *stream);
+                        uint16_t *c, int64_t ldc, int32_t m, int32_t n, int32_t k,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * moe_dense_workspace_bytes - host-side size query: the workspace bytes the split-K form
+ * of moe_dense_gemm_bf16 (swiglu = 0, n = output width) or of
+ * moe_dense_gate_up_swiglu_bf16 (swiglu = 1, n = inter) needs for these sizes: an FP32
+ * partial tile (128 x 128) per 128-row x 128-weight-row tile and K split (K splits 8, 4,
+ * 2 or 1 ways: the most that divide the 64-k steps evenly with at least 8 per split).
+ * Returns 0 when m <= 0, n <= 0 or k < 0. Enqueues nothing.
+ */
+int64_t moe_dense_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t swiglu);
 
 /*
  * moe_dense_gate_up_swiglu_bf16 - the gate and up projections of forward_dense and its
@@ -275,13 +296,18 @@ int moe_dense_gemm_bf16(const uint16_t *a, int64_t lda, const uint16_t *b, int64
  *   a               bf16 [m, lda]
  *   gate_w, up_w    bf16 [inter, ldw] each
  *   act             bf16 [m, ld_act]
- * Requirements (else MOE_EINVAL): limit > 0; inter % 16 == 0; the requirements of
- * moe_dense_gemm_bf16 with n = inter, b = gate_w and up_w, c = act.
+ *   workspace       as for moe_dense_gemm_bf16, sized by
+ *                   moe_dense_workspace_bytes(m, inter, k, 1). The bit identity above holds
+ *                   between calls of the same form (both with a workspace, or both
+ *                   without).
+ * Requirements (else MOE_EINVAL / MOE_ECAPACITY): limit > 0; inter % 16 == 0; the
+ * requirements of moe_dense_gemm_bf16 with n = inter, b = gate_w and up_w, c = act.
  */
 int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda, const uint16_t *gate_w,
                                   const uint16_t *up_w, int64_t ldw, uint16_t *act,
                                   int64_t ld_act, int32_t m, int32_t inter, int32_t k,
-                                  float limit, void *stream);
+                                  float limit, void *workspace, int64_t workspace_bytes,
+                                  void *stream);
 
 /*
  * moe_w4a16_dequant_bf16 - diagnostic: write the BF16 weight operand the grouped GEMM

@@ -8,6 +8,9 @@ against the oracle's dense_mlp.
   oracle's activation within the gate, including clamped values.
 - The shared expert (both calls) at the layer workloads' full sizes, and the routed
   layer with the shared expert in its combine, against the oracle.
+- The split-K form (with a workspace) against the oracle, repeated calls give the same
+  bits, one workspace serves calls of two shapes in turn, and its gate/up form gives the
+  bits of the two plain split-K GEMMs followed by swiglu_clamp.
 - Nothing outside the output rows and columns is written; bad arguments raise.
 
 Tolerance: the parity gate, max |gpu - oracle| / max |oracle| <= 5e-3 against the FP64
@@ -105,6 +108,33 @@ def test_dense_gemm_strided_views_and_k_zero(hip):
     hip.moe_dense_gemm_bf16(a_full[:, :k], b_full[:0, :k], c[:, :0])
 
 
+def _check_against_oracle(a_bits, g_bits, u_bits, gate, up, act, limit, w_scale):
+    """The gate/up form against the oracle's dense_mlp. G and U (the GEMM outputs the fused
+    form reproduces bit for bit) at the parity gate; the activation at the gate when the
+    weights are unscaled. With scaled weights most outputs sit at the clamp and reach
+    ~49: there one BF16 rounding flip of U (the pages' BF16 buffer; FP32 and FP64 sums
+    round to neighbours now and then) moves an output by silu(7) * ulp(U) ~ 0.22, up to
+    one BF16 ulp of the largest output (2^-7 of it, above the 5e-3 gate), so the
+    activation is checked elementwise within the bound from one such flip of G and of U
+    plus the output rounding."""
+    zeros = np.zeros((8, g_bits.shape[0]))
+    _, mid = moe.dense_mlp(_bf16(a_bits), _bf16(g_bits), _bf16(u_bits), zeros, limit, "bf16w")
+    assert rel_err(f64(gate), mid["gate"]) <= GATE
+    assert rel_err(f64(up), mid["up"]) <= GATE
+    got = f64(act)
+    if w_scale <= 4:
+        assert rel_err(got, mid["act"]) <= GATE
+    else:
+        assert np.mean(np.abs(mid["gate"]) > limit) > 0.05  # the clamp was exercised
+        ulp = lambda v: 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126))) - 7)
+        silu_max = limit / (1.0 + np.exp(-limit))
+        # silu' <= 1.1 everywhere; |clamped U| <= limit; FP32 swiglu: a few 2^-24
+        bound = 0.5 * ulp(mid["act"]) + silu_max * ulp(np.clip(mid["up"], -limit, limit)) \
+            + 1.1 * limit * ulp(np.minimum(mid["gate"], limit)) + 1e-6 * np.abs(mid["act"])
+        assert np.all(np.abs(got - mid["act"]) <= bound)
+        assert rel_err(got, mid["act"]) <= 2.0 ** -7 + 2.0 ** -9
+
+
 # (m, inter, k, weight scale): every tile shape of the gate/up form on a 256-CU part;
 # scales 6 and 8 push many gate and up values past the clamp.
 @pytest.mark.parametrize("m,inter,k,w_scale", [
@@ -130,12 +160,102 @@ def test_gate_up_swiglu_bits_and_oracle(hip, m, inter, k, w_scale):
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits_host(act), bf16_bits_host(ref_act))
     assert _untouched(buf, m, inter)
-    # against the oracle (dense_mlp's activation stage)
-    zeros = np.zeros((8, inter))
-    _, mid = moe.dense_mlp(_bf16(a_bits), _bf16(g_bits), _bf16(u_bits), zeros, limit, "bf16w")
+    _check_against_oracle(a_bits, g_bits, u_bits, gate, up, act, limit, w_scale)
+
+
+# Split-K form (with a workspace): (m, n, k) with K split 4, 2 and 1 ways, ragged row and
+# column tiles, a column-tile count that does not divide by 8, the shared expert's shapes.
+SPLITK_SHAPES = [
+    (1, 16, 64), (17, 80, 192), (130, 272, 1024), (100, 2048, 768), (300, 4096, 512),
+    (256, 2048, 6144), (256, 6144, 2048), (33, 48, 4096),
+]
+
+
+@pytest.mark.parametrize("m,n,k", SPLITK_SHAPES)
+def test_dense_gemm_split_k_vs_oracle(hip, m, n, k):
+    a_bits, b_bits = _operands(m * 5 + n + k, m, n, k)
+    a, b = bf16_dev(a_bits), bf16_dev(b_bits)
+    ws = hip.dense_workspace(m, n, k)
+    buf, c = _padded(m, n, 3, 16)
+    hip.moe_dense_gemm_bf16(a, b, c, workspace=ws)
+    torch.cuda.synchronize()
+    got = f64(c)
+    ref = _gemm_ref(a_bits, b_bits)
+    assert rel_err(got, ref) <= GATE
+    assert np.mean(got == ref) > 0.97
+    assert _untouched(buf, m, n)
+    # deterministic: a second call over a workspace full of the first call's partials
+    first = bf16_bits_host(c).copy()
+    hip.moe_dense_gemm_bf16(a, b, c, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(c), first)
+
+
+def test_dense_split_k_workspace_shared_by_two_shapes(hip):
+    """One workspace for the gate/up form and the plain GEMM of another shape, in turns
+    (stream-ordered), three times: the same bits each time and the oracle's values."""
+    m, inter, k = 200, 1024, 1536
+    a_bits, g_bits = _operands(41, m, inter, k)
+    _, u_bits = _operands(42, m, inter, k)
+    _, d_bits = _operands(43, m, k, inter)
+    a, g, u, d = (bf16_dev(x) for x in (a_bits, g_bits, u_bits, d_bits))
+    ws = torch.zeros(max(hip.moe_dense_workspace_bytes(m, inter, k, True),
+                         hip.moe_dense_workspace_bytes(m, k, inter, False)),
+                     dtype=torch.uint8, device="cuda")
+    act = torch.empty((m, inter), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    runs = []
+    for _ in range(3):
+        hip.moe_dense_gate_up_swiglu_bf16(a, g, u, act, 7.0, workspace=ws)
+        hip.moe_dense_gemm_bf16(act, d, out, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append((bf16_bits_host(act).copy(), bf16_bits_host(out).copy()))
+    for r in runs[1:]:
+        assert np.array_equal(r[0], runs[0][0]) and np.array_equal(r[1], runs[0][1])
+    ref, mid = moe.dense_mlp(_bf16(a_bits), _bf16(g_bits), _bf16(u_bits), _bf16(d_bits), 7.0,
+                             "bf16w")
     assert rel_err(f64(act), mid["act"]) <= GATE
-    if w_scale > 4:  # the clamp was exercised
-        assert np.mean(np.abs(mid["gate"]) > limit) > 0.05
+    assert rel_err(f64(out), ref) <= GATE
+
+
+@pytest.mark.parametrize("m,inter,k,w_scale", [
+    (33, 48, 192, 6.0), (19, 16, 1024, 6.0), (100, 768, 2048, 8.0), (256, 2048, 6144, 1.0),
+])
+def test_gate_up_swiglu_split_k_bits_and_oracle(hip, m, inter, k, w_scale):
+    a_bits, g_bits = _operands(m + inter + k + 1, m, inter, k, w_scale)
+    _, u_bits = _operands(m + inter + k + 2, m, inter, k, w_scale)
+    a, g, u = bf16_dev(a_bits), bf16_dev(g_bits), bf16_dev(u_bits)
+    limit = 7.0
+    ws = hip.dense_workspace(m, inter, k, swiglu=True)
+    buf, act = _padded(m, inter, 2, 8)
+    hip.moe_dense_gate_up_swiglu_bf16(a, g, u, act, limit, workspace=ws)
+    # the two plain split-K GEMMs (one workspace, stream-ordered), then swiglu_clamp
+    ws_plain = hip.dense_workspace(m, inter, k)
+    gate = torch.empty((m, inter), dtype=torch.bfloat16, device="cuda")
+    up = torch.empty_like(gate)
+    ref_act = torch.empty_like(gate)
+    hip.moe_dense_gemm_bf16(a, g, gate, workspace=ws_plain)
+    hip.moe_dense_gemm_bf16(a, u, up, workspace=ws_plain)
+    hip.swiglu_clamp(gate, up, ref_act, limit)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(act), bf16_bits_host(ref_act))
+    assert _untouched(buf, m, inter)
+    _check_against_oracle(a_bits, g_bits, u_bits, gate, up, act, limit, w_scale)
+
+
+def test_dense_split_k_workspace_errors(hip):
+    m, n, k = 64, 128, 1024
+    a = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((n, k), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((m, n), dtype=torch.bfloat16, device="cuda")
+    need = hip.moe_dense_workspace_bytes(m, n, k)
+    small = torch.zeros(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hip.MoeError) as e:  # MOE_ECAPACITY
+        hip.moe_dense_gemm_bf16(a, b, c, workspace=small)
+    assert e.value.status == 2
+    big = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hip.MoeError):  # not 256-byte aligned
+        hip.moe_dense_gemm_bf16(a, b, c, workspace=big[16:16 + need])
 
 
 def _shared_on_device(hip, w, scale=1.0):

@@ -90,3 +90,28 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.moe_combine(_bad(), 16, 4, _bad(), _bad(), n, 0, _bad(), 16, 4, 16, 0, n) == 1
     # dequant: k not a multiple of 32
     assert lib.moe_w4a16_dequant_bf16(_bad(), _bad(), 1.0, _bad(), 4, 48, n) == 1
+    # dense split-K: a workspace below the size query (capacity), one not 256-byte aligned
+    need = lib.moe_dense_workspace_bytes(64, 128, 1024, 0)
+    assert lib.moe_dense_gemm_bf16(_bad(), 1024, _bad(), 1024, _bad(), 128, 64, 128, 1024,
+                                   _bad(), need - 1, n) == 2
+    assert lib.moe_dense_gemm_bf16(_bad(), 1024, _bad(), 1024, _bad(), 128, 64, 128, 1024,
+                                   _bad(0x1010), need, n) == 1
+
+
+def _splitk_bytes(m, n, k, swiglu):
+    """The split-K workspace size from its definition: 128 x 128 FP32 per tile of 128 rows
+    x 128 weight rows (64 output columns in the gate/up form) and K split; K splits 8, 4
+    or 2 ways (the most with every split at least 8 steps of 64 k and the steps dividing
+    evenly), else 1."""
+    steps = k // 64
+    ways = next((s for s in (8, 4, 2) if steps % s == 0 and steps // s >= 8), 1)
+    tiles = -(-m // 128) * -(-n // (64 if swiglu else 128))
+    return tiles * ways * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("m,n,k,swiglu", [
+    (256, 2048, 6144, 1), (256, 6144, 2048, 0), (1, 16, 64, 0), (130, 272, 1024, 0),
+    (300, 4096, 512, 1), (8, 48, 0, 0), (4096, 16, 2560, 1)])
+def test_dense_workspace_size_query(lib, m, n, k, swiglu):
+    assert lib.moe_dense_workspace_bytes(m, n, k, swiglu) == _splitk_bytes(m, n, k, swiglu)
+    assert lib.moe_dense_workspace_bytes(0, n, k, swiglu) == 0
