@@ -239,7 +239,8 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_kernel(
 // once per 64 output columns and B once per 64 rows; what bounds it is the bytes each CU
 // pulls through its L1 (misses in flight per CU, not HBM): about 400 MB for the shared
 // expert's gate/up at 256 rows. Tiles of 128 x 128 halve those bytes, and splitting K
-// S ways restores the block count (two blocks per CU at the shared expert's shapes).
+// S ways restores the block count (one to two blocks per CU at the shared expert's
+// shapes).
 //   1. Partial GEMM. 4 waves as 2 x 2, each owning 64 A rows x 64 B rows (16 MFMA tiles,
 //      64 accumulator VGPRs). A and B tiles of 64 k are staged in LDS, double buffered,
 //      one barrier per step; the global loads run two steps ahead in registers. LDS rows
@@ -262,11 +263,12 @@ constexpr int kLStage = 2 * kLOperand;          // A and B
 constexpr int kLLds = 2 * kLStage;              // double buffered: 64 KB
 constexpr int kLPieces = kLT * (kLRowBytes / 16) / kThreads;  // 16-byte pieces per thread
 constexpr int kLFrags = kWaves * 16 * 64;       // f32x4 fragments per tile partial
-constexpr int kLMaxWays = 8;
+constexpr int kLMaxWays = 4;
 static_assert(kLPieces == 4, "four pieces of each operand per thread and step");
 
-// Split count for K: the largest power of two up to 8 that divides the 64-k steps evenly
-// and leaves each split at least 8 of them.
+// Split count for K: the largest power of two up to 4 that divides the 64-k steps evenly
+// and leaves each split at least 8 of them. (At the shared expert's gate/up, 8 ways gave
+// two blocks per CU but twice the partial-tile bytes: no faster; 16 ways was slower.)
 int splitk_ways(int32_t k) {
   const int steps = k / kLK;
   for (int s = kLMaxWays; s > 1; s /= 2)

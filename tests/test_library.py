@@ -100,11 +100,11 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
 
 def _splitk_bytes(m, n, k, swiglu):
     """The split-K workspace size from its definition: 128 x 128 FP32 per tile of 128 rows
-    x 128 weight rows (64 output columns in the gate/up form) and K split; K splits 8, 4
-    or 2 ways (the most with every split at least 8 steps of 64 k and the steps dividing
+    x 128 weight rows (64 output columns in the gate/up form) and K split; K splits 4 or
+    2 ways (the most with every split at least 8 steps of 64 k and the steps dividing
     evenly), else 1."""
     steps = k // 64
-    ways = next((s for s in (8, 4, 2) if steps % s == 0 and steps // s >= 8), 1)
+    ways = next((s for s in (4, 2) if steps % s == 0 and steps // s >= 8), 1)
     tiles = -(-m // 128) * -(-n // (64 if swiglu else 128))
     return tiles * ways * 128 * 128 * 4
 
