@@ -266,13 +266,17 @@ constexpr int kLFrags = kWaves * 16 * 64;       // f32x4 fragments per tile part
 constexpr int kLMaxWays = 4;
 static_assert(kLPieces == 4, "four pieces of each operand per thread and step");
 
-// Split count for K: the largest power of two up to 4 that divides the 64-k steps evenly
-// and leaves each split at least 8 of them. (At the shared expert's gate/up, 8 ways gave
-// two blocks per CU but twice the partial-tile bytes: no faster; 16 ways was slower.)
-int splitk_ways(int32_t k) {
+// Split count for K: the largest power of two up to 4, and up to 8 / (row tiles), that
+// divides the 64-k steps evenly and leaves each split at least 8 of them. (At the shared
+// expert's gate/up, 8 ways gave two blocks per CU but twice the partial-tile bytes: no
+// faster; 16 ways was slower. With many row tiles the tiles alone fill the chip and each
+// split only adds partial-tile bytes.) It depends on m and k, not n, so the gate/up form
+// and the plain GEMM of the same rows split alike.
+int splitk_ways(int32_t m, int32_t k) {
   const int steps = k / kLK;
+  const int row_tiles = (m + kLT - 1) / kLT;
   for (int s = kLMaxWays; s > 1; s /= 2)
-    if (steps % s == 0 && steps / s >= 8) return s;
+    if (s * row_tiles <= 8 && steps % s == 0 && steps / s >= 8) return s;
   return 1;
 }
 
@@ -285,7 +289,7 @@ SplitKShape splitk_shape(int32_t m, int32_t n, int32_t k, bool swiglu) {
   SplitKShape sh;
   sh.tiles_m = (m + kLT - 1) / kLT;
   sh.tiles_n = (n + (swiglu ? kLT / 2 : kLT) - 1) / (swiglu ? kLT / 2 : kLT);
-  sh.ways = splitk_ways(k);
+  sh.ways = splitk_ways(m, k);
   sh.tiles = static_cast<int64_t>(sh.tiles_m) * sh.tiles_n;
   sh.bytes = sh.tiles * sh.ways * kLFrags * 16;
   return sh;
