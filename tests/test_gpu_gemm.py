@@ -244,6 +244,27 @@ def test_no_gather_and_row_cut_off(hip):
     assert rel_err(got[:35], ref[:35]) <= GATE
 
 
+def test_many_experts_without_room_for_overflow_rows(hip):
+    """65500 experts: the grid rows for overflow chunks would pass the 65535 limit, so the
+    launch falls back to one block row per expert taking all of its rows (here 150 rows,
+    three passes past 64). Three live experts at the ends and the middle of the table."""
+    rng = np.random.default_rng(9)
+    n, k, e_n = 32, 256, 65500
+    counts = np.zeros(e_n, np.int64)
+    live = {0: 150, 30000: 5, e_n - 1: 70}
+    for e, c in live.items():
+        counts[e] = c
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    experts = [None] * e_n
+    for e in live:
+        experts[e] = wl.random_nvfp4(rng, n, k)
+    s2 = rng.uniform(0.5, 2, e_n).astype(np.float32)
+    x_bits = wl.bf16_normal(rng, (offsets[-1], k))
+    got = _gemm(hip, x_bits, experts, s2, offsets, n, k)
+    ref = _oracle(x_bits, experts, s2, offsets, n, None, "bf16w")
+    _check_gemm(got, ref, _acc_bound(x_bits, experts, s2, offsets, None, k))
+
+
 def test_row_cut_off_inside_an_overflow_chunk(hip):
     """Experts of 150 and 100 rows (past 64: more blocks per expert), max_rows cutting the
     second expert's rows inside its first chunk and the first expert's third chunk whole."""
