@@ -283,7 +283,7 @@ def time_decode_leg(hip, torch, steps):
         "union": [
             ("moe_row_union", lambda: hip.moe_row_union(ids, w.num_experts, dws.u_eid, u_slot,
                                                         dws.slot_perm, dws.counters)),
-            ("zero_expert_out", lambda: dws.expert_out[:s].zero_()),
+            ("zero_expert_out", lambda: hip.moe_zero_rows(dws.expert_out[:s])),
             ("gemv_union_gate_up_swiglu", lambda: hip.moe_w4a16_gemv_union_swiglu(
                 x, gt, dws.u_eid, u_slot, dws.act, w.limit, rows, top_k)),
             ("gemv_union_down", lambda: hip.moe_w4a16_gemv_union(
@@ -295,7 +295,7 @@ def time_decode_leg(hip, torch, steps):
                                                 ws.sorted_expert_ids, ws.expert_offsets,
                                                 ws.token_to_perm, ws.active_experts,
                                                 ws.counters)),
-            ("zero_expert_out", lambda: ws.expert_out[:s].zero_()),
+            ("zero_expert_out", lambda: hip.moe_zero_rows(ws.expert_out[:s])),
             ("grouped_gemm_gate_up_swiglu", lambda: hip.moe_w4a16_grouped_gemm_swiglu(
                 x, gt, ws.expert_offsets, ws.act, w.limit, ws.sorted_token_ids, max_rows=s)),
             ("grouped_gemm_down", lambda: hip.moe_w4a16_grouped_gemm(
@@ -422,7 +422,7 @@ def main():
                       ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
 
     def st_zero(x, ids, wts):  # null down entries: their rows must read as zero in the combine
-        ws.expert_out[:s].zero_()
+        hip.moe_zero_rows(ws.expert_out[:s], stream)
 
     def st_gate_up(x, ids, wts):
         hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
@@ -453,7 +453,7 @@ def main():
                           dws.counters)
 
     def st_union_zero(x, ids, wts):
-        dws.expert_out[:s].zero_()
+        hip.moe_zero_rows(dws.expert_out[:s], stream)
 
     def st_union_gate_up(x, ids, wts):
         hip.moe_w4a16_gemv_union_swiglu(x, gt, dws.u_eid, dws.u_slot[:s * rows], dws.act,

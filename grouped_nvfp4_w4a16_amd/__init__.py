@@ -34,7 +34,7 @@ __all__ = [
     "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "moe_router_topk",
     "moe_layer_from_logits", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
     "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "moe_dense_workspace_bytes",
-    "dense_workspace", "SharedExpert",
+    "dense_workspace", "SharedExpert", "moe_zero_rows",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
     "moe_layer_decode", "UNION_MAX_ROWS",
 ]
@@ -46,7 +46,8 @@ EXPORTS = (
     "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
-    "moe_dense_workspace_bytes", "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu",
+    "moe_dense_workspace_bytes", "moe_zero_rows", "moe_row_union", "moe_w4a16_gemv_union",
+    "moe_w4a16_gemv_union_swiglu",
 )
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
@@ -82,6 +83,7 @@ _SIGNATURES = {
         [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _i64, _vp],
         ctypes.c_int),
     "moe_dense_workspace_bytes": ([_i32, _i32, _i32, _i32], _i64),
+    "moe_zero_rows": ([_vp, _i64, _i32, _i32, _vp], ctypes.c_int),
     "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_w4a16_gemv_union": (
         [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32,
@@ -388,6 +390,13 @@ def moe_w4a16_dequant_bf16(packed, scales, scale2: float, out, stream=None) -> N
         _p(packed), _p(scales), float(scale2), _p(out), n, k, _stream(stream)))
 
 
+def moe_zero_rows(c, stream=None) -> None:
+    """Zero a BF16 ``[rows, cols]`` row-major view (the zero-first step on expert_out)."""
+    c, ldc = _bf16_matrix(c, "c")
+    _check("moe_zero_rows", load().moe_zero_rows(_p(c), ldc, c.shape[0], c.shape[1],
+                                                 _stream(stream)))
+
+
 def moe_dense_workspace_bytes(m: int, n: int, k: int, swiglu: bool = False) -> int:
     """Bytes of the split-K workspace of moe_dense_gemm_bf16 (``n`` = output width) or of
     moe_dense_gate_up_swiglu_bf16 (``swiglu=True``, ``n`` = inter) at these sizes."""
@@ -580,7 +589,7 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     moe_align(topk_ids, gate_up.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
               ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters, stream)
     if not all(down.present):
-        ws.expert_out[:s].zero_()
+        moe_zero_rows(ws.expert_out[:s], stream)
     mi = moe_intermediate
     if fused:
         moe_w4a16_grouped_gemm_swiglu(x, gate_up, ws.expert_offsets, ws.act, limit,
@@ -651,7 +660,7 @@ def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: Expe
     moe_row_union(topk_ids, gate_up.num_experts, ws.u_eid, u_slot, ws.slot_perm, ws.counters,
                   stream)
     if not all(down.present):
-        ws.expert_out[:t].zero_()
+        moe_zero_rows(ws.expert_out[:t], stream)
     mi = moe_intermediate
     if fused:
         moe_w4a16_gemv_union_swiglu(x, gate_up, ws.u_eid, u_slot, ws.act, limit, rows, top_k,

@@ -1,9 +1,12 @@
-// swiglu_clamp and moe_combine: the bandwidth-bound steps around the grouped GEMMs.
+// swiglu_clamp, moe_combine and moe_zero_rows: the bandwidth-bound steps around the
+// grouped GEMMs.
 //
 // swiglu_clamp follows swiglu_rows on the 2026-09-25 glm5next_mlp forward.rs page:
 // out = silu(min(gate, limit)) * clamp(up, -limit, limit). moe_combine follows that
 // page's forward_moe: one launch for all rows, each slot's expert-sorted row found
 // through token_to_perm, weighted by its top-k weight, plus the shared-expert output.
+// moe_zero_rows is that forward_moe's zero-first step on expert_out, so that the rows of
+// remote experts (never written by the down GEMM) add zero in the combine.
 //
 // Both kernels move 16 bytes (8 BF16) per thread per operand with 128-bit loads and
 // stores and compute in FP32; a block of 256 threads covers 2048 columns of one row.
@@ -77,7 +80,34 @@ __global__ __launch_bounds__(kThreads) void moe_combine_kernel(
   *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(acc);
 }
 
+// Zeroes rows x cols of a BF16 matrix: one 16-byte store per thread.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint16_t *__restrict__ c,
+                                                             int64_t ldc, int64_t units_per_row,
+                                                             int64_t units) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int64_t row = u / units_per_row, col8 = u - row * units_per_row;
+  *reinterpret_cast<uint4 *>(c + row * ldc + col8 * 8) = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace
+
+extern "C" int moe_zero_rows(uint16_t *c, int64_t ldc, int32_t rows, int32_t cols,
+                             void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(rows >= 0 && cols >= 0 && cols % 8 == 0,
+              "zero_rows: need rows >= 0 and cols >= 0 a multiple of 8 (rows=%d cols=%d)", rows,
+              cols);
+  MOE_REQUIRE(ldc >= cols && ldc % 8 == 0,
+              "zero_rows: ldc must be >= cols and a multiple of 8");
+  if (rows == 0 || cols == 0) return MOE_OK;
+  MOE_REQUIRE(c != nullptr && moe::aligned16(c), "zero_rows: c must be non-NULL and 16-byte aligned");
+  const int64_t per_row = cols / 8, units = per_row * rows;
+  MOE_REQUIRE((units + kThreads - 1) / kThreads <= INT32_MAX, "zero_rows: matrix too large");
+  return moe::launch("moe_zero_rows", zero_rows_kernel,
+                     dim3(static_cast<unsigned>((units + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, c, ldc, per_row, units);
+}
 
 extern "C" int swiglu_clamp(const uint16_t *gate, const uint16_t *up, int64_t ld_in,
                             uint16_t *out, int64_t ld_out, int32_t rows, int32_t n, float limit,

@@ -7,6 +7,7 @@
  *   moe_w4a16_grouped_gemm  one launch over all experts: gathered BF16 rows x NVFP4 weights
  *   swiglu_clamp            silu(min(gate, L)) * clamp(up, -L, L)
  *   moe_combine             top-k weighted sum of the expert-sorted rows per token
+ *   moe_zero_rows           the zero-first step on expert_out (absent experts add zero)
  *   moe_w4a16_grouped_gemm_swiglu  the gate_up grouped GEMM with swiglu_clamp fused into
  *                           its epilogue (same bits as the two calls in sequence)
  *   moe_router_topk         router logits -> top-k expert ids and weights (feeds moe_align
@@ -244,6 +245,18 @@ int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
                 const int32_t *token_to_perm, const float *topk_weights,
                 const uint16_t *shared, int64_t ld_s, uint16_t *out, int64_t ld_out,
                 int32_t rows, int32_t hidden, int32_t top_k, void *stream);
+
+/*
+ * moe_zero_rows - c[r, j] = 0 for r < rows, j < cols: forward_moe's zero-first step on
+ * expert_out ([FWD] forward_moe), so that the rows of experts absent from the table
+ * (never written by the down GEMM) add zero in moe_combine. A kernel, not a memset, so
+ * that it may sit in a captured graph.
+ *
+ *   c  bf16 [rows, ldc]
+ * Requirements (else MOE_EINVAL): rows >= 0; cols >= 0 and cols % 8 == 0; ldc >= cols and
+ * a multiple of 8; c non-NULL and 16-byte aligned when rows * cols > 0.
+ */
+int moe_zero_rows(uint16_t *c, int64_t ldc, int32_t rows, int32_t cols, void *stream);
 
 /*
  * moe_dense_gemm_bf16 - c[m, n] = bf16( sum_k a[m, k] * b[n, k] ), FP32 accumulation: the

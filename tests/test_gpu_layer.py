@@ -141,6 +141,23 @@ def test_small_m_half_null_vs_oracle(hip):
             assert np.all(got[r] == 0.0)
 
 
+def test_zero_rows_strided_view(hip):
+    """moe_zero_rows writes zeros into exactly the rows x cols of a strided view."""
+    buf = torch.full((40, 200), 3.0, dtype=torch.bfloat16, device="cuda")
+    view = buf[3:37, 8:8 + 176]
+    hip.moe_zero_rows(view)
+    torch.cuda.synchronize()
+    got = buf.float().cpu().numpy()
+    mask = np.zeros(got.shape, bool)
+    mask[3:37, 8:184] = True
+    assert np.all(got[mask] == 0.0) and np.all(got[~mask] == 3.0)
+    hip.moe_zero_rows(buf[:0])  # nothing to do
+    with pytest.raises(hip.MoeError):  # cols not a multiple of 8
+        hip.moe_zero_rows(buf[:4, :12])
+    with pytest.raises(hip.MoeError):  # misaligned by one element
+        hip.moe_zero_rows(buf[:4, 1:17])
+
+
 def test_expert_parallel_halves_sum_to_full(hip):
     """Complementary null halves of the table give partial outputs that sum to the full
     output (the per-GPU partial sums an all-reduce would add)."""
