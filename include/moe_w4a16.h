@@ -40,7 +40,10 @@
  *     or reads device memory from the host ([FPG] "Buffer discipline": nothing on the
  *     path allocates). There is no host<->device traffic inside any call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Each call
- *     only enqueues work on it and returns.
+ *     only enqueues kernels on it and returns (no allocation, no synchronisation, no
+ *     memset or copy nodes), so calls may be captured into a HIP graph and replayed; the
+ *     first call of some entry points sets a kernel attribute once per process, so make
+ *     one call of each outside the capture first.
  *   - BF16 tensors are passed as uint16_t bit patterns. Matrices are row-major with the
  *     given leading dimension in ELEMENTS.
  *   - Return value: 0 (MOE_OK) or a moe_status code. On error nothing was enqueued and
