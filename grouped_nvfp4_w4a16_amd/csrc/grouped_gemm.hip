@@ -174,15 +174,23 @@ __device__ int2 find_overflow_chunk(const int32_t *__restrict__ offsets, int num
 // kSwiglu = false: c[s, n] for the N weight rows.
 // kSwiglu = true: N = 2 mi; c[s, j] = swiglu(gate sum of row j, up sum of row mi + j) for
 // j < mi (c is the activation buffer, ldc its leading dimension).
-template <bool kSwiglu>
-__global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
+//
+// kMT: 16-row MFMA tiles of sorted rows per pass (1 or 2). With 2, each decoded weight
+// feeds two tiles: half the decode work and weight re-reads for experts with more than
+// 16 rows, at two blocks per CU (registers and LDS).
+template <bool kSwiglu, int kMT>
+__global__ __launch_bounds__(kThreads, kMT == 1 ? 3 : 2) void grouped_gemm_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t a_rows,
     const int32_t *__restrict__ gather, const uint64_t *__restrict__ packed_ptrs,
     const uint64_t *__restrict__ scale_ptrs, const float *__restrict__ scale2s,
     const int32_t *__restrict__ offsets, int32_t num_experts, int32_t chunk_rows,
     uint16_t *__restrict__ c, int64_t ldc, int32_t max_rows, int32_t N, int32_t K,
     float limit) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kLdsBufBytes];
+  constexpr int kPassM = kBlockM * kMT;                      // sorted rows per pass
+  constexpr int kXBufBytes = kPassM * kLdsRowBytes;
+  constexpr int kXP = kPassM * kPiecesPerRow / kThreads;       // pieces per thread per step
+  static_assert(kPassM * kPiecesPerRow == kXP * kThreads, "whole activation pieces");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kXBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
 
@@ -292,16 +300,16 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
   // This lane's scale dword of tile 0 within a staged block (tile 1: + kScaleHalfLds).
   const int s_read = (16 * wave + r16) * kScaleRowBytes + 4 * kb;
 
-  for (int m0 = lo; m0 < hi; m0 += kBlockM) {
-    const int m_cnt = min(kBlockM, hi - m0);
+  for (int m0 = lo; m0 < hi; m0 += kPassM) {
+    const int m_cnt = min(kPassM, hi - m0);
     // Activation staging: thread -> (row of the pass, 16-byte piece of a step) for rows
     // tid / 32 and 8 + tid / 32. Rows past the pass and out-of-range gather indices read
     // zeros (offset past the end). The gather indices are loaded first, the step's
     // weights and scales next, so that only the gather is waited for before the
     // activation loads can be addressed.
-    int g_row[kXPieces], piece_col[kXPieces], lds_off[kXPieces];
+    int g_row[kXP], piece_col[kXP], lds_off[kXP];
 #pragma unroll
-    for (int p = 0; p < kXPieces; ++p) {
+    for (int p = 0; p < kXP; ++p) {
       const int piece = tid + p * kThreads;
       const int piece_row = piece / kPiecesPerRow;
       piece_col[p] = piece % kPiecesPerRow;
@@ -314,9 +322,11 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       g_row[p] = g;
     }
 
-    f32x4_t acc[kTiles];
+    f32x4_t acc[kTiles][kMT];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     WeightRegs w0, w1;
     load_weights(w0, w_rsrc, w_voff, 0, n_steps);
     // Scales of steps 0-3 to LDS now; steps 4-7 wait in sc_keep.
@@ -330,9 +340,9 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     // barrier below. Later passes write the same values again (every read of the previous
     // pass is behind its last barrier), which costs less than a branch around it.
     build_code_table_lut(lut, tid, scale2);
-    uint32_t x_voff[kXPieces];
+    uint32_t x_voff[kXP];
 #pragma unroll
-    for (int p = 0; p < kXPieces; ++p) {
+    for (int p = 0; p < kXP; ++p) {
       const int g = g_row[p];
       x_voff[p] = (g >= 0 && g < a_rows)
                       ? (static_cast<uint32_t>(g) * static_cast<uint32_t>(lda) + piece_col[p] * 8u) * 2u
@@ -342,13 +352,13 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
     for (int p = 0; p < kSPieces; ++p)
       *reinterpret_cast<u32x4_t *>(ss[0] + s_lds + p * kScaleHalfLds) = permute_scales(sc_next[p]);
 #pragma unroll
-    for (int p = 0; p < kXPieces; ++p)
+    for (int p = 0; p < kXP; ++p)
       *reinterpret_cast<u32x4_t *>(xs[0] + lds_off[p]) = permute_k8(load16(x_rsrc, x_voff[p], 0));
-    u32x4_t xr[kXAhead][kXPieces];
+    u32x4_t xr[kXAhead][kXP];
 #pragma unroll
     for (int d = 1; d < kXAhead; ++d)
 #pragma unroll
-      for (int p = 0; p < kXPieces; ++p)
+      for (int p = 0; p < kXP; ++p)
         xr[d][p] = load16(x_rsrc, d < n_steps ? x_voff[p] : kNoLoad,
                           static_cast<uint32_t>(d) * (kChunkK * 2));
     __syncthreads();
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
         }
       }
 #pragma unroll
-      for (int p = 0; p < kXPieces; ++p)
+      for (int p = 0; p < kXP; ++p)
         xr[i % kXAhead][p] = load16(x_rsrc, step + kXAhead < n_steps ? x_voff[p] : kNoLoad,
                                     static_cast<uint32_t>(step + kXAhead) * (kChunkK * 2));
       load_weights(ahead, w_rsrc, w_voff, step + 1, n_steps);
@@ -381,22 +391,25 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
         lut_blocks(sc1, lut, blk1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          bf16x8_t B[4];
+          bf16x8_t B[kMT][4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            B[j] = *reinterpret_cast<const bf16x8_t *>(brow + 256 * h + 16 * j);
+          for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              B[mt][j] = *reinterpret_cast<const bf16x8_t *>(
+                  brow + 16 * mt * kLdsRowBytes + 256 * h + 16 * j);
           const u32x4_t &x0 = h ? cur.b[0] : cur.a[0];
           const uint32_t w0w[4] = {x0[0], x0[1], x0[2], x0[3]};
-          mfma4(w0w, blk0[2 * h], blk0[2 * h + 1], B, acc[0]);
+          moe::mfma4_tiles<kMT>(w0w, blk0[2 * h], blk0[2 * h + 1], B, acc[0]);
           if (tile1_on) {
             const u32x4_t &x1 = h ? cur.b[1] : cur.a[1];
             const uint32_t w1w[4] = {x1[0], x1[1], x1[2], x1[3]};
-            mfma4(w1w, blk1[2 * h], blk1[2 * h + 1], B, acc[1]);
+            moe::mfma4_tiles<kMT>(w1w, blk1[2 * h], blk1[2 * h + 1], B, acc[1]);
           }
         }
       }
 #pragma unroll
-      for (int p = 0; p < kXPieces; ++p)
+      for (int p = 0; p < kXP; ++p)
         *reinterpret_cast<u32x4_t *>(xs[(step + 1) & 1] + lds_off[p]) =
             permute_k8(xr[(i + 1) % kXAhead][p]);
       // Each stage buffer is filled mid-way through the other stage (its last reads are
@@ -428,16 +441,19 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
       if (s0 + 7 < n_steps) run_step(g, 7, w1, w0);
     }
 
-    // acc[t][i] = result for weight row n_tile_t + 4 kb + i and sorted row m0 + r16.
-    if (r16 < m_cnt) {
-      uint16_t *crow = c + static_cast<size_t>(m0 + r16) * ldc;
+    // acc[t][mt][i] = result for weight row n_tile_t + 4 kb + i and sorted row
+    // m0 + 16 mt + r16.
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (16 * mt + r16 >= m_cnt) continue;
+      uint16_t *crow = c + static_cast<size_t>(m0 + 16 * mt + r16) * ldc;
       if (kSwiglu) {
         if (tile0_on) {
           float o[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // the BF16 values the unfused path stores, then its SwiGLU
-            const uint32_t gu = moe::pack_bf16x2(acc[0][i], acc[1][i]);
+            const uint32_t gu = moe::pack_bf16x2(acc[0][mt][i], acc[1][mt][i]);
             o[i] = moe::swiglu_clamp1(__uint_as_float(gu << 16),
                                       __uint_as_float(gu & 0xFFFF0000u), limit);
           }
@@ -451,8 +467,8 @@ __global__ __launch_bounds__(kThreads, 3) void grouped_gemm_kernel(
         for (int t = 0; t < kTiles; ++t) {
           if (t == 0 ? tile0_on : tile1_on) {
             uint2 v;
-            v.x = moe::pack_bf16x2(acc[t][0], acc[t][1]);
-            v.y = moe::pack_bf16x2(acc[t][2], acc[t][3]);
+            v.x = moe::pack_bf16x2(acc[t][mt][0], acc[t][mt][1]);
+            v.y = moe::pack_bf16x2(acc[t][mt][2], acc[t][mt][3]);
             *reinterpret_cast<uint2 *>(crow + (t == 0 ? n_tile0 : n_tile1) + 4 * kb) = v;
           }
         }
@@ -544,6 +560,14 @@ int grid_rows(int32_t num_experts, int32_t max_rows, int *chunk_rows) {
   return num_experts;
 }
 
+// Two 16-row tiles per pass when the experts average at least 24 rows: passes over 32
+// rows then halve the decode work and the weight re-reads. (The average comes from the
+// sizes alone; a few hot experts among light ones, as under skewed routing, keep one
+// tile per pass and three blocks per CU.)
+bool two_row_tiles(int32_t num_experts, int32_t max_rows) {
+  return static_cast<int64_t>(max_rows) >= 24LL * num_experts;
+}
+
 }  // namespace
 
 extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -560,9 +584,12 @@ extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_
   if (rc != MOE_OK || max_rows == 0) return rc;
   int chunk_rows = 0;
   const dim3 grid((n + kBlockN - 1) / kBlockN, grid_rows(num_experts, max_rows, &chunk_rows));
-  return moe::launch("moe_w4a16_grouped_gemm", grouped_gemm_kernel<false>, grid, dim3(kThreads),
-                     0, stream, a, lda, a_rows, a_gather, packed_ptrs, scale_ptrs, scale2,
-                     expert_offsets, num_experts, chunk_rows, c, ldc, max_rows, n, k, 0.0f);
+  return moe::launch("moe_w4a16_grouped_gemm",
+                     two_row_tiles(num_experts, max_rows) ? grouped_gemm_kernel<false, 2>
+                                                          : grouped_gemm_kernel<false, 1>,
+                     grid, dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
+                     scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows, c, ldc,
+                     max_rows, n, k, 0.0f);
 }
 
 extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -583,8 +610,10 @@ extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int
   if (rc != MOE_OK || max_rows == 0) return rc;
   int chunk_rows = 0;
   const dim3 grid((mi + kHalfN - 1) / kHalfN, grid_rows(num_experts, max_rows, &chunk_rows));
-  return moe::launch("moe_w4a16_grouped_gemm_swiglu", grouped_gemm_kernel<true>, grid,
-                     dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
+  return moe::launch("moe_w4a16_grouped_gemm_swiglu",
+                     two_row_tiles(num_experts, max_rows) ? grouped_gemm_kernel<true, 2>
+                                                          : grouped_gemm_kernel<true, 1>,
+                     grid, dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
                      scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows, act, ld_act,
                      max_rows, 2 * mi, k, limit);
 }

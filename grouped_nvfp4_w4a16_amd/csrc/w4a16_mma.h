@@ -47,6 +47,22 @@ __device__ __forceinline__ void mfma4(const uint32_t *words, const Fp4Table &b0,
   }
 }
 
+// As mfma4 for kMT B tiles (kMT x 16 activation rows): each packed dword is decoded once
+// and multiplied into every tile's accumulator.
+template <int kMT>
+__device__ __forceinline__ void mfma4_tiles(const uint32_t *words, const Fp4Table &b0,
+                                            const Fp4Table &b1, const bf16x8_t (*B)[4],
+                                            f32x4_t *acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t wd[4];
+    decode8(words[j], j < 2 ? b0 : b1, wd);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wd), B[mt][j], acc[mt], 0, 0, 0);
+  }
+}
+
 // The decode tables of four blocks whose E4M3 codes are the bytes of `sc`, from the LUT.
 __device__ __forceinline__ void lut_blocks(uint32_t sc, const uint8_t *lut, Fp4Table *blk) {
 #pragma unroll

@@ -244,6 +244,41 @@ def test_no_gather_and_row_cut_off(hip):
     assert rel_err(got[:35], ref[:35]) <= GATE
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_unused_experts_change_no_bits(hip, fused):
+    """Experts of 40, 50 and 33 rows average over 24 rows: the GEMM passes over 32 rows
+    at a time (two row tiles per decoded weight). Ten unused experts appended to the
+    table lower the average, and the GEMM then passes over 16 rows. Each output element
+    sums the same products in the same order either way: the bits must not change."""
+    rng = np.random.default_rng(12)
+    n, k = 96, 512
+    counts = [40, 50, 33]
+    x_bits = wl.bf16_normal(rng, (130, k))
+    experts = [wl.random_nvfp4(rng, n, k) for _ in counts]
+    s2 = rng.uniform(0.5, 2, 13).astype(np.float32)
+    gather = rng.integers(0, 130, sum(counts)).astype(np.int32)
+    outs = []
+    for extra in (0, 10):
+        offsets = np.concatenate([[0], np.cumsum(counts + [0] * extra)]).astype(np.int32)
+        table = upload_table(hip, experts + [None] * extra, s2[:3 + extra], n, k)
+        rows = int(offsets[-1])
+        x, g, off = bf16_dev(x_bits), dev(gather), dev(offsets)
+        if fused:
+            c = torch.full((rows, n // 2), -3.0, dtype=torch.bfloat16, device="cuda")
+            hip.moe_w4a16_grouped_gemm_swiglu(x, table, off, c, 7.0, g, max_rows=rows)
+        else:
+            c = torch.full((rows, n), -3.0, dtype=torch.bfloat16, device="cuda")
+            hip.moe_w4a16_grouped_gemm(x, table, off, c, g, max_rows=rows)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits_host(c).copy())
+    assert np.array_equal(outs[0], outs[1])
+    if not fused:
+        offsets = np.concatenate([[0], np.cumsum(counts)])
+        ref = _oracle(x_bits, experts, s2, offsets, n, gather, "bf16w")
+        _check_gemm(codecs.bf16_bits_to_f64(outs[0]), ref,
+                    _acc_bound(x_bits, experts, s2, offsets, gather, k))
+
+
 def test_many_experts_without_room_for_overflow_rows(hip):
     """65500 experts: the grid rows for overflow chunks would pass the 65535 limit, so the
     launch falls back to one block row per expert taking all of its rows (here 150 rows,
