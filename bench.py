@@ -134,13 +134,15 @@ def upload_workload(hip, w, torch):
         p, s = wl.expert_gate_up(w, e)
         gp.append(dev(p))
         gs.append(dev(s))
+        if w.gemm_n:  # a single grouped GEMM: no down projection
+            continue
         p, s = wl.expert_down(w, e)
         dp.append(dev(p))
         ds.append(dev(s))
     n_gu, k_gu = wl.gate_up_shape(w)
     n_dn, k_dn = wl.down_shape(w)
     gt = hip.ExpertTable(gp, gs, wl.scale2_gate_up(w), n_gu, k_gu)
-    dt = hip.ExpertTable(dp, ds, wl.scale2_down(w), n_dn, k_dn)
+    dt = None if w.gemm_n else hip.ExpertTable(dp, ds, wl.scale2_down(w), n_dn, k_dn)
     ids, wts = wl.routing(w)
     x = dev(wl.activations(w).view(np.int16)).view(torch.bfloat16)
     return gt, dt, dev(ids), dev(wts), x, ids
@@ -164,6 +166,7 @@ def cpu_baseline(w, ids_chunk, seconds_budget=15.0):
     n_gu, k_gu = wl.gate_up_shape(w)
     n_dn, k_dn = wl.down_shape(w)
     mi = w.moe_intermediate
+    single = bool(w.gemm_n)  # one grouped GEMM: no SwiGLU and no down projection
     done_bytes, flops, experts = 0, 0.0, 0
     c = np.zeros((int(offsets[-1]), n_gu))
     act = np.zeros((int(offsets[-1]), mi))
@@ -176,23 +179,26 @@ def cpu_baseline(w, ids_chunk, seconds_budget=15.0):
         gu = [None] * w.num_experts
         dn = [None] * w.num_experts
         gu[e] = wl.expert_gate_up(w, e)  # input generation: not timed
-        dn[e] = wl.expert_down(w, e)
+        if not single:
+            dn[e] = wl.expert_down(w, e)
         t0 = time.perf_counter()
         moe.grouped_gemm(x, al["sorted_token_ids"], gu, s2gu, offsets, c, "bf16w",
                          expert_subset=[e])
-        cr = codecs.round_bf16(c[lo:hi])
-        act[lo:hi] = codecs.round_bf16(moe.swiglu_clamp(cr[:, :mi], cr[:, mi:], w.limit))
-        moe.grouped_gemm(act, None, dn, s2dn, offsets, out, "bf16w", expert_subset=[e])
+        if not single:
+            cr = codecs.round_bf16(c[lo:hi])
+            act[lo:hi] = codecs.round_bf16(moe.swiglu_clamp(cr[:, :mi], cr[:, mi:], w.limit))
+            moe.grouped_gemm(act, None, dn, s2dn, offsets, out, "bf16w", expert_subset=[e])
         spent += time.perf_counter() - t0
-        done_bytes += proj_bytes(n_gu, k_gu) + proj_bytes(n_dn, k_dn)
-        flops += 2.0 * (hi - lo) * (n_gu * k_gu + n_dn * k_dn)
+        done_bytes += proj_bytes(n_gu, k_gu) + (0 if single else proj_bytes(n_dn, k_dn))
+        flops += 2.0 * (hi - lo) * (n_gu * k_gu + (0 if single else n_dn * k_dn))
         experts += 1
         if spent > seconds_budget:
             break
     dt = spent
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"{experts} experts of the {w.name} batch (gate_up + SwiGLU + down, "
+            "sample": (f"{experts} experts of the {w.name} batch "
+                       f"({'the grouped GEMM' if single else 'gate_up + SwiGLU + down'}, "
                        f"all their routed rows, BF16-weight mode, generation excluded), "
                        f"{dt:.1f} s"),
             "tflops": round(flops / dt / 1e12, 6)}
@@ -377,6 +383,11 @@ def main():
     # runs one sub-chunk, cycling through them).
     n_gu, k_gu = wl.gate_up_shape(w)
     n_dn, k_dn = wl.down_shape(w)
+    single = bool(w.gemm_n)  # one grouped GEMM (no SwiGLU, down or combine)
+    if single and (args.decode or args.unfused or args.device_router):
+        print(f"bench.py: {w.name} is a single grouped GEMM step (align + GEMM)",
+              file=sys.stderr)
+        sys.exit(2)
     step_bytes, step_flops, gu_bytes_alg = [], [], []
     gu_w, dn_w, gu_fl, dn_fl = [], [], [], []
     for c in range(n_chunks):
@@ -384,23 +395,24 @@ def main():
         cnt = np.bincount(ids_c.reshape(-1), minlength=w.num_experts)
         live = [e for e in range(w.num_experts) if cnt[e] > 0 and not w.is_null(e)]
         slots_live = int(sum(cnt[e] for e in live))
-        wb = len(live) * (proj_bytes(n_gu, k_gu) + proj_bytes(n_dn, k_dn))
+        dn_proj = proj_bytes(n_dn, k_dn) if not single else 0
+        wb = len(live) * (proj_bytes(n_gu, k_gu) + dn_proj)
         step_bytes.append(wb)
-        step_flops.append(2.0 * slots_live * (n_gu * k_gu + n_dn * k_dn))
+        step_flops.append(2.0 * slots_live * (n_gu * k_gu + (0 if single else n_dn * k_dn)))
         gu_w.append(len(live) * proj_bytes(n_gu, k_gu))
-        dn_w.append(len(live) * proj_bytes(n_dn, k_dn))
+        dn_w.append(len(live) * dn_proj)
         gu_fl.append(2.0 * slots_live * n_gu * k_gu)
-        dn_fl.append(2.0 * slots_live * n_dn * k_dn)
+        dn_fl.append(0.0 if single else 2.0 * slots_live * n_dn * k_dn)
         # gate_up launch, algorithmic bytes: touched weights + the activation rows read
         # once + the output rows written once (the SwiGLU output when fused, else the
         # gate_up values) + routing metadata
-        out_cols = n_gu if args.unfused else mi
+        out_cols = n_gu if (args.unfused or single) else mi
         gu_bytes_alg.append(len(live) * proj_bytes(n_gu, k_gu) + rows * hidden * 2
                             + slots_live * out_cols * 2 + (w.num_experts + 1) * 4
                             + rows * w.top_k * 4)
 
     stream = torch.cuda.current_stream()
-    need_zero = not all(dt.present)
+    need_zero = dt is not None and not all(dt.present)
     se = None
     if (args.with_shared or not args.no_shared) and w.moe_intermediate > 0:
         sg, su, sd = (torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
@@ -423,6 +435,13 @@ def main():
 
     def st_zero(x, ids, wts):  # null down entries: their rows must read as zero in the combine
         hip.moe_zero_rows(ws.expert_out[:s], stream)
+
+    c_single = (torch.empty((max(s, 1), n_gu), dtype=torch.bfloat16, device="cuda")
+                if single else None)
+
+    def st_single(x, ids, wts):
+        hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, c_single, ws.sorted_token_ids,
+                                   max_rows=s)
 
     def st_gate_up(x, ids, wts):
         hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
@@ -474,6 +493,9 @@ def main():
         stages += [("gemv_union_gate_up_swiglu", st_union_gate_up),
                    ("gemv_union_down", st_union_down)]
         gu_name, dn_name = "gemv_union_gate_up_swiglu", "gemv_union_down"
+    elif single:
+        stages += [("moe_align", st_align), ("grouped_gemm", st_single)]
+        gu_name, dn_name = "grouped_gemm", None
     else:
         stages.append(("moe_align", st_align))
         if need_zero:
@@ -492,7 +514,8 @@ def main():
         for c in range(n_chunks):
             step_bytes[c] += 3 * mi * hidden * 2
             step_flops[c] += 2.0 * rows * 3 * mi * hidden
-    stages.append(("moe_combine", st_union_combine if args.decode else st_combine))
+    if not single:
+        stages.append(("moe_combine", st_union_combine if args.decode else st_combine))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
 
@@ -540,7 +563,7 @@ def main():
     tflops = total_flops / (gpu_ms / 1000.0) / 1e12
 
     gu_s = np.array(per[gu_name]) / 1000.0
-    dn_s = np.array(per[dn_name]) / 1000.0
+    dn_s = np.array(per[dn_name]) / 1000.0 if dn_name else None
     gu_alg = np.array([gu_bytes_alg[c] for c in chunk_of])
     achieved = float(np.mean(gu_alg) / np.mean(gu_s) / 1e9)
 
@@ -550,8 +573,11 @@ def main():
                 "weight_GBps": round(float(np.mean([wb[c] for c in chunk_of])) / t / 1e9, 1),
                 "TFLOPs": round(float(np.mean([fl[c] for c in chunk_of])) / t / 1e12, 2)}
 
-    per_gemm = {"gate_up": gemm_line(gu_w, gu_fl, gu_s), "down": gemm_line(dn_w, dn_fl, dn_s)}
+    per_gemm = {"gate_up": gemm_line(gu_w, gu_fl, gu_s)}
+    if dn_name:
+        per_gemm["down"] = gemm_line(dn_w, dn_fl, dn_s)
     kernel_label = ("moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)" if args.decode
+                    else "moe_w4a16_grouped_gemm (single GEMM)" if single
                     else "moe_w4a16_grouped_gemm (gate_up)" if args.unfused
                     else "moe_w4a16_grouped_gemm_swiglu (gate_up + SwiGLU)")
     roofline = {"kernel": kernel_label, "bound": "hbm",
