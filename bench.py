@@ -21,7 +21,8 @@ feeds its output to the combine.
 
 ``decode`` times the decode / verify path on the small-M workload (8 rows, 256 experts,
 half of them absent) after the timed steps, outside ``value``: the union path
-(moe_row_union -> union GEMVs -> combine) and the sorted path on the same rows.
+(moe_row_union -> union GEMVs -> combine; the union leaves out experts absent from the
+table, so this path needs no zeroing) and the sorted path on the same rows.
 ``--decode`` runs the main step itself through the union path (rows <= 16).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -287,9 +288,11 @@ def time_decode_leg(hip, torch, steps):
               + int(sum(1 for e in ids_host.reshape(-1) if not w.is_null(int(e)))) * mi * 2)
     paths = {
         "union": [
+            # experts absent from the down table are left out of the union (the combine
+            # skips their slots): no zero-first step on this path
             ("moe_row_union", lambda: hip.moe_row_union(ids, w.num_experts, dws.u_eid, u_slot,
-                                                        dws.slot_perm, dws.counters)),
-            ("zero_expert_out", lambda: hip.moe_zero_rows(dws.expert_out[:s])),
+                                                        dws.slot_perm, dws.counters,
+                                                        present=dt)),
             ("gemv_union_gate_up_swiglu", lambda: hip.moe_w4a16_gemv_union_swiglu(
                 x, gt, dws.u_eid, u_slot, dws.act, w.limit, rows, top_k)),
             ("gemv_union_down", lambda: hip.moe_w4a16_gemv_union(
@@ -467,12 +470,9 @@ def main():
     # The decode path: the union of the rows' experts, outputs by (row, slot).
     dws = hip.DecodeWorkspace(rows, w.top_k, hidden, mi) if args.decode else None
 
-    def st_union(x, ids, wts):
+    def st_union(x, ids, wts):  # absent experts' slots left out: no zero-first step
         hip.moe_row_union(ids, w.num_experts, dws.u_eid, dws.u_slot[:s * rows], dws.slot_perm,
-                          dws.counters)
-
-    def st_union_zero(x, ids, wts):
-        hip.moe_zero_rows(dws.expert_out[:s], stream)
+                          dws.counters, present=dt if need_zero else None)
 
     def st_union_gate_up(x, ids, wts):
         hip.moe_w4a16_gemv_union_swiglu(x, gt, dws.u_eid, dws.u_slot[:s * rows], dws.act,
@@ -488,8 +488,6 @@ def main():
     stages = [("moe_router_topk", st_router)] if args.device_router else []
     if args.decode:
         stages.append(("moe_row_union", st_union))
-        if need_zero:
-            stages.append(("zero_expert_out", st_union_zero))
         stages += [("gemv_union_gate_up_swiglu", st_union_gate_up),
                    ("gemv_union_down", st_union_down)]
         gu_name, dn_name = "gemv_union_gate_up_swiglu", "gemv_union_down"

@@ -84,7 +84,7 @@ _SIGNATURES = {
         ctypes.c_int),
     "moe_dense_workspace_bytes": ([_i32, _i32, _i32, _i32], _i64),
     "moe_zero_rows": ([_vp, _i64, _i32, _i32, _vp], ctypes.c_int),
-    "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_w4a16_gemv_union": (
         [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32,
          _vp], ctypes.c_int),
@@ -242,10 +242,11 @@ def moe_w4a16_grouped_gemm_swiglu(a, table: "ExpertTable", expert_offsets, act, 
 
 
 def moe_row_union(topk_ids, num_experts: int, u_eid, u_slot, slot_perm=None, counters=None,
-                  stream=None) -> None:
+                  stream=None, present=None) -> None:
     """The union of the experts the rows of ``topk_ids`` (int32 ``[rows, top_k]``) selected:
     ``u_eid [rows*top_k]``, ``u_slot [rows*top_k, rows]``, optional ``slot_perm`` and
-    ``counters``; see the header."""
+    ``counters``; see the header. ``present`` (an ``ExpertTable``) leaves out the experts
+    with null entries in that table: their slots are not covered."""
     import torch
 
     for t, n in ((topk_ids, "topk_ids"), (u_eid, "u_eid"), (u_slot, "u_slot"),
@@ -259,8 +260,13 @@ def moe_row_union(topk_ids, num_experts: int, u_eid, u_slot, slot_perm=None, cou
                        (slot_perm, t_ids, "slot_perm"), (counters, 2, "counters")):
         if t is not None and (t.numel() < need or not t.is_contiguous()):
             raise ValueError(f"{n}: needs {need} contiguous elements")
+    pres = None
+    if present is not None:
+        if present.num_experts != num_experts:
+            raise ValueError("present: the table has another number of experts")
+        pres = _p(present.packed_ptrs)
     _check("moe_row_union", load().moe_row_union(
-        _p(topk_ids), rows, top_k, num_experts, _p(u_eid), _p(u_slot), _p(slot_perm),
+        _p(topk_ids), rows, top_k, num_experts, pres, _p(u_eid), _p(u_slot), _p(slot_perm),
         _p(counters), _stream(stream)))
 
 
@@ -650,17 +656,17 @@ def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: Expe
     union GEMV down (each slot's activation) -> combine through ``slot_perm``. Outputs are
     laid out by (row, slot), so no sort and no expert-sorted permutation are needed.
     ``fused=False`` runs the gate_up GEMV and swiglu_clamp as two calls (same bits).
-    Slots of absent experts must read as zero in the combine, so ``ws.expert_out`` is
-    zeroed first unless every down entry is present."""
+    Slots of experts absent from the down table are left out of the union (the combine
+    skips them), so unlike the sorted path no zero-first step is needed."""
     rows, top_k = topk_ids.shape
     t = rows * top_k
     if rows > ws.max_rows or top_k != ws.top_k:
         raise ValueError("the workspace was made for fewer rows or another top_k")
     u_slot = ws.u_slot[:t * rows]
+    # Slots of experts absent from the down table are left out of the union: the combine
+    # skips them, so no row needs the zero-first step.
     moe_row_union(topk_ids, gate_up.num_experts, ws.u_eid, u_slot, ws.slot_perm, ws.counters,
-                  stream)
-    if not all(down.present):
-        moe_zero_rows(ws.expert_out[:t], stream)
+                  stream, present=None if all(down.present) else down)
     mi = moe_intermediate
     if fused:
         moe_w4a16_gemv_union_swiglu(x, gate_up, ws.u_eid, u_slot, ws.act, limit, rows, top_k,

@@ -50,7 +50,8 @@ constexpr int kUnionMaxIds = 1024;  // rows * top_k: one thread per id, one work
 
 __global__ __launch_bounds__(kUnionMaxIds) void row_union_kernel(
     const int32_t *__restrict__ ids, int32_t rows, int32_t top_k, int32_t num_experts,
-    int32_t *__restrict__ u_eid, int32_t *__restrict__ u_slot, int32_t *__restrict__ slot_perm,
+    const uint64_t *__restrict__ present, int32_t *__restrict__ u_eid,
+    int32_t *__restrict__ u_slot, int32_t *__restrict__ slot_perm,
     int32_t *__restrict__ counters) {
   __shared__ int32_t s_id[kUnionMaxIds];    // id of a covered slot, else -1
   __shared__ int32_t s_uid[kUnionMaxIds];   // union entries in order
@@ -59,11 +60,12 @@ __global__ __launch_bounds__(kUnionMaxIds) void row_union_kernel(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = t / top_k, j = t - r * top_k;
 
-  // 1. A slot is covered when its id is in range and no lower slot of its row has it.
+  // 1. A slot is covered when its id is in range, its expert present and no lower slot
+  //    of its row has it.
   int id = -1;
   if (t < n_ids) {
     const int v = ids[t];
-    if (v >= 0 && v < num_experts) id = v;
+    if (v >= 0 && v < num_experts && (present == nullptr || present[v] != 0)) id = v;
   }
   s_id[t] = id;
   __syncthreads();
@@ -128,7 +130,8 @@ __global__ __launch_bounds__(kUnionMaxIds) void row_union_kernel(
 // covered lane has it. An entry's number is the count of openers below its opener.
 __global__ __launch_bounds__(64) void row_union_wave_kernel(
     const int32_t *__restrict__ ids, int32_t rows, int32_t top_k, int32_t num_experts,
-    int32_t *__restrict__ u_eid, int32_t *__restrict__ u_slot, int32_t *__restrict__ slot_perm,
+    const uint64_t *__restrict__ present, int32_t *__restrict__ u_eid,
+    int32_t *__restrict__ u_slot, int32_t *__restrict__ slot_perm,
     int32_t *__restrict__ counters) {
   __shared__ int32_t s_slot[64 * 64];  // u_slot: [n_ids][rows], n_ids * rows <= 64 * 64
   const int n_ids = rows * top_k;
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(64) void row_union_wave_kernel(
   int id = -1;
   if (t < n_ids) {
     const int v = ids[t];
-    if (v >= 0 && v < num_experts) id = v;
+    if (v >= 0 && v < num_experts && (present == nullptr || present[v] != 0)) id = v;
   }
   const bool valid = id >= 0;
   const int bits = num_experts > 1 ? 32 - __clz(num_experts - 1) : 1;
@@ -531,8 +534,9 @@ int check_union_gemv_args(const char *name, const uint16_t *a, int64_t lda, int3
 }  // namespace
 
 extern "C" int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_k,
-                             int32_t num_experts, int32_t *u_eid, int32_t *u_slot,
-                             int32_t *slot_perm, int32_t *counters, void *stream) {
+                             int32_t num_experts, const uint64_t *present, int32_t *u_eid,
+                             int32_t *u_slot, int32_t *slot_perm, int32_t *counters,
+                             void *stream) {
   moe::clear_error();
   MOE_REQUIRE(rows >= 0 && top_k >= 1 && num_experts >= 1,
               "row_union: need rows >= 0, top_k >= 1, num_experts >= 1");
@@ -544,10 +548,12 @@ extern "C" int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_
   const int n_ids = rows * top_k;
   if (n_ids <= 64)
     return moe::launch("moe_row_union", row_union_wave_kernel, dim3(1), dim3(64), 0, stream,
-                       topk_ids, rows, top_k, num_experts, u_eid, u_slot, slot_perm, counters);
+                       topk_ids, rows, top_k, num_experts, present, u_eid, u_slot, slot_perm,
+                       counters);
   const int threads = (n_ids + 63) / 64 * 64;
   return moe::launch("moe_row_union", row_union_kernel, dim3(1), dim3(threads), 0, stream,
-                     topk_ids, rows, top_k, num_experts, u_eid, u_slot, slot_perm, counters);
+                     topk_ids, rows, top_k, num_experts, present, u_eid, u_slot, slot_perm,
+                     counters);
 }
 
 extern "C" int moe_w4a16_gemv_union(const uint16_t *a, int64_t lda, int32_t a_rows,

@@ -347,11 +347,17 @@ int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales, float s
  * moe_row_union - the union of the experts a few rows selected ([FWD] workspace fields
  * u_eid, u_slot; the union is found by pairwise scans in one workgroup, no sort).
  *
- * Slot t = r * top_k + j is covered when topk_ids[t] is in [0, num_experts) and no lower
- * slot of row r holds the same id (a proper top-k never repeats an expert in a row; a
- * repeat is treated like an invalid id).
+ * Slot t = r * top_k + j is covered when topk_ids[t] is in [0, num_experts), the expert
+ * is present (below) and no lower slot of row r holds the same id (a proper top-k never
+ * repeats an expert in a row; a repeat is treated like an invalid id).
  *
  *   topk_ids   int32 [rows * top_k]          in
+ *   present    uint64 [num_experts] or NULL  in: with it, an expert whose entry is 0 (a
+ *                                            null table entry, e.g. a projection's
+ *                                            packed_ptrs) is treated like an invalid id:
+ *                                            its slots are not covered and open no entry.
+ *                                            The combine then skips them, so the rows of
+ *                                            absent experts need no zeroing.
  *   u_eid      int32 [rows * top_k]          out: the distinct ids of the covered slots in
  *                                            order of first appearance in t, then -1
  *   u_slot     int32 [rows * top_k, rows]    out: u_slot[p, r] = j when row r's slot j is
@@ -365,8 +371,8 @@ int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales, float s
  * rows * top_k > MOE_UNION_MAX_IDS, or a required pointer is NULL while rows > 0.
  */
 int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
-                  int32_t *u_eid, int32_t *u_slot, int32_t *slot_perm, int32_t *counters,
-                  void *stream);
+                  const uint64_t *present, int32_t *u_eid, int32_t *u_slot,
+                  int32_t *slot_perm, int32_t *counters, void *stream);
 
 /*
  * moe_w4a16_gemv_union - the W4A16 product of each union expert's rows, each expert's

@@ -329,12 +329,14 @@ def dense_mlp(x, gate_w, up_w, down_w, limit: float, mode: str):
 # Decode / verify: the union of a few rows' experts, each swept once
 # ---------------------------------------------------------------------------------------
 
-def row_union(topk_ids: np.ndarray, num_experts: int) -> dict:
+def row_union(topk_ids: np.ndarray, num_experts: int, present=None) -> dict:
     """The union of the experts the rows selected, with each row's slot per union entry.
 
-    Flat slot ``t = r * top_k + j``. A slot is covered when its id is in ``[0, E)`` and no
-    lower slot of the same row holds the same id (a proper top-k never repeats an expert
-    in a row; a repeat is treated like an invalid id). Returns:
+    Flat slot ``t = r * top_k + j``. A slot is covered when its id is in ``[0, E)``, the
+    expert is present (``present[e]`` true, when a mask is given: an expert absent from
+    this GPU's table is treated like an invalid id) and no lower slot of the same row holds
+    the same id (a proper top-k never repeats an expert in a row; a repeat is treated like
+    an invalid id). Returns:
 
     - ``u_eid[rows * top_k]``: the distinct ids of the covered slots in order of first
       appearance in the flat order, then -1.
@@ -356,6 +358,8 @@ def row_union(topk_ids: np.ndarray, num_experts: int) -> dict:
             e = int(ids[r, j])
             if not 0 <= e < num_experts:
                 continue
+            if present is not None and not present[e]:
+                continue  # absent expert: like an invalid id
             if any(int(ids[r, jj]) == e for jj in range(j)):
                 continue  # repeated in this row
             if e not in entry_of:

@@ -3,6 +3,8 @@ moe_w4a16_gemv_union and its SwiGLU-fused form (one-hot layout pins exact, per-e
 FP32 accumulation bound, fused == unfused bits), and the whole layer through the union.
 """
 
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 # --------------------------------------------------------------------------- row union
 
-def _union_gpu(hip, ids, num_experts):
+def _union_gpu(hip, ids, num_experts, present=None):
     rows, top_k = ids.shape
     t = rows * top_k
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -24,7 +26,12 @@ def _union_gpu(hip, ids, num_experts):
     u_slot = torch.full((t * rows,), -7, **i32)
     perm = torch.full((t,), -7, **i32)
     cnt = torch.full((2,), -7, **i32)
-    hip.moe_row_union(dev(ids.astype(np.int32)), num_experts, u_eid, u_slot, perm, cnt)
+    table = None
+    if present is not None:  # a stand-in table: only its pointer array is read
+        ptrs = np.where(present, 0x1000, 0).astype(np.int64)
+        table = types.SimpleNamespace(num_experts=num_experts, packed_ptrs=dev(ptrs))
+    hip.moe_row_union(dev(ids.astype(np.int32)), num_experts, u_eid, u_slot, perm, cnt,
+                      present=table)
     torch.cuda.synchronize()
     return (u_eid.cpu().numpy(), u_slot.cpu().numpy().reshape(t, rows), perm.cpu().numpy(),
             cnt.cpu().numpy())
@@ -45,6 +52,23 @@ def test_row_union_bit_exact(hip, rows, top_k, num_experts, seed):
         ids[0, 2] = ids[0, 1]  # a repeat inside a row: not covered
     u_eid, u_slot, perm, cnt = _union_gpu(hip, ids, num_experts)
     ref = moe.row_union(ids, num_experts)
+    assert np.array_equal(u_eid, ref["u_eid"])
+    assert np.array_equal(u_slot, ref["u_slot"])
+    assert np.array_equal(perm, ref["slot_perm"].reshape(-1))
+    assert cnt.tolist() == [ref["n_union"], ref["n_uncovered"]]
+
+
+@pytest.mark.parametrize("rows,top_k,num_experts,seed", [
+    (8, 8, 256, 20), (3, 5, 11, 21), (16, 8, 64, 22), (128, 8, 256, 23)])
+def test_row_union_present_mask_bit_exact(hip, rows, top_k, num_experts, seed):
+    """Experts absent from a table (null entries) are left out, in the one-wave kernel
+    (at most 64 ids) and the block-wide one."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, num_experts + 1, size=(rows, top_k)).astype(np.int32)
+    ids[1] = ids[0][::-1]
+    present = rng.random(num_experts) < 0.5
+    u_eid, u_slot, perm, cnt = _union_gpu(hip, ids, num_experts, present)
+    ref = moe.row_union(ids, num_experts, present)
     assert np.array_equal(u_eid, ref["u_eid"])
     assert np.array_equal(u_slot, ref["u_slot"])
     assert np.array_equal(perm, ref["slot_perm"].reshape(-1))
@@ -237,8 +261,13 @@ def test_decode_layer_small_m_vs_oracle(hip, fused):
                                       wl.scale2_gate_up(w), wl.scale2_down(w),
                                       w.moe_intermediate, w.limit, "bf16w")
     assert rel_err(got, ref) <= GATE
-    un = inter["union"]
+    # the layer's union leaves out the experts absent from the table (the combine skips
+    # their slots, so no zero-first step is needed); the oracle's layer keeps them and adds
+    # their zeros: the same outputs
+    present = np.isin(np.arange(w.num_experts), live)
+    un = moe.row_union(ids, w.num_experts, present)
     assert np.array_equal(ws.u_eid.cpu().numpy(), un["u_eid"])
+    assert np.array_equal(ws.slot_perm.cpu().numpy()[:ids.size], un["slot_perm"].reshape(-1))
     for r in range(w.rows):  # a row whose experts are all null gets exactly zero
         if all(w.is_null(int(e)) for e in ids[r]):
             assert np.all(got[r] == 0.0)

@@ -32,6 +32,31 @@ def test_row_union_hand_example():
     assert u["n_union"] == 3 and u["n_uncovered"] == 1
 
 
+def test_row_union_present_mask_hand_example():
+    # as above with expert 1 absent: its slots are not covered and open no entry
+    ids = np.array([[3, 1], [1, 5], [-1, 3]], dtype=np.int32)
+    present = np.array([True, False, True, True, True, True])
+    u = moe.row_union(ids, 6, present)
+    assert u["u_eid"].tolist() == [3, 5, -1, -1, -1, -1]
+    assert u["u_slot"].tolist() == [[0, -1, 1], [-1, 1, -1], [-1, -1, -1],
+                                    [-1, -1, -1], [-1, -1, -1], [-1, -1, -1]]
+    assert u["slot_perm"].tolist() == [[0, -1], [-1, 3], [-1, 5]]
+    assert u["n_union"] == 2 and u["n_uncovered"] == 3
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_row_union_absent_expert_is_an_invalid_id(seed):
+    rng = np.random.default_rng(seed)
+    e_n = 24
+    ids = rng.integers(-1, e_n, size=(8, 6)).astype(np.int32)
+    ids[2] = ids[1]
+    present = rng.random(e_n) < 0.5
+    masked = np.where((ids >= 0) & present[np.clip(ids, 0, e_n - 1)], ids, -1).astype(np.int32)
+    a, b = moe.row_union(ids, e_n, present), moe.row_union(masked, e_n)
+    for key in ("u_eid", "u_slot", "slot_perm", "n_union", "n_uncovered"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def _union_by_unique(ids, num_experts):
     """Second construction: dedupe each row, then numpy's unique with first indices."""
     rows, top_k = ids.shape
