@@ -10,6 +10,7 @@
 //
 // Both kernels move 16 bytes (8 BF16) per thread per operand with 128-bit loads and
 // stores and compute in FP32; a block of 256 threads covers 2048 columns of one row.
+#include "buffer_io.h"
 #include "common.h"
 #include "swiglu.h"
 
@@ -90,6 +91,56 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint16_t *__restric
   *reinterpret_cast<uint4 *>(c + row * ldc + col8 * 8) = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// The same combine for top_k == 8 with the expert rows read through a buffer resource:
+// the eight slot indices and weights are loaded first, then the eight rows together (an
+// excluded slot's offset is past the end and reads zeros without a memory access), so a
+// thread waits on two memory round trips instead of two per slot. The sum is still taken
+// in slot order and skips excluded slots, so the result has the generic kernel's bits.
+__global__ __launch_bounds__(kThreads) void moe_combine8_kernel(
+    const uint16_t *__restrict__ expert_out, int64_t ld_e, int32_t expert_rows,
+    const int32_t *__restrict__ token_to_perm, const float *__restrict__ weights,
+    const uint16_t *__restrict__ shared, int64_t ld_s, uint16_t *__restrict__ out,
+    int64_t ld_out, int32_t hidden) {
+  constexpr int kK = 8;
+  const int row = blockIdx.y;
+  const int col = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (col >= hidden) return;
+  const __amdgpu_buffer_rsrc_t er = moe::make_rsrc(
+      expert_out, static_cast<uint32_t>(static_cast<uint64_t>(expert_rows) * ld_e * 2));
+  int p[kK];
+  float w[kK];
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    p[j] = token_to_perm[static_cast<size_t>(row) * kK + j];
+    w[j] = weights[static_cast<size_t>(row) * kK + j];
+  }
+  moe::u32x4_t v[kK];
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    const bool ok = p[j] >= 0 && p[j] < expert_rows;
+    const uint32_t off = ok ? (static_cast<uint32_t>(p[j]) * static_cast<uint32_t>(ld_e) +
+                               static_cast<uint32_t>(col)) * 2u
+                            : moe::kNoLoad;
+    v[j] = moe::load16(er, off, 0);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    if (p[j] < 0 || p[j] >= expert_rows) continue;  // excluded slot: adds nothing
+    float f[8];
+    unpack8(make_uint4(v[j][0], v[j][1], v[j][2], v[j][3]), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += w[j] * f[i];
+  }
+  if (shared != nullptr) {
+    float sh[8];
+    unpack8(*reinterpret_cast<const uint4 *>(shared + static_cast<size_t>(row) * ld_s + col), sh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += sh[i];
+  }
+  *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(acc);
+}
+
 }  // namespace
 
 extern "C" int moe_zero_rows(uint16_t *c, int64_t ldc, int32_t rows, int32_t cols,
@@ -148,6 +199,12 @@ extern "C" int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t exp
                   (shared == nullptr || moe::aligned16(shared)),
               "moe_combine: BF16 pointers must be 16-byte aligned");
   const dim3 grid((hidden + kColsPerBlock - 1) / kColsPerBlock, rows);
+  // top_k 8 with expert rows below 2 GiB (buffer offsets are 32-bit; an excluded slot's
+  // offset 2^31 must lie past the end): all slot rows in flight at once.
+  if (top_k == 8 && static_cast<uint64_t>(expert_rows) * ld_e * 2 < (1ull << 31))
+    return moe::launch("moe_combine", moe_combine8_kernel, grid, dim3(kThreads), 0, stream,
+                       expert_out, ld_e, expert_rows, token_to_perm, topk_weights, shared,
+                       ld_s, out, ld_out, hidden);
   return moe::launch("moe_combine", moe_combine_kernel, grid, dim3(kThreads), 0, stream,
                      expert_out, ld_e, expert_rows, token_to_perm, topk_weights, shared, ld_s,
                      out, ld_out, hidden, top_k);

@@ -6,7 +6,8 @@ import torch
 
 import workloads as wl
 from oracle import codecs, moe
-from gpu_util import GATE, LazyExperts, bf16_dev, dev, f64, rel_err, upload_table, workload_tables
+from gpu_util import (GATE, LazyExperts, bf16_bits_host, bf16_dev, dev, f64, rel_err, upload_table,
+                      workload_tables)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +55,29 @@ def test_combine_vs_oracle(hip, shared):
     got = f64(out)
     bound = _ulp_bf16(ref) * 0.5 + 2 ** -20 * (np.abs(codecs.bf16_bits_to_f64(e_bits)).max() * 8 + 8)
     assert np.all(np.abs(got - ref) <= bound)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_combine_top8_form_has_the_generic_bits(hip, shared):
+    """top_k 8 takes the form with all slot rows in flight; the same 8 slots plus an
+    excluded ninth (top_k 9) take the generic loop. Both sum in slot order: same bits."""
+    rng = np.random.default_rng(13)
+    rows, hidden, s_rows = 40, 1032, 300
+    e_bits = wl.bf16_normal(rng, (s_rows, hidden))
+    ttp = rng.integers(0, s_rows, (rows, 8)).astype(np.int32)
+    ttp[2, 5] = -1
+    ttp[7, 0] = s_rows  # out of range
+    wts = rng.random((rows, 8)).astype(np.float32)
+    sh = bf16_dev(wl.bf16_normal(rng, (rows, hidden))) if shared else None
+    e = bf16_dev(e_bits)
+    out8 = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    out9 = torch.empty_like(out8)
+    hip.moe_combine(e, dev(ttp), dev(wts), out8, sh)
+    ttp9 = np.concatenate([ttp, np.full((rows, 1), -1, np.int32)], axis=1)
+    wts9 = np.concatenate([wts, np.zeros((rows, 1), np.float32)], axis=1)
+    hip.moe_combine(e, dev(ttp9), dev(wts9), out9, sh)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(out8), bf16_bits_host(out9))
 
 
 def test_combine_top1_unit_weight_copies(hip):
