@@ -265,14 +265,17 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
       const int q = q0 + lane;
       const int e = q < n_ids ? u_eid[q] : -1;
       const bool in = e >= 0 && e < num_experts;
+      // the entry's three table values in one round trip
       const uint64_t pk = in ? packed_ptrs[e] : 0;
+      const uint64_t sp = in ? scale_ptrs[e] : 0;
+      const float s2 = in ? scale2s[e] : 0.0f;
       const bool ok = pk != 0;
       const uint64_t m = __ballot(ok);
       if (ok) {
         LiveEntry le;
         le.packed = pk;
-        le.scales = scale_ptrs[e];
-        le.scale2 = scale2s[e];
+        le.scales = sp;
+        le.scale2 = s2;
         le.p = q;
         live[n + __popcll(m & ((1ull << lane) - 1ull))] = le;
       }
@@ -284,30 +287,6 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
   const int n_live = n_live_s;
   const int n_items = n_live * items_per_entry;
   if (static_cast<int>(blockIdx.x) >= n_items) return;  // uniform: the whole block
-  // Each live entry's tokens: its routed rows (u_slot[p, r] >= 0) in order of r, as
-  // output rows r * top_k + slot. A wave reads the u_slot rows of 64 / rows entries at
-  // once, one lane per (entry, row); a present row's token index is its rank in its
-  // entry's lanes.
-  for (int q = tid; q < n_live * 16; q += kThreads) tok[q] = -1;
-  __syncthreads();
-  {
-    const int epw = 64 / rows;  // entries per wave and pass (rows >= 1 here)
-    const int le_lane = lane / rows, r = lane - le_lane * rows;
-    const int seg0 = le_lane * rows;
-    for (int base = wave * epw; base < n_live; base += kWaves * epw) {
-      const int li = base + le_lane;
-      const bool mine = le_lane < epw && li < n_live;
-      const int slot = mine ? u_slot[static_cast<int64_t>(live[li].p) * rows + r] : -1;
-      const uint64_t m = __ballot(slot >= 0);
-      if (slot >= 0) {
-        const uint64_t below = (1ull << lane) - 1ull, seg_below = (1ull << seg0) - 1ull;
-        const int rank = __popcll(m & below & ~seg_below);
-        tok[li * 16 + rank] = static_cast<int16_t>(r * top_k + slot);
-      }
-    }
-  }
-  __syncthreads();
-
   // readfirstlane works on int: widen through uint32_t, so that a low word with its top
   // bit set is not sign-extended into the high word of an address.
   const auto rfl32 = [](uint32_t v) {
@@ -319,8 +298,8 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
   };
   const __amdgpu_buffer_rsrc_t x_rsrc =
       make_rsrc(a, static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(lda) * 2u);
-  // The whole Item of it: its entry's buffers (uniform), its rows, this lane's token.
-  const auto make_item = [&](int it) {
+  // Item it without its tokens: its entry's buffers (uniform) and its rows.
+  const auto make_item_w = [&](int it) {
     Item m;
     const int li = it / items_per_entry, g = it - li * items_per_entry;
     const LiveEntry &le = live[li];
@@ -335,16 +314,26 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
     m.w_base[1] = static_cast<uint32_t>(n_t1) * row_bytes;
     m.s_base[0] = static_cast<uint32_t>(n_t0) * srow_bytes;
     m.s_base[1] = static_cast<uint32_t>(n_t1) * srow_bytes;
+    return m;
+  };
+  // This lane's token of item it (the entry's token r16: output row and input row).
+  const auto set_tokens = [&](Item &m, int it) {
+    const int li = it / items_per_entry;
     m.dst_row = tok[li * 16 + r16];
     const int src = m.dst_row < 0 ? -1 : (a_per_slot ? m.dst_row : m.dst_row / top_k);
     m.x_voff = (src >= 0 && src < a_rows)
                    ? (static_cast<uint32_t>(src) * static_cast<uint32_t>(lda) + 64u * kb) * 2u
                    : kNoLoad;
+  };
+  // The whole Item of it: its entry's buffers (uniform), its rows, this lane's token.
+  const auto make_item = [&](int it) {
+    Item m = make_item_w(it);
+    set_tokens(m, it);
     return m;
   };
   // Step i of this wave's share of an item (steps kw, kw + kKSplit, ...); live = false
   // loads nothing, so every load stays unconditional.
-  const auto load_step = [&](StepRegs &st, const Item &m, int i, bool live_step) {
+  const auto load_w = [&](StepRegs &st, const Item &m, int i, bool live_step) {
     const int step = kw + i * kKSplit;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -357,10 +346,17 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
           m.s, static_cast<int>(on ? s_lane : kNoLoad),
           static_cast<int>(m.s_base[t] + static_cast<uint32_t>(step) * 16u), 0);
     }
+  };
+  const auto load_x = [&](StepRegs &st, const Item &m, int i, bool live_step) {
+    const int step = kw + i * kKSplit;
     const uint32_t xv = live_step ? m.x_voff : kNoLoad;
     const uint32_t xsoff = static_cast<uint32_t>(step) * (kChunkK * 2);
 #pragma unroll
     for (int q = 0; q < 8; ++q) st.x[q] = load16(x_rsrc, xv + 16u * q, xsoff);
+  };
+  const auto load_step = [&](StepRegs &st, const Item &m, int i, bool live_step) {
+    load_w(st, m, i, live_step);
+    load_x(st, m, i, live_step);
   };
 
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -397,11 +393,40 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
     }
   };
 
-  const int G = gridDim.x;
+  // The first item's weights go out before the token maps are built (they need only its
+  // entry), its activations after.
   int item = blockIdx.x;
-  Item cur = make_item(item);
+  Item cur = make_item_w(item);
   StepRegs sA, sB;
-  load_step(sA, cur, 0, true);
+  load_w(sA, cur, 0, true);
+
+  // Each live entry's tokens: its routed rows (u_slot[p, r] >= 0) in order of r, as
+  // output rows r * top_k + slot. A wave reads the u_slot rows of 64 / rows entries at
+  // once, one lane per (entry, row); a present row's token index is its rank in its
+  // entry's lanes.
+  for (int q = tid; q < n_live * 16; q += kThreads) tok[q] = -1;
+  __syncthreads();
+  {
+    const int epw = 64 / rows;  // entries per wave and pass (rows >= 1 here)
+    const int le_lane = lane / rows, r = lane - le_lane * rows;
+    const int seg0 = le_lane * rows;
+    for (int base = wave * epw; base < n_live; base += kWaves * epw) {
+      const int li = base + le_lane;
+      const bool mine = le_lane < epw && li < n_live;
+      const int slot = mine ? u_slot[static_cast<int64_t>(live[li].p) * rows + r] : -1;
+      const uint64_t m = __ballot(slot >= 0);
+      if (slot >= 0) {
+        const uint64_t below = (1ull << lane) - 1ull, seg_below = (1ull << seg0) - 1ull;
+        const int rank = __popcll(m & below & ~seg_below);
+        tok[li * 16 + rank] = static_cast<int16_t>(r * top_k + slot);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int G = gridDim.x;
+  set_tokens(cur, item);
+  load_x(sA, cur, 0, true);
   moe::build_code_table_lut(lut[0], tid, cur.scale2);
   __syncthreads();  // table 0 is complete
 
