@@ -11,7 +11,8 @@
 //   weight = score, / (sum of the selected scores) when renormalize, * routed_scale
 //
 // gfx950 design: one wave64 per row, four rows per block. Lane l holds logits
-// l, l + 64, ... in registers (up to 32 per lane, E <= 2048). The max and the softmax sum
+// l, l + 64, ... in registers: kPL of them, the smallest of 4, 8, 16, 32 that covers E
+// (E <= 2048), so that the per-round scans do no work for absent experts. The max and the softmax sum
 // are wave reductions; each of the top_k rounds is a local argmax over the lane's values
 // followed by a wave-wide (key, id) reduction, and lane r keeps the r-th pick. The
 // weights then take one expf per selected logit.
@@ -21,8 +22,8 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 constexpr int kThreads = 64 * kRowsPerBlock;
-constexpr int kPerLane = MOE_ROUTER_MAX_EXPERTS / 64;
-static_assert(MOE_ROUTER_MAX_EXPERTS % 64 == 0, "whole lanes");
+static_assert(MOE_ROUTER_MAX_EXPERTS % 64 == 0 && MOE_ROUTER_MAX_EXPERTS <= 32 * 64,
+              "whole lanes, at most 32 values per lane");
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -43,6 +44,7 @@ __device__ __forceinline__ void better(float &k, int &i, float k2, int i2) {
   i = take ? i2 : i;
 }
 
+template <int kPL>
 __global__ __launch_bounds__(kThreads) void router_topk_kernel(
     const float *__restrict__ logits, int64_t ld, int32_t rows, int32_t E,
     const float *__restrict__ bias, int32_t top_k, float routed_scale, int32_t renormalize,
@@ -52,10 +54,10 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
   if (row >= rows) return;  // whole waves leave together (no barriers below)
   const float *lg = logits + static_cast<size_t>(row) * ld;
 
-  float l[kPerLane];
+  float l[kPL];
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+  for (int i = 0; i < kPL; ++i) {
     const int e = lane + 64 * i;
     l[i] = e < E ? lg[e] : -INFINITY;
     m = fmaxf(m, l[i]);
@@ -63,17 +65,17 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
   m = wave_max(m);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+  for (int i = 0; i < kPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) sum += __expf(l[i] - m);
   }
   sum = wave_sum(sum);
 
   // Selection keys; a taken entry has its bit cleared in `avail`.
-  float key[kPerLane];
+  float key[kPL];
   unsigned avail = 0;  // bit i: entry lane + 64 i is still selectable
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+  for (int i = 0; i < kPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
       avail |= 1u << i;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
     float bk = 0.f;
     int bi = -1, bslot = -1;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < kPL; ++i) {
       const int e = lane + 64 * i;
       const bool ok = (avail >> i) & 1u;
       const bool take = ok && (bi < 0 || key[i] > bk);  // ids rise with i: keep the first
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
     const int owner = wi & 63, oslot = wi >> 6;
     float ol = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) ol = i == oslot ? l[i] : ol;
+    for (int i = 0; i < kPL; ++i) ol = i == oslot ? l[i] : ol;
     ol = __shfl(ol, owner, 64);
     if (lane == r) {
       my_id = wi;
@@ -148,7 +150,14 @@ extern "C" int moe_router_topk(const float *logits, int64_t ld_logits, int32_t r
   if (rows == 0) return MOE_OK;
   MOE_REQUIRE(logits && topk_ids && topk_weights, "router_topk: a required pointer is NULL");
   const dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  return moe::launch("moe_router_topk", router_topk_kernel, grid, dim3(kThreads), 0, stream,
-                     logits, ld_logits, rows, num_experts, bias, top_k, routed_scale,
-                     renormalize, topk_ids, topk_weights);
+  const auto go = [&](auto kern) {
+    return moe::launch("moe_router_topk", kern, grid, dim3(kThreads), 0, stream, logits,
+                       ld_logits, rows, num_experts, bias, top_k, routed_scale, renormalize,
+                       topk_ids, topk_weights);
+  };
+  const int per_lane = (num_experts + 63) / 64;
+  if (per_lane <= 4) return go(router_topk_kernel<4>);
+  if (per_lane <= 8) return go(router_topk_kernel<8>);
+  if (per_lane <= 16) return go(router_topk_kernel<16>);
+  return go(router_topk_kernel<32>);
 }

@@ -58,7 +58,8 @@ def test_router_workload_logits_bit_exact_ids(hip, name):
 
 
 @pytest.mark.parametrize("rows,e,k,seed", [(37, 5, 2, 1), (64, 64, 8, 2), (9, 300, 13, 3),
-                                           (5, 2048, 64, 4), (3, 1, 1, 5), (50, 2000, 1, 6)])
+                                           (5, 2048, 64, 4), (3, 1, 1, 5), (50, 2000, 1, 6),
+                                           (20, 1000, 8, 7), (11, 512, 6, 8)])
 def test_router_shapes_and_limits(hip, rows, e, k, seed):
     rng = np.random.default_rng(seed)
     lg = (rng.standard_normal((rows, e)) * 3).astype(np.float32)
