@@ -354,8 +354,8 @@ def time_decode_leg(hip, torch, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the expert-parallel split across GPUs is a design note, not built.",
+        print(f"bench.py: the routed-MoE path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "splitting the experts across GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 
