@@ -36,14 +36,15 @@ __all__ = [
     "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "moe_dense_workspace_bytes",
     "dense_workspace", "SharedExpert", "moe_zero_rows",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
-    "moe_layer_decode", "UNION_MAX_ROWS",
+    "moe_layer_decode", "UNION_MAX_ROWS", "source_sha256",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
 
 # Every symbol include/moe_w4a16.h declares.
 EXPORTS = (
-    "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_align", "moe_w4a16_grouped_gemm",
+    "moe_w4a16_status_string", "moe_w4a16_last_error", "moe_w4a16_source_sha256", "moe_align",
+    "moe_w4a16_grouped_gemm",
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
     "moe_dense_workspace_bytes", "moe_zero_rows", "moe_row_union", "moe_w4a16_gemv_union",
@@ -64,6 +65,7 @@ _f32 = ctypes.c_float
 _SIGNATURES = {
     "moe_w4a16_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_w4a16_last_error": ([], ctypes.c_char_p),
+    "moe_w4a16_source_sha256": ([], ctypes.c_char_p),
     "moe_align": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_w4a16_grouped_gemm": (
         [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp],
@@ -103,7 +105,8 @@ class MoeError(RuntimeError):
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
-    """Load the shared library (once). Raises if it has not been built."""
+    """Load the shared library (once). Raises if it has not been built, or if it was built
+    from sources other than the ones on disk (the source hash compiled into it differs)."""
     global _LIB
     if _LIB is not None:
         return _LIB
@@ -116,8 +119,20 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    from . import build as _build
+
+    built, on_disk = lib.moe_w4a16_source_sha256().decode(), _build.source_sha256()
+    if built != on_disk:
+        raise RuntimeError(
+            f"{path} was built from other sources (library {built[:16]}, sources on disk "
+            f"{on_disk[:16]}): rebuild it with `python -m grouped_nvfp4_w4a16_amd.build`")
     _LIB = lib
     return lib
+
+
+def source_sha256() -> str:
+    """The source hash compiled into the loaded library (equal to the sources on disk)."""
+    return load().moe_w4a16_source_sha256().decode()
 
 
 def _check(name: str, status: int) -> None:
@@ -577,6 +592,14 @@ class Workspace:
         self.expert_out = torch.empty(s, hidden, **bf)
 
 
+def _same_experts(gate_up: ExpertTable, down: ExpertTable) -> None:
+    """A layer's two tables must hold the same experts: a down entry whose gate_up entry is
+    null would read activation rows nothing wrote."""
+    if gate_up.num_experts != down.num_experts or gate_up.present != down.present:
+        raise ValueError("gate_up and down tables must have the same experts present "
+                         "(null entries at the same expert ids)")
+
+
 def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable,
               moe_intermediate: int, limit: float, ws: Workspace, out, shared=None,
               stream=None, fused: bool = True) -> None:
@@ -590,6 +613,7 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     (each valid slot's row lies in its expert's segment), so the zeroing is skipped.
     ``shared`` is the combine's shared term: a ``[rows, H]`` BF16 tensor, or a
     ``SharedExpert``, which is then run over ``x`` after the routed experts."""
+    _same_experts(gate_up, down)
     rows, top_k = topk_ids.shape
     s = rows * top_k
     moe_align(topk_ids, gate_up.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
@@ -658,6 +682,7 @@ def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: Expe
     ``fused=False`` runs the gate_up GEMV and swiglu_clamp as two calls (same bits).
     Slots of experts absent from the down table are left out of the union (the combine
     skips them), so unlike the sorted path no zero-first step is needed."""
+    _same_experts(gate_up, down)
     rows, top_k = topk_ids.shape
     t = rows * top_k
     if rows > ws.max_rows or top_k != ws.top_k:

@@ -30,6 +30,28 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cpp")))
 
 
+def hashed_files() -> list[str]:
+    """Every file the library is compiled from: the sources, their headers and the C ABI."""
+    csrc = os.path.join(PKG_DIR, "csrc")
+    return sorted(sources() + glob.glob(os.path.join(csrc, "*.h")) +
+                  glob.glob(os.path.join(ROOT, "include", "*.h")))
+
+
+def source_sha256() -> str:
+    """SHA-256 over the names and contents of hashed_files(). The build compiles it into
+    the library (moe_w4a16_source_sha256), so a loaded library can be matched to the
+    sources on disk."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for path in hashed_files():
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def command(out_path: str) -> list[str]:
     return [
         hipcc(),
@@ -44,6 +66,7 @@ def command(out_path: str) -> list[str]:
         "-Wno-unused-function",
         f"-I{os.path.join(ROOT, 'include')}",
         f"-I{os.path.join(PKG_DIR, 'csrc')}",
+        f'-DMOE_W4A16_SOURCE_SHA256="{source_sha256()}"',
         *sources(),
         "-o", out_path,
     ]

@@ -30,3 +30,9 @@ extern "C" const char *moe_w4a16_status_string(int status) {
 }
 
 extern "C" const char *moe_w4a16_last_error(void) { return moe::g_last_error; }
+
+#ifndef MOE_W4A16_SOURCE_SHA256
+#define MOE_W4A16_SOURCE_SHA256 "unknown"
+#endif
+
+extern "C" const char *moe_w4a16_source_sha256(void) { return MOE_W4A16_SOURCE_SHA256; }

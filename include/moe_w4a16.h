@@ -74,6 +74,12 @@ const char *moe_w4a16_status_string(int status);
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char *moe_w4a16_last_error(void);
 
+/* SHA-256 (64 lowercase hex digits) of the sources this library was compiled from: every
+ * csrc/ source and header and this file, hashed by name and content at build time. A
+ * loader compares it with the same hash of the sources on disk to refuse a library built
+ * from other sources. Never NULL; a static string owned by the library. */
+const char *moe_w4a16_source_sha256(void);
+
 /* Largest expert count moe_align accepts (one workgroup holds the histograms). */
 #define MOE_ALIGN_MAX_EXPERTS 2048
 

@@ -4,8 +4,10 @@ The fused call must give the same bits as the two calls it replaces (grouped GEM
 [rows, 2 mi] buffer, then swiglu_clamp on its halves), for every shape the two calls
 accept: mi not a multiple of the block's 64 gate columns, experts with more rows than
 one pass, null entries (their rows are left alone), out-of-range gather indices, and
-scale codes that take the exact decode path. Its agreement with the oracle is checked
-at layer level (tests/test_gpu_layer.py runs the layer fused and unfused).
+zero, subnormal, negative and NaN scale codes (every code goes through the same per-block
+decode table). Its agreement with the oracle is checked at layer level
+(tests/test_gpu_layer.py runs the layer fused and unfused); the table itself is checked
+against the oracle on all 256 scale codes in tests/test_gpu_gemm.py.
 """
 
 import numpy as np
@@ -29,7 +31,7 @@ def _problem(seed, mi, k, counts, null, special):
             experts.append(None)
             continue
         packed, scales = wl.random_nvfp4(rng, 2 * mi, k)
-        if special:  # zero, subnormal, max and NaN codes take the exact path
+        if special:  # zero, subnormal, max, negative and NaN scale codes
             flat = scales.reshape(-1)
             idx = rng.choice(flat.size, size=min(64, flat.size), replace=False)
             flat[idx] = rng.choice(np.array([0x00, 0x01, 0x07, 0x7E, 0x7F, 0x80, 0xB8], np.uint8),

@@ -48,6 +48,16 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, name) is not None
 
 
+def test_library_was_built_from_these_sources(lib):
+    """The source hash compiled into the library is the hash of the sources on disk, and
+    load() refuses a library whose hash differs."""
+    assert lib.moe_w4a16_source_sha256().decode() == builder.source_sha256()
+    assert len(builder.source_sha256()) == 64
+    names = [os.path.relpath(p, ROOT) for p in builder.hashed_files()]
+    assert "include/moe_w4a16.h" in names
+    assert "grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip" in names
+
+
 def test_status_strings(lib):
     assert lib.moe_w4a16_status_string(0) == b"ok"
     assert lib.moe_w4a16_status_string(1) == b"invalid argument"
