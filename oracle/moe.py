@@ -199,7 +199,7 @@ def router_topk(logits, top_k: int, bias=None, routed_scale: float = 1.0,
 # ---------------------------------------------------------------------------------------
 
 def grouped_gemm(a, a_gather, experts, scale2, expert_offsets, out, mode: str,
-                 expert_subset=None):
+                 expert_subset=None, workers: int = 1):
     """Grouped W4A16 product over the expert-sorted rows, written into ``out`` (float64).
 
     For every expert e whose table entry is not null (``experts[e]`` is a
@@ -211,20 +211,37 @@ def grouped_gemm(a, a_gather, experts, scale2, expert_offsets, out, mode: str,
     in FP64, with ``w_e`` from :func:`dequant` in ``mode``. Rows of null experts are left
     as they are: the caller's zeros stand. ``expert_subset`` limits the work to some
     experts (used for sampled checks at large sizes).
+
+    Each expert writes only its own segment of rows, so the experts are independent;
+    ``workers > 1`` runs them on that many threads (for full-size checks), with the same
+    result.
     """
     a = np.asarray(a, dtype=np.float64)
     offsets = np.asarray(expert_offsets, dtype=np.int64)
     num_experts = offsets.size - 1
     todo = range(num_experts) if expert_subset is None else expert_subset
-    for e in todo:
+
+    def one_expert(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi <= lo or experts[e] is None:
-            continue
-        packed, scales = experts[e]
+        if hi <= lo:
+            return
+        ex = experts[e]
+        if ex is None:
+            return
+        packed, scales = ex
         w = dequant(packed, scales, float(scale2[e]), mode)
         rows = np.arange(lo, hi)
         src = rows if a_gather is None else np.asarray(a_gather, dtype=np.int64)[rows]
         out[lo:hi, :] = a[src, :] @ w.T
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(one_expert, todo))  # list() re-raises a worker's exception
+    else:
+        for e in todo:
+            one_expert(e)
     return out
 
 
@@ -264,7 +281,7 @@ def combine(expert_out, token_to_perm, topk_weights, shared=None):
 
 
 def moe_layer(x, topk_ids, topk_weights, gate_up, down, scale2_gate_up, scale2_down,
-              moe_intermediate: int, limit: float, mode: str, shared=None):
+              moe_intermediate: int, limit: float, mode: str, shared=None, workers: int = 1):
     """One routed MoE layer over the rows of ``x`` (float64 ``[T, H]``).
 
     Steps, in the order of the grouped-prefill arm of forward_moe (2026-09-25):
@@ -275,7 +292,7 @@ def moe_layer(x, topk_ids, topk_weights, gate_up, down, scale2_gate_up, scale2_d
 
     In ``mode="bf16w"`` the three buffers the kernels keep in BF16 (gate_up output,
     activation, expert_out) are rounded to BF16; the returned output is left unrounded.
-    Returns ``(out, intermediates)``.
+    ``workers`` is passed to both grouped GEMMs. Returns ``(out, intermediates)``.
     """
     x = np.asarray(x, dtype=np.float64)
     rows, hidden = x.shape
@@ -285,11 +302,13 @@ def moe_layer(x, topk_ids, topk_weights, gate_up, down, scale2_gate_up, scale2_d
     rnd = round_bf16 if mode == "bf16w" else (lambda v: v)
 
     c = np.full((n_slots, 2 * moe_intermediate), np.nan)  # null-expert rows stay undefined
-    grouped_gemm(x, al["sorted_token_ids"], gate_up, scale2_gate_up, al["expert_offsets"], c, mode)
+    grouped_gemm(x, al["sorted_token_ids"], gate_up, scale2_gate_up, al["expert_offsets"], c, mode,
+                 workers=workers)
     c = rnd(c)
     act = rnd(swiglu_clamp(c[:, :moe_intermediate], c[:, moe_intermediate:], limit))
     expert_out = np.zeros((n_slots, hidden))  # zero first: skipped slots add exactly 0
-    grouped_gemm(act, None, down, scale2_down, al["expert_offsets"], expert_out, mode)
+    grouped_gemm(act, None, down, scale2_down, al["expert_offsets"], expert_out, mode,
+                 workers=workers)
     expert_out = rnd(expert_out)
     out = combine(expert_out, al["token_to_perm"], topk_weights, shared)
     return out, {"align": al, "c": c, "act": act, "expert_out": expert_out}

@@ -6,6 +6,8 @@ come only from ``oracle``. Nothing here computes any part of the path.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -13,6 +15,10 @@ import workloads as wl
 
 # The parity gate: max |gpu - oracle| / max |oracle| against the BF16-weight oracle.
 GATE = 5e-3
+
+# Host threads for the oracle's per-expert loop at full size (the GPU machine gives a process
+# 16 CPUs; its count of the host's cores may be larger).
+ORACLE_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
 def dev(a) -> torch.Tensor:
@@ -40,17 +46,36 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / scale) if scale > 0 else float(np.max(np.abs(got)))
 
 
+def rel_err_rows(got, ref) -> float:
+    """The gate taken row by row: max over rows of max |got - ref| / max |ref| in the row."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert got.shape == ref.shape and got.ndim == 2
+    assert np.all(np.isfinite(got)), "non-finite output"
+    scale = np.max(np.abs(ref), axis=1)
+    err = np.max(np.abs(got - ref), axis=1)
+    return float(np.max(np.where(scale > 0, err / np.where(scale > 0, scale, 1.0), err)))
+
+
+def oracle_threads():
+    """Context for a full-size oracle call on ORACLE_WORKERS threads: BLAS runs one thread
+    per worker, so the workers do not oversubscribe the cores."""
+    from threadpoolctl import threadpool_limits
+
+    return threadpool_limits(limits=1)
+
+
 class LazyExperts:
     """Per-expert NVFP4 weights of a workload, drawn on first use (None = null entry)."""
 
-    def __init__(self, w: wl.Workload, which: str, null=()):
-        self.w, self.which, self.null = w, which, set(null)
+    def __init__(self, w: wl.Workload, which: str, null=(), keep: bool = True):
+        self.w, self.which, self.null, self.keep = w, which, set(null), keep
         self._cache = {}
 
     def __len__(self):
         return self.w.num_experts
 
-    def get(self, e, keep=True):
+    def get(self, e, keep=None):
+        keep = self.keep if keep is None else keep
         if e in self.null or self.w.is_null(e):
             return None
         if e in self._cache:
@@ -106,7 +131,7 @@ def workload_tables(hip, w: wl.Workload, only=None):
     built once per test session. ``only``: upload just these experts."""
     key = (w.name, None if only is None else tuple(sorted(only)))
     if key not in _TABLES:
-        gu, dn = LazyExperts(w, "gate_up"), LazyExperts(w, "down")
+        gu, dn = LazyExperts(w, "gate_up", keep=False), LazyExperts(w, "down", keep=False)
         gt = upload_table(hip, gu, wl.scale2_gate_up(w), *wl.gate_up_shape(w), only=only)
         dt = upload_table(hip, dn, wl.scale2_down(w), *wl.down_shape(w), only=only)
         _TABLES[key] = (gu, dn, gt, dt)

@@ -6,8 +6,8 @@ import torch
 
 import workloads as wl
 from oracle import codecs, moe
-from gpu_util import (GATE, LazyExperts, bf16_bits_host, bf16_dev, dev, f64, rel_err, upload_table,
-                      workload_tables)
+from gpu_util import (GATE, ORACLE_WORKERS, LazyExperts, bf16_bits_host, bf16_dev, dev, f64,
+                      oracle_threads, rel_err, rel_err_rows, upload_table, workload_tables)
 
 pytestmark = pytest.mark.gpu
 
@@ -165,6 +165,25 @@ def test_small_m_half_null_vs_oracle(hip):
             assert np.all(got[r] == 0.0)
 
 
+def test_layer_refuses_tables_with_different_experts(hip):
+    """A down entry whose gate_up entry is null would read activation rows nothing wrote:
+    both layer calls refuse such a pair of tables before enqueuing anything."""
+    w = wl.custom("mismatch", 78, rows=16, num_experts=4, top_k=2, hidden=256,
+                  moe_intermediate=256)
+    ids, wts, x_bits = _layer_inputs(w)
+    _, _, gt, _ = _tables(hip, w, only={0, 1, 2})
+    _, _, _, dt = _tables(hip, w)
+    ws = hip.Workspace(w.rows, w.top_k, w.num_experts, w.hidden, w.moe_intermediate)
+    out = torch.empty((w.rows, w.hidden), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        hip.moe_layer(bf16_dev(x_bits), dev(ids), dev(wts), gt, dt, w.moe_intermediate,
+                      w.limit, ws, out)
+    dws = hip.DecodeWorkspace(w.rows, w.top_k, w.hidden, w.moe_intermediate)
+    with pytest.raises(ValueError):
+        hip.moe_layer_decode(bf16_dev(x_bits), dev(ids), dev(wts), gt, dt,
+                             w.moe_intermediate, w.limit, dws, out)
+
+
 def test_zero_rows_strided_view(hip):
     """moe_zero_rows writes zeros into exactly the rows x cols of a strided view."""
     buf = torch.full((40, 200), 3.0, dtype=torch.bfloat16, device="cuda")
@@ -200,21 +219,55 @@ def test_expert_parallel_halves_sum_to_full(hip):
     assert np.all(np.abs(a + b - full) <= tol)
 
 
-@pytest.mark.parametrize("name,rows", [("prefill_subchunk", [0, 131]), ("long_prefill", [4000])])
-def test_full_size_layer_sampled_rows(hip, name, rows):
-    """The 256-expert layer at full size (whole sub-chunk on the GPU, in the bench's launch
-    configuration); sampled output rows against the oracle computed row by row."""
-    w = wl.WORKLOADS[name]
-    ids, wts = wl.routing(w)
-    x_bits = wl.activations(w)
-    c = rows[0] // w.chunk  # the sub-chunk holding the sampled rows
-    sl = slice(c * w.chunk, (c + 1) * w.chunk)
+@pytest.mark.timeout(900)
+def test_prefill_subchunk_layer_every_row(hip):
+    """The 256-row, 256-expert sub-chunk at full size in the bench's launch configuration
+    (fused gate_up + SwiGLU): every output row, and the layer's own intermediate buffers
+    (SwiGLU output and expert_out, every expert's rows), against the oracle."""
+    w = wl.WORKLOADS["prefill_subchunk"]
+    ids, wts, x_bits = _layer_inputs(w)
     gu, dn, gt, dt = workload_tables(hip, w)
-    got, _ = _run_layer(hip, w, ids[sl], wts[sl], x_bits[sl], gt, dt)
-    assert np.all(np.isfinite(got)) and np.all(np.abs(got).max(axis=1) > 0)
-    local = [r - c * w.chunk for r in rows]
-    ref = _oracle_rows(w, ids[rows], wts[rows], x_bits[rows], gu, dn, "bf16w")
-    assert rel_err(got[local], ref) <= GATE
+    got, ws = _run_layer(hip, w, ids, wts, x_bits, gt, dt)
+    s = w.rows * w.top_k
+    act, e_out = f64(ws.act[:s]), f64(ws.expert_out[:s])
+    with oracle_threads():
+        ref, inter = moe.moe_layer(codecs.bf16_bits_to_f64(x_bits), ids, wts, gu, dn,
+                                   wl.scale2_gate_up(w), wl.scale2_down(w), w.moe_intermediate,
+                                   w.limit, "bf16w", workers=ORACLE_WORKERS)
+    r, rr = rel_err(got, ref), rel_err_rows(got, ref)
+    r_act, r_eo = rel_err(act, inter["act"]), rel_err(e_out, inter["expert_out"])
+    print(f"prefill_subchunk: out {r:.2e} (worst row {rr:.2e}), act {r_act:.2e}, "
+          f"expert_out {r_eo:.2e}")
+    assert r <= GATE and rr <= GATE
+    assert r_act <= GATE and r_eo <= GATE
+
+
+@pytest.mark.timeout(900)
+def test_long_prefill_every_subchunk(hip):
+    """Skewed routing at full size: all 16 sub-chunks of 256 rows through the layer (each
+    with its hot experts' overflow chunks), every output row against the oracle. Each
+    row's output depends only on its own input and routing, so the oracle runs the 4096
+    rows in one call."""
+    w = wl.WORKLOADS["long_prefill"]
+    ids, wts, x_bits = _layer_inputs(w)
+    gu, dn, gt, dt = workload_tables(hip, w)
+    got = np.empty((w.rows, w.hidden))
+    over = []  # (sub-chunk, rows of its largest expert)
+    for c in range(w.n_chunks):
+        sl = slice(c * w.chunk, (c + 1) * w.chunk)
+        got[sl], _ = _run_layer(hip, w, ids[sl], wts[sl], x_bits[sl], gt, dt)
+        over.append(int(np.bincount(ids[sl].reshape(-1), minlength=w.num_experts).max()))
+    assert min(over) > 64  # every sub-chunk has a hot expert cut into overflow chunks
+    with oracle_threads():
+        ref, _ = moe.moe_layer(codecs.bf16_bits_to_f64(x_bits), ids, wts, gu, dn,
+                               wl.scale2_gate_up(w), wl.scale2_down(w), w.moe_intermediate,
+                               w.limit, "bf16w", workers=ORACLE_WORKERS)
+    per_chunk = [rel_err(got[c * w.chunk:(c + 1) * w.chunk], ref[c * w.chunk:(c + 1) * w.chunk])
+                 for c in range(w.n_chunks)]
+    rr = rel_err_rows(got, ref)
+    print(f"long_prefill: worst sub-chunk {max(per_chunk):.2e}, worst row {rr:.2e}, "
+          f"hottest expert rows per sub-chunk {min(over)}..{max(over)}")
+    assert max(per_chunk) <= GATE and rr <= GATE
 
 
 def test_layer_from_router_logits_vs_oracle(hip):

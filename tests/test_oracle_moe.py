@@ -93,6 +93,27 @@ def test_dequant_matches_torch_fp32_arithmetic():
         assert np.array_equal(got_bits, ref_bits)
 
 
+def test_dequant_every_code_and_nibble_matches_torch():
+    # Row n: E4M3 code n in every block (zero, subnormal, negative, 448 and the two NaN
+    # codes included), nibbles (k + n) % 16; against torch's FP8 decode and FP32/BF16
+    # arithmetic of the same formula, NaN where torch gives NaN.
+    k_total = 64
+    nib = ((np.arange(k_total)[None, :] + np.arange(256)[:, None]) % 16).astype(np.uint8)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], k_total // 16, axis=1)
+    packed = _pack(nib)
+    v = torch.tensor([[_spec_nibble_value(int(q)) for q in row] for row in nib],
+                     dtype=torch.float32)
+    d = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float32)
+    for s2 in (np.float32(1.3719), np.float32(0.51)):
+        w32 = (v * d.repeat_interleave(16, dim=1)) * torch.tensor(float(s2), dtype=torch.float32)
+        ref = w32.to(torch.bfloat16).double().numpy()
+        got = moe.dequant(packed, scales, float(s2), "bf16w")
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        assert np.array_equal(np.isnan(got).all(axis=1), np.isin(np.arange(256), [0x7F, 0xFF]))
+        ok = ~np.isnan(ref)
+        assert np.array_equal(got[ok], ref[ok])
+
+
 def test_dequant_product_order_matters():
     # (v * d) * s2 and v * (d * s2) differ after BF16 rounding for a few inputs per
     # million; the oracle must follow the grouped GEMM's order (scale2 multiplied into
@@ -352,8 +373,9 @@ def _brute_layer(ids, wts, x_bits, gate_up, down, s2gu, s2dn, mi, limit, bf16w):
     return out
 
 
+@pytest.mark.parametrize("workers", [1, 3])
 @pytest.mark.parametrize("mode", ["exact", "bf16w"])
-def test_layer_brute_force(mode):
+def test_layer_brute_force(mode, workers):
     rng = np.random.default_rng(31)
     rows, top_k, num_experts, hidden, mi = 5, 2, 4, 32, 16
     ids = np.stack([rng.permutation(num_experts)[:top_k] for _ in range(rows)]).astype(np.int32)
@@ -371,7 +393,8 @@ def test_layer_brute_force(mode):
     s2gu = rng.uniform(0.5, 2, num_experts).astype(np.float32)
     s2dn = rng.uniform(0.5, 2, num_experts).astype(np.float32)
     x = codecs.bf16_bits_to_f64(x_bits)
-    got, _ = moe.moe_layer(x, ids, wts, gate_up, down, s2gu, s2dn, mi, 7.0, mode)
+    got, _ = moe.moe_layer(x, ids, wts, gate_up, down, s2gu, s2dn, mi, 7.0, mode,
+                           workers=workers)
     ref = _brute_layer(ids, wts, x_bits, gate_up, down, s2gu, s2dn, mi, 7.0, mode == "bf16w")
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
 
