@@ -31,7 +31,7 @@ table, so this path needs no zeroing) and the sorted path on the same rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe] [--unfused] [--device-router]
-                       [--with-shared] [--no-shared] [--decode] [--no-decode]
+                       [--with-shared] [--no-shared] [--decode] [--no-decode] [--no-long]
 """
 
 from __future__ import annotations
@@ -50,10 +50,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 SETTLE_S = 0.15  # untimed warm-up time before the timed steps (clock ramp)
-# Counter-measured HBM traffic of the gate_up GEMM, valid only for the kernel source it
-# was measured on (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated with a copy kernel).
-TRAFFIC_FILE = os.path.join(ROOT, "profiles",
-                            "grouped_gemm_gate_up_swiglu_prefill_subchunk_hbm_traffic.md")
+# Counter-measured HBM traffic of the gate_up GEMM on a workload, valid only for the kernel
+# source it was measured on (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated with a copy
+# kernel).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_swiglu_{}_hbm_traffic.md")
 KERNEL_SOURCES = ("grouped_nvfp4_w4a16_amd/csrc/grouped_gemm.hip",
                   "grouped_nvfp4_w4a16_amd/csrc/nvfp4_decode.h",
                   "grouped_nvfp4_w4a16_amd/csrc/w4a16_mma.h",
@@ -77,11 +77,12 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per gate_up launch from the committed counter summary, or None when the
-    summary is missing, covers another kernel or was taken on a different kernel source."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per gate_up launch from the committed counter summary of the workload, or
+    None when the summary is missing, covers another kernel or was taken on a different
+    kernel source."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILE.format(workload)).read()
     except OSError:
         return None
     fields = {}
@@ -95,6 +96,57 @@ def measured_traffic(kernel: str):
         return int(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+FLUSH_BYTES = 2 << 30  # 8x the 256 MB last-level cache (MALL)
+
+
+class HbmProbe:
+    """The library's pure-read probe over a 2 GiB buffer: the measured HBM read ceiling
+    (best of a few launch shapes), and a cache-evicting stream between timed iterations
+    of workloads that would otherwise stay cache-resident."""
+
+    SHAPES = ((1024, 8), (2048, 8), (4096, 8), (2048, 16), (4096, 16))
+
+    def __init__(self, hip, torch):
+        self.hip, self.torch = hip, torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.buf.fill_(1)
+        self.sink = torch.empty(max(b for b, _ in self.SHAPES), dtype=torch.int32,
+                                device="cuda")
+
+    def flush(self):
+        self.hip.moe_hbm_read_probe(self.buf, self.sink, 2048, 8)
+
+    def ceiling(self, reps: int = 10) -> dict:
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        best = None
+        for blocks, unroll in self.SHAPES:
+            for _ in range(2):
+                self.hip.moe_hbm_read_probe(self.buf, self.sink, blocks, unroll)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                self.hip.moe_hbm_read_probe(self.buf, self.sink, blocks, unroll)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gbs = FLUSH_BYTES * reps / (e0.elapsed_time(e1) / 1000.0) / 1e9
+            if best is None or gbs > best["GBps"]:
+                best = {"GBps": round(gbs, 1), "blocks": blocks, "unroll": unroll}
+        return {"kernel": "moe_hbm_read_probe", "bytes": FLUSH_BYTES, **best}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def parse():
@@ -121,6 +173,8 @@ def parse():
                          "each swept once; rows <= 16)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the separate decode-path measurement")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the skewed-routing long-prefill leg")
     return ap.parse_args()
 
 
@@ -202,7 +256,7 @@ def cpu_baseline(w, ids_chunk, seconds_budget=15.0):
             break
     dt = spent
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"{experts} experts of the {w.name} batch "
                        f"({'the grouped GEMM' if single else 'gate_up + SwiGLU + down'}, "
                        f"all their routed rows, BF16-weight mode, generation excluded), "
@@ -210,13 +264,14 @@ def cpu_baseline(w, ids_chunk, seconds_budget=15.0):
             "tflops": round(flops / dt / 1e12, 6)}
 
 
-def time_shared_expert(se, x, w, steps, torch, stream):
+def time_shared_expert(se, x, w, steps, torch, stream, probe):
     """The shared expert over one batch of rows: the gate/up GEMM with the SwiGLU, then the
-    down GEMM, each launched ``steps`` times back to back between two HIP events on the
-    stream (a pair of events around one launch of a few tens of microseconds would add
-    the event packets' own time to it). Each kernel's roofline bound is the larger of its
-    HBM time (weights + input rows + output rows, once) and its matrix-core time (dense
-    BF16 peak)."""
+    down GEMM. Its working set (~84 MB) fits in the last-level cache, so each timed launch
+    follows a cache-evicting stream (``probe.flush``) and has its own pair of HIP events
+    (median reported); the MALL-warm rate (``steps`` launches back to back between two
+    events) is reported beside it. Each kernel's roofline bound is the larger of its HBM
+    time (weights + input rows + output rows, once) and its matrix-core time (dense BF16
+    peak)."""
     import grouped_nvfp4_w4a16_amd as hip
 
     rows, hidden, inter = x.shape[0], w.hidden, w.moe_intermediate
@@ -230,21 +285,31 @@ def time_shared_expert(se, x, w, steps, torch, stream):
             for fn in launches:
                 fn()
         torch.cuda.synchronize()
-        secs = []
+        cold, warm = [], []
         for fn in launches:
+            pairs = []
+            for _ in range(steps):
+                probe.flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                pairs.append((e0, e1))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(steps):
                 fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            secs.append(e0.elapsed_time(e1) / 1000.0 / steps)
-        return secs
+            cold.append(float(np.median([a.elapsed_time(b) for a, b in pairs])) / 1000.0)
+            warm.append(e0.elapsed_time(e1) / 1000.0 / steps)
+        return cold, warm
 
     # the split-K form (the shared expert's own, through its workspace), then the
     # single-pass form for comparison
-    gu, dn = timed(se.workspace)
-    gu1, dn1 = timed(None)
+    (gu, dn), (gu_w, dn_w) = timed(se.workspace)
+    (gu1, dn1), _ = timed(None)
 
     def roof(name, secs, wbytes, in_bytes, out_bytes, flops):
         nbytes = wbytes + in_bytes + out_bytes
@@ -265,16 +330,21 @@ def time_shared_expert(se, x, w, steps, torch, stream):
             "down": roof("moe_dense_gemm_bf16", dn, hidden * inter * 2, rows * inter * 2,
                          rows * hidden * 2, 2.0 * rows * hidden * inter),
             "total_us": round((gu + dn) * 1e6, 2), "form": "split-K (workspace)",
+            "timing": "each launch after a 2 GiB cache-evicting read, median",
+            "mall_warm_us": {"gate_up_swiglu": round(gu_w * 1e6, 2),
+                             "down": round(dn_w * 1e6, 2)},
             "single_pass_us": {"gate_up_swiglu": round(gu1 * 1e6, 2),
                                "down": round(dn1 * 1e6, 2)}}
 
 
-def time_decode_leg(hip, torch, steps):
+def time_decode_leg(hip, torch, steps, probe):
     """The decode / verify path on the small-M workload (8 rows over 256 experts, experts
     [128, 256) absent), timed per stage with HIP events: the union path (moe_row_union ->
     union GEMV gate_up with the SwiGLU -> union GEMV down -> combine) and the sorted path
-    (moe_align -> zero -> grouped GEMMs -> combine) on the same rows. GB/s is unique
-    weight bytes (live experts, both projections) per step."""
+    (moe_align -> zero -> grouped GEMMs -> combine) on the same rows. Its weights (0.68 GB)
+    would partly stay in the 256 MB last-level cache from one step to the next, so every
+    timed step follows a cache-evicting stream outside its events. GB/s is unique weight
+    bytes (live experts, both projections) per step."""
     import workloads as wl
 
     w = wl.WORKLOADS["small_m"]
@@ -326,16 +396,15 @@ def time_decode_leg(hip, torch, steps):
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
               for _ in range(steps)]
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
         for i in range(steps):
+            probe.flush()
             for j, (_, fn) in enumerate(stages):
                 ev[i][j].record(stream)
                 fn()
             ev[i][len(stages)].record(stream)
-        t1.record(stream)
         torch.cuda.synchronize()
-        step_us = t0.elapsed_time(t1) * 1000.0 / steps
+        step_us = float(np.mean([ev[i][0].elapsed_time(ev[i][len(stages)]) * 1000.0
+                                 for i in range(steps)]))
         kus = {n: round(float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0
                                        for i in range(steps)])), 2)
                for j, (n, _) in enumerate(stages)}
@@ -344,39 +413,24 @@ def time_decode_leg(hip, torch, steps):
     gu_us = res["union"]["kernel_us"]["gemv_union_gate_up_swiglu"]
     achieved = gu_alg / gu_us / 1e3
     return {"workload": w.name, "rows": rows, "live_experts": len(live),
-            "unique_weight_bytes": int(wbytes), **res,
+            "unique_weight_bytes": int(wbytes),
+            "timing": "each step after a 2 GiB cache-evicting read", **res,
             "roofline": {"kernel": "moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)",
                          "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "alg_bytes_per_launch": int(gu_alg)}}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: the routed-MoE path runs on one GPU only (asked for --gpus {args.gpus}); "
-              "splitting the experts across GPUs is not implemented.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import grouped_nvfp4_w4a16_amd as hip
+def measure_workload(hip, torch, w, args, probe, steps: int, warmup: int):
+    """Runs the step on workload ``w``: ``warmup`` untimed steps, untimed steps until the
+    clock has settled, then exactly ``steps`` timed steps (one sub-chunk each, cycling
+    through the workload's sub-chunks). Workloads whose unique weight bytes per step are
+    under 1 GiB would stay partly in the 256 MB last-level cache between steps, so for
+    them each timed step follows a cache-evicting stream outside the step's events and
+    the step time is the mean of the per-step event times. Returns the measured fields,
+    the stream, the first sub-chunk's rows and host routing (for the side legs)."""
     import workloads as wl
 
-    if not os.path.exists(hip.LIB_PATH):
-        from grouped_nvfp4_w4a16_amd import build as builder
-        builder.build()
-    hip.load()
-    torch.cuda.set_device(0)
-    w = wl.WORKLOADS[args.workload]
-    if args.with_shared and w.moe_intermediate == 0:
-        print(f"bench.py: {w.name} is a single GEMM; it has no shared expert", file=sys.stderr)
-        sys.exit(2)
-    if args.decode and (w.chunk > hip.UNION_MAX_ROWS or w.moe_intermediate == 0):
-        print(f"bench.py: the decode path takes layer workloads of at most "
-              f"{hip.UNION_MAX_ROWS} rows per step ({w.name} has {w.chunk})", file=sys.stderr)
-        sys.exit(2)
     t_gen = time.perf_counter()
     gt, dt, ids_all, wts_all, x_all, ids_host = upload_workload(hip, w, torch)
     print(f"bench: uploaded {w.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
@@ -387,16 +441,12 @@ def main():
     out = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
     n_chunks = w.n_chunks
 
-    # Per-step work (first sub-chunk of the batch; for a multi-chunk workload each step
-    # runs one sub-chunk, cycling through them).
+    # Per-step work (for a multi-chunk workload each step runs one sub-chunk, cycling
+    # through them).
     n_gu, k_gu = wl.gate_up_shape(w)
     n_dn, k_dn = wl.down_shape(w)
     single = bool(w.gemm_n)  # one grouped GEMM (no SwiGLU, down or combine)
-    if single and (args.decode or args.unfused or args.device_router):
-        print(f"bench.py: {w.name} is a single grouped GEMM step (align + GEMM)",
-              file=sys.stderr)
-        sys.exit(2)
-    step_bytes, step_flops, gu_bytes_alg = [], [], []
+    step_bytes, step_flops, gu_bytes_alg, dn_bytes_alg = [], [], [], []
     gu_w, dn_w, gu_fl, dn_fl = [], [], [], []
     for c in range(n_chunks):
         ids_c = ids_host[c * rows:(c + 1) * rows]
@@ -418,6 +468,9 @@ def main():
         gu_bytes_alg.append(len(live) * proj_bytes(n_gu, k_gu) + rows * hidden * 2
                             + slots_live * out_cols * 2 + (w.num_experts + 1) * 4
                             + rows * w.top_k * 4)
+        # down launch: touched weights + the activation rows in + expert_out rows out
+        dn_bytes_alg.append(len(live) * dn_proj + slots_live * (mi + hidden) * 2
+                            + (w.num_experts + 1) * 4)
 
     stream = torch.cuda.current_stream()
     need_zero = dt is not None and not all(dt.present)
@@ -520,7 +573,8 @@ def main():
     if not single:
         stages.append(("moe_combine", st_union_combine if args.decode else st_combine))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(args.steps)]
+          for _ in range(steps)]
+    flush = max(step_bytes) < (1 << 30)
 
     def step(i, events=None):
         c = i % n_chunks
@@ -537,7 +591,7 @@ def main():
             events[len(stages)].record(stream)
 
     t_warm = time.perf_counter()
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     # Clock settle: the GPU needs some tens of milliseconds of load to reach its steady
@@ -548,31 +602,33 @@ def main():
     t_w = time.perf_counter() - t_warm
     while t_w < SETTLE_S and settle < 1000:
         for _ in range(5):
-            step(args.warmup + settle)
+            step(warmup + settle)
             settle += 1
         torch.cuda.synchronize()
         t_w = time.perf_counter() - t_warm
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
+        if flush:
+            probe.flush()
         step(i, ev[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(end)
-    ms_per_step = gpu_ms / args.steps
 
     names = [n for n, _ in stages]
     per = {n: [] for n in names}
     step_ms = []
-    for i in range(args.steps):
+    for i in range(steps):
         for j, n in enumerate(names):
             per[n].append(ev[i][j].elapsed_time(ev[i][j + 1]))
         step_ms.append(ev[i][0].elapsed_time(ev[i][len(stages)]))
     kern_us = {n: round(1000.0 * float(np.mean(v)), 2) for n, v in per.items()}
+    gpu_ms = float(np.sum(step_ms)) if flush else start.elapsed_time(end)
+    ms_per_step = gpu_ms / steps
 
-    chunk_of = [i % n_chunks for i in range(args.steps)]
+    chunk_of = [i % n_chunks for i in range(steps)]
     total_bytes = sum(step_bytes[c] for c in chunk_of)
     total_flops = sum(step_flops[c] for c in chunk_of)
     value = total_bytes / (gpu_ms / 1000.0) / 1e9
@@ -583,32 +639,105 @@ def main():
     gu_alg = np.array([gu_bytes_alg[c] for c in chunk_of])
     achieved = float(np.mean(gu_alg) / np.mean(gu_s) / 1e9)
 
-    def gemm_line(wb, fl, secs):
+    def gemm_line(wb, fl, secs, alg=None):
         t = float(np.mean(secs))
-        return {"us": round(t * 1e6, 2),
-                "weight_GBps": round(float(np.mean([wb[c] for c in chunk_of])) / t / 1e9, 1),
-                "TFLOPs": round(float(np.mean([fl[c] for c in chunk_of])) / t / 1e12, 2)}
+        d = {"us": round(t * 1e6, 2),
+             "weight_GBps": round(float(np.mean([wb[c] for c in chunk_of])) / t / 1e9, 1),
+             "TFLOPs": round(float(np.mean([fl[c] for c in chunk_of])) / t / 1e12, 2)}
+        if alg is not None:
+            d["alg_GBps"] = round(float(np.mean([alg[c] for c in chunk_of])) / t / 1e9, 1)
+        return d
 
-    per_gemm = {"gate_up": gemm_line(gu_w, gu_fl, gu_s)}
+    per_gemm = {"gate_up": gemm_line(gu_w, gu_fl, gu_s, gu_bytes_alg)}
     if dn_name:
-        per_gemm["down"] = gemm_line(dn_w, dn_fl, dn_s)
+        per_gemm["down"] = gemm_line(dn_w, dn_fl, dn_s, dn_bytes_alg)
     kernel_label = ("moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)" if args.decode
                     else "moe_w4a16_grouped_gemm (single GEMM)" if single
                     else "moe_w4a16_grouped_gemm (gate_up)" if args.unfused
                     else "moe_w4a16_grouped_gemm_swiglu (gate_up + SwiGLU)")
     roofline = {"kernel": kernel_label, "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel_label),
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kernel_label, w.name),
                 "avg_launch_us": round(float(np.mean(gu_s)) * 1e6, 2),
                 "alg_bytes_per_launch": int(np.mean(gu_alg))}
+    fields = {
+        "value": round(value, 2), "ms_per_step": round(ms_per_step, 4), "settle_steps": settle,
+        "tflops": round(tflops, 2),
+        "step_ms_p10_p90": [round(float(np.percentile(step_ms, 10)), 4),
+                            round(float(np.percentile(step_ms, 90)), 4)],
+        "gemms": per_gemm, "kernel_us": kern_us, "roofline": roofline,
+        "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
+        "wall_s": round(wall, 4),
+        "cache_flush_between_steps": bool(flush),
+    }
+    return fields, {"stream": stream, "se": se, "x_rows": x_all[:rows], "ids_host": ids_host}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: the routed-MoE path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "splitting the experts across GPUs is not implemented.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import grouped_nvfp4_w4a16_amd as hip
+    import workloads as wl
+
+    if not os.path.exists(hip.LIB_PATH):
+        from grouped_nvfp4_w4a16_amd import build as builder
+        builder.build()
+    hip.load()
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    if args.with_shared and w.moe_intermediate == 0:
+        print(f"bench.py: {w.name} is a single GEMM; it has no shared expert", file=sys.stderr)
+        sys.exit(2)
+    if args.decode and (w.chunk > hip.UNION_MAX_ROWS or w.moe_intermediate == 0):
+        print(f"bench.py: the decode path takes layer workloads of at most "
+              f"{hip.UNION_MAX_ROWS} rows per step ({w.name} has {w.chunk})", file=sys.stderr)
+        sys.exit(2)
+    if w.gemm_n and (args.decode or args.unfused or args.device_router):
+        print(f"bench.py: {w.name} is a single grouped GEMM step (align + GEMM)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    probe = HbmProbe(hip, torch)
+    ceiling = probe.ceiling()
+    print(f"bench: HBM read ceiling {ceiling['GBps']} GB/s", file=sys.stderr, flush=True)
+
+    fields, side = measure_workload(hip, torch, w, args, probe, args.steps, args.warmup)
+    fields["roofline"]["ceiling_GBps"] = ceiling["GBps"]
+    fields["roofline"]["frac_of_ceiling"] = round(fields["roofline"]["achieved"] /
+                                                  ceiling["GBps"], 4)
 
     shared = None
-    if se is not None and not args.with_shared:
-        shared = time_shared_expert(se, x_all[:rows], w, args.steps, torch, stream)
+    if side["se"] is not None and not args.with_shared:
+        shared = time_shared_expert(side["se"], side["x_rows"], w, args.steps, torch,
+                                    side["stream"], probe)
 
     decode = None
     if w.name == "prefill_subchunk" and not args.no_decode and not args.decode:
-        decode = time_decode_leg(hip, torch, args.steps)
+        decode = time_decode_leg(hip, torch, args.steps, probe)
+
+    long_leg = None
+    if w.name == "prefill_subchunk" and not args.no_long and not args.decode:
+        # skewed routing: the 16 sub-chunks of the long prefill, each a step, two passes
+        wl_long = wl.WORKLOADS["long_prefill"]
+        side = None
+        long_args = argparse.Namespace(**{**vars(args), "with_shared": False, "no_shared": True,
+                                          "device_router": False})
+        lf, _ = measure_workload(hip, torch, wl_long, long_args, probe,
+                                 2 * wl_long.n_chunks, args.warmup)
+        lf["roofline"]["ceiling_GBps"] = ceiling["GBps"]
+        lf["roofline"]["frac_of_ceiling"] = round(lf["roofline"]["achieved"] / ceiling["GBps"], 4)
+        long_leg = {"workload": wl_long.name, "rows_per_step": wl_long.chunk,
+                    "sub_chunks": wl_long.n_chunks, "routing": wl_long.routing,
+                    "steps": 2 * wl_long.n_chunks, "unit": "GB/s",
+                    "frac_of_peak": round(lf["value"] / HBM_PEAK_GBS, 4), **lf}
 
     if args.copy_probe:  # a plain copy of known size, for scaling HBM counters
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -618,32 +747,38 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, ids_host[:rows])
+        ids_host = wl.routing(w)[0]
+        cpu = cpu_baseline(w, ids_host[:w.chunk])
 
+    mi, hidden = w.moe_intermediate, w.hidden
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "settle_steps": settle,
-        "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC, "value": fields["value"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": fields["settle_steps"],
+        "ms_per_step": fields["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded NVFP4 weights and BF16 N(0,1) activations, random init)",
-        "config": {"workload": w.name, "rows_per_step": rows, "experts": w.num_experts,
+        "config": {"workload": w.name, "rows_per_step": w.chunk, "experts": w.num_experts,
                    "top_k": w.top_k, "hidden": hidden, "moe_intermediate": mi,
                    "routing": w.routing, "weight_format": "NVFP4 (E2M1 + E4M3/16 + FP32)",
                    "parallelism": "single GPU"},
-        "tflops": round(tflops, 2),
-        "step_ms_p10_p90": [round(float(np.percentile(step_ms, 10)), 4),
-                            round(float(np.percentile(step_ms, 90)), 4)],
-        "gemms": per_gemm,
+        "tflops": fields["tflops"],
+        "step_ms_p10_p90": fields["step_ms_p10_p90"],
+        "frac_of_peak": round(fields["value"] / HBM_PEAK_GBS, 4),
+        "frac_of_ceiling": round(fields["value"] / ceiling["GBps"], 4),
+        "hbm_ceiling": ceiling,
+        "gemms": fields["gemms"],
         "gate_up_fused_swiglu": not args.unfused,
         "device_router": bool(args.device_router),
         "shared_expert_in_step": bool(args.with_shared),
         "shared_expert": shared,
         "decode_path": bool(args.decode),
         "decode": decode,
-        "unique_weight_bytes_per_step": int(np.mean([step_bytes[c] for c in chunk_of])),
-        "wall_s": round(wall, 4),
-        "kernel_us": kern_us,
-        "roofline": roofline,
+        "long_prefill": long_leg,
+        "unique_weight_bytes_per_step": fields["unique_weight_bytes_per_step"],
+        "cache_flush_between_steps": fields["cache_flush_between_steps"],
+        "wall_s": fields["wall_s"],
+        "kernel_us": fields["kernel_us"],
+        "roofline": fields["roofline"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -36,7 +36,7 @@ __all__ = [
     "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "moe_dense_workspace_bytes",
     "dense_workspace", "SharedExpert", "moe_zero_rows",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
-    "moe_layer_decode", "UNION_MAX_ROWS", "source_sha256",
+    "moe_layer_decode", "UNION_MAX_ROWS", "source_sha256", "moe_hbm_read_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -48,7 +48,7 @@ EXPORTS = (
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
     "moe_dense_workspace_bytes", "moe_zero_rows", "moe_row_union", "moe_w4a16_gemv_union",
-    "moe_w4a16_gemv_union_swiglu",
+    "moe_w4a16_gemv_union_swiglu", "moe_hbm_read_probe",
 )
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
@@ -85,6 +85,7 @@ _SIGNATURES = {
         [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _i64, _vp],
         ctypes.c_int),
     "moe_dense_workspace_bytes": ([_i32, _i32, _i32, _i32], _i64),
+    "moe_hbm_read_probe": ([_vp, _i64, _vp, _i32, _i32, _vp], ctypes.c_int),
     "moe_zero_rows": ([_vp, _i64, _i32, _i32, _vp], ctypes.c_int),
     "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_w4a16_gemv_union": (
@@ -409,6 +410,23 @@ def moe_w4a16_dequant_bf16(packed, scales, scale2: float, out, stream=None) -> N
         raise ValueError("shape mismatch")
     _check("moe_w4a16_dequant_bf16", load().moe_w4a16_dequant_bf16(
         _p(packed), _p(scales), float(scale2), _p(out), n, k, _stream(stream)))
+
+
+def moe_hbm_read_probe(buf, sink, blocks: int = 2048, unroll: int = 8, stream=None) -> None:
+    """Diagnostic: stream every byte of the contiguous device tensor ``buf`` (a read-only
+    HBM ceiling probe, or a cache-evicting stream); ``sink`` is a uint32 device tensor of
+    at least ``blocks`` elements that the loads feed."""
+    import torch
+
+    if sink.dtype not in (torch.int32, torch.uint32) or not sink.is_cuda:
+        raise TypeError("sink: expected an int32 or uint32 device tensor")
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_contiguous():
+        raise ValueError("buf and sink must be contiguous device tensors")
+    if sink.numel() < blocks:
+        raise ValueError("sink needs one element per block")
+    nbytes = buf.numel() * buf.element_size()
+    _check("moe_hbm_read_probe", load().moe_hbm_read_probe(
+        _p(buf), nbytes, _p(sink), int(blocks), int(unroll), _stream(stream)))
 
 
 def moe_zero_rows(c, stream=None) -> None:

@@ -344,6 +344,22 @@ int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda, const uint16_t
 int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales, float scale2,
                            uint16_t *out, int32_t n, int32_t k, void *stream);
 
+/*
+ * moe_hbm_read_probe - diagnostic: stream `bytes` of device memory at `buf` and do nothing
+ * else. It measures the practical HBM read ceiling that the weight-streaming kernels are
+ * judged against ([FPG] "What this replaces" judges a kernel by its own DRAM roofline),
+ * and a run over a buffer several times the last-level cache evicts that cache between
+ * timed iterations. Each wave reads 1 KB per instruction with `unroll` instructions in
+ * flight; `blocks` workgroups of 256 threads stride over the buffer.
+ *
+ *   buf   device, 16-byte aligned, `bytes` readable (contents are irrelevant)
+ *   sink  device uint32 [blocks]: overwritten with meaningless values (the loads feed it)
+ * Requirements (else MOE_EINVAL): non-NULL pointers, bytes > 0 and % 16 == 0,
+ * 1 <= blocks <= 2^20, unroll in {4, 8, 16}.
+ */
+int moe_hbm_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int32_t blocks,
+                       int32_t unroll, void *stream);
+
 /* Limits of the decode / verify path. */
 #define MOE_UNION_MAX_IDS 1024 /* rows * top_k of moe_row_union (one workgroup) */
 #define MOE_UNION_MAX_ROWS 16  /* rows of moe_w4a16_gemv_union (one matrix-core tile) */
