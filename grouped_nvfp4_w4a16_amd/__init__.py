@@ -115,6 +115,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m grouped_nvfp4_w4a16_amd.build`")
+    # torch's HIP runtime first: the library then binds to the one torch uses instead of
+    # loading a second runtime into the process.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     for name, (args, res) in _SIGNATURES.items():
         fn = getattr(lib, name)

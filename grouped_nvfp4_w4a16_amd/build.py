@@ -52,6 +52,19 @@ def source_sha256() -> str:
     return h.hexdigest()
 
 
+def built_source_sha256(path: str = LIB_PATH) -> str | None:
+    """The source hash a built library carries, read from the file's bytes (the library is
+    not loaded: a process must load its HIP runtime through torch first). None if absent."""
+    import re
+
+    try:
+        data = open(path, "rb").read()
+    except OSError:
+        return None
+    m = re.search(rb"moe_w4a16_source_sha256=([0-9a-f]{64})", data)
+    return m.group(1).decode() if m else None
+
+
 def command(out_path: str) -> list[str]:
     return [
         hipcc(),

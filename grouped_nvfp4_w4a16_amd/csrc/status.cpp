@@ -35,4 +35,9 @@ extern "C" const char *moe_w4a16_last_error(void) { return moe::g_last_error; }
 #define MOE_W4A16_SOURCE_SHA256 "unknown"
 #endif
 
-extern "C" const char *moe_w4a16_source_sha256(void) { return MOE_W4A16_SOURCE_SHA256; }
+// The tag lets a reader find the hash in the file without loading the library.
+static const char g_source_tag[] = "moe_w4a16_source_sha256=" MOE_W4A16_SOURCE_SHA256;
+
+extern "C" const char *moe_w4a16_source_sha256(void) {
+  return g_source_tag + sizeof("moe_w4a16_source_sha256=") - 1;
+}

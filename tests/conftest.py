@@ -9,18 +9,15 @@ if ROOT not in sys.path:
 
 
 def pytest_report_header(config):
-    """Names the library the run loads and the sources it was built from: load() refuses a
-    library whose compiled-in source hash differs from the sources on disk."""
-    from grouped_nvfp4_w4a16_amd import LIB_PATH, build
+    """Names the sources the library was built from (read from the file, not loaded: torch
+    must load its HIP runtime first). load() refuses a library whose compiled-in source
+    hash differs from the sources on disk."""
+    from grouped_nvfp4_w4a16_amd import build
 
     on_disk = build.source_sha256()
-    if not os.path.exists(LIB_PATH):
+    built = build.built_source_sha256()
+    if built is None:
         return f"libmoe_w4a16.so: not built (sources {on_disk[:16]})"
-    import ctypes
-
-    lib = ctypes.CDLL(LIB_PATH)
-    lib.moe_w4a16_source_sha256.restype = ctypes.c_char_p
-    built = lib.moe_w4a16_source_sha256().decode()
     state = "matches the sources on disk" if built == on_disk else "STALE: differs from the sources"
     return f"libmoe_w4a16.so: built from sources {built[:16]} ({state})"
 

@@ -52,6 +52,7 @@ def test_library_was_built_from_these_sources(lib):
     """The source hash compiled into the library is the hash of the sources on disk, and
     load() refuses a library whose hash differs."""
     assert lib.moe_w4a16_source_sha256().decode() == builder.source_sha256()
+    assert builder.built_source_sha256() == builder.source_sha256()
     assert len(builder.source_sha256()) == 64
     names = [os.path.relpath(p, ROOT) for p in builder.hashed_files()]
     assert "include/moe_w4a16.h" in names
