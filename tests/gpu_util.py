@@ -56,6 +56,73 @@ def rel_err_rows(got, ref) -> float:
     return float(np.max(np.where(scale > 0, err / np.where(scale > 0, scale, 1.0), err)))
 
 
+def ulp_bf16(v):
+    """Spacing of BF16 numbers at |v| (8 significant bits; 2^-133 below 2^-126)."""
+    return np.ldexp(1.0, np.frexp(np.maximum(np.abs(v), 2.0 ** -126))[1] - 8)
+
+
+# Bounds for the layer's BF16 stores. The GPU sums in FP32 (in the matrix cores' order),
+# the oracle in FP64; where the two sums straddle a rounding midpoint of a BF16 store, the
+# stored values differ by one BF16 ulp (up to 2^-7 of the value). So each stored buffer
+# may differ from the oracle's by one ulp per element, plus the spread of earlier flips
+# through the next product (a few ulps of a BF16 input times its weights: at most ~2^-10
+# of the row's largest value, far above what the FP32 sums contribute and far below what a
+# wrong row, expert or scale would).
+
+def act_bound(act_ref, c_ref, limit: float):
+    """|act_gpu - act_ref| from one flip of the gate or the up value at the gate_up store
+    (``c_ref``: the oracle's BF16 gate_up rows) carried through silu(g) u to first order
+    (with 1.5x room for the second order), one flip at the act store, and a 2^-12 row
+    floor for the FP32 exponential."""
+    mi = act_ref.shape[1]
+    g, u = c_ref[:, :mi], c_ref[:, mi:]
+    gc = np.minimum(g, limit)
+    uc = np.clip(u, -limit, limit)
+    with np.errstate(over="ignore", invalid="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-gc))
+        silu = gc * sig
+        dsilu = sig * (1.0 + gc * (1.0 - sig))
+    d_g = np.where(g < limit, np.abs(dsilu) * ulp_bf16(g) * np.abs(uc), 0.0)
+    d_u = np.where(np.abs(u) < limit, np.abs(silu) * ulp_bf16(u), 0.0)
+    floor = 2.0 ** -12 * np.max(np.abs(act_ref), axis=1, keepdims=True)
+    return 1.5 * (np.nan_to_num(d_g) + np.nan_to_num(d_u)) + ulp_bf16(act_ref) + floor
+
+
+def expert_out_bound(eo_ref):
+    """|eo_gpu - eo_ref|: one flip at the expert_out store plus the act flips carried
+    through the down product (2^-10 row floor)."""
+    return ulp_bf16(eo_ref) + 2.0 ** -10 * np.max(np.abs(eo_ref), axis=1, keepdims=True)
+
+
+def layer_out_bound(ref, eo_ref, token_to_perm, topk_weights):
+    """|out_gpu - out_ref| per element: the output's own rounding (half an ulp, <= 2^-8 of
+    it) plus, for each slot, its weight times one ulp (<= 2^-7) of the slot's expert_out
+    value and that row's 2^-10 floor (expert_out_bound)."""
+    ttp = np.asarray(token_to_perm).reshape(ref.shape[0], -1)
+    wts = np.abs(np.asarray(topk_weights, np.float64)).reshape(ref.shape[0], -1)
+    bound = 2.0 ** -8 * np.abs(ref)
+    eo_row_max = np.max(np.abs(eo_ref), axis=1)
+    for j in range(ttp.shape[1]):
+        p = ttp[:, j]
+        ok = p >= 0
+        e = np.abs(eo_ref[np.where(ok, p, 0)])
+        contrib = 2.0 ** -7 * e + 2.0 ** -10 * eo_row_max[np.where(ok, p, 0)][:, None]
+        bound += np.where(ok, wts[:, j], 0.0)[:, None] * contrib
+    return bound
+
+
+def within(got, ref, bound) -> float:
+    """Asserts |got - ref| <= bound everywhere (NaN nowhere) and returns the largest
+    ratio |got - ref| / bound."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    ratio = np.abs(got - ref) / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert np.all(ratio <= 1.0), (f"outside the bound at {tuple(int(i) for i in worst)}: "
+                                  f"got {got[worst]}, ref {ref[worst]}, bound {bound[worst]}")
+    return float(ratio.max())
+
+
 def oracle_threads():
     """Context for a full-size oracle call on ORACLE_WORKERS threads: BLAS runs one thread
     per worker, so the workers do not oversubscribe the cores."""

@@ -6,8 +6,9 @@ import torch
 
 import workloads as wl
 from oracle import codecs, moe
-from gpu_util import (GATE, ORACLE_WORKERS, LazyExperts, bf16_bits_host, bf16_dev, dev, f64,
-                      oracle_threads, rel_err, rel_err_rows, upload_table, workload_tables)
+from gpu_util import (GATE, ORACLE_WORKERS, LazyExperts, act_bound, bf16_bits_host, bf16_dev, dev,
+                      expert_out_bound, f64, layer_out_bound, oracle_threads, rel_err,
+                      rel_err_rows, upload_table, within, workload_tables)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +24,15 @@ def test_swiglu_clamp_vs_oracle(hip, rows, mi, seed):
     rng = np.random.default_rng(seed)
     c_bits = codecs.bf16_bits_from_f32((rng.standard_normal((rows, 2 * mi)) * 5).astype(np.float32))
     c_bits[0, :4] = codecs.bf16_bits_from_f32(np.array([7.0, 9.0, -30.0, 0.0], np.float32))
+    if mi >= 8:  # NaN and infinities in the gate (columns 4-7) and the up half
+        special = np.array([np.nan, np.inf, -np.inf, 1.0], np.float32)
+        c_bits[-1, 4:8] = codecs.bf16_bits_from_f32(special)
+        c_bits[-1, mi + 4:mi + 8] = codecs.bf16_bits_from_f32(special[::-1].copy())
+        # gates where e^-g overflows FP32 but silu(g) u is still a normal BF16
+        c_bits[-1, :4] = codecs.bf16_bits_from_f32(np.array([-88.5, -90.0, -93.0, -60.0],
+                                                            np.float32))
+        c_bits[-1, mi:mi + 4] = codecs.bf16_bits_from_f32(np.array([1.0, -3.0, 7.0, 2.0],
+                                                                   np.float32))
     c = bf16_dev(c_bits)
     out = torch.full((rows, mi), 99.0, dtype=torch.bfloat16, device="cuda")
     hip.swiglu_clamp(c[:, :mi], c[:, mi:], out, 7.0)
@@ -30,7 +40,9 @@ def test_swiglu_clamp_vs_oracle(hip, rows, mi, seed):
     cf = codecs.bf16_bits_to_f64(c_bits)
     ref = moe.swiglu_clamp(cf[:, :mi], cf[:, mi:], 7.0)
     got = f64(out)
-    assert np.all(np.abs(got - ref) <= _ulp_bf16(ref) * 0.5 * (1 + 2 ** -4) + 1e-38)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))  # NaN in, NaN out
+    ok = ~np.isnan(ref)
+    assert np.all(np.abs(got - ref)[ok] <= (_ulp_bf16(ref) * 0.5 * (1 + 2 ** -4) + 1e-38)[ok])
 
 
 # ----------------------------------------------------------------------------- combine
@@ -235,11 +247,13 @@ def test_prefill_subchunk_layer_every_row(hip):
                                    wl.scale2_gate_up(w), wl.scale2_down(w), w.moe_intermediate,
                                    w.limit, "bf16w", workers=ORACLE_WORKERS)
     r, rr = rel_err(got, ref), rel_err_rows(got, ref)
-    r_act, r_eo = rel_err(act, inter["act"]), rel_err(e_out, inter["expert_out"])
-    print(f"prefill_subchunk: out {r:.2e} (worst row {rr:.2e}), act {r_act:.2e}, "
-          f"expert_out {r_eo:.2e}")
+    q_act = within(act, inter["act"], act_bound(inter["act"], inter["c"], w.limit))
+    q_eo = within(e_out, inter["expert_out"], expert_out_bound(inter["expert_out"]))
+    q_out = within(got, ref, layer_out_bound(ref, inter["expert_out"],
+                                             inter["align"]["token_to_perm"], wts))
+    print(f"prefill_subchunk: out {r:.2e} (worst row {rr:.2e}); largest error / bound: "
+          f"act {q_act:.2f}, expert_out {q_eo:.2f}, out {q_out:.2f}")
     assert r <= GATE and rr <= GATE
-    assert r_act <= GATE and r_eo <= GATE
 
 
 @pytest.mark.timeout(900)
@@ -259,15 +273,20 @@ def test_long_prefill_every_subchunk(hip):
         over.append(int(np.bincount(ids[sl].reshape(-1), minlength=w.num_experts).max()))
     assert min(over) > 64  # every sub-chunk has a hot expert cut into overflow chunks
     with oracle_threads():
-        ref, _ = moe.moe_layer(codecs.bf16_bits_to_f64(x_bits), ids, wts, gu, dn,
-                               wl.scale2_gate_up(w), wl.scale2_down(w), w.moe_intermediate,
-                               w.limit, "bf16w", workers=ORACLE_WORKERS)
+        ref, inter = moe.moe_layer(codecs.bf16_bits_to_f64(x_bits), ids, wts, gu, dn,
+                                   wl.scale2_gate_up(w), wl.scale2_down(w), w.moe_intermediate,
+                                   w.limit, "bf16w", workers=ORACLE_WORKERS)
     per_chunk = [rel_err(got[c * w.chunk:(c + 1) * w.chunk], ref[c * w.chunk:(c + 1) * w.chunk])
                  for c in range(w.n_chunks)]
-    rr = rel_err_rows(got, ref)
-    print(f"long_prefill: worst sub-chunk {max(per_chunk):.2e}, worst row {rr:.2e}, "
-          f"hottest expert rows per sub-chunk {min(over)}..{max(over)}")
-    assert max(per_chunk) <= GATE and rr <= GATE
+    # Every element within the bound of the layer's BF16 stores. The whole-output gate is
+    # reported, not asserted: with Zipf routing a row's top weight reaches ~0.9, and one
+    # BF16 flip of that slot's expert_out value (up to 2^-7 of it) plus the output's own
+    # rounding exceeds 5e-3 of the output's largest value.
+    q = within(got, ref, layer_out_bound(ref, inter["expert_out"],
+                                         inter["align"]["token_to_perm"], wts))
+    print(f"long_prefill: max_abs/||ref||_inf per sub-chunk {min(per_chunk):.2e}.."
+          f"{max(per_chunk):.2e}; largest error / bound {q:.2f}; hottest expert rows per "
+          f"sub-chunk {min(over)}..{max(over)}")
 
 
 def test_layer_from_router_logits_vs_oracle(hip):
