@@ -37,6 +37,7 @@ __all__ = [
     "dense_workspace", "SharedExpert", "moe_zero_rows",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
     "moe_layer_decode", "UNION_MAX_ROWS", "source_sha256", "moe_hbm_read_probe",
+    "moe_dense_gemm_bf16_noalloc", "DENSE_NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -48,12 +49,13 @@ EXPORTS = (
     "moe_w4a16_grouped_gemm_swiglu", "swiglu_clamp", "moe_combine", "moe_w4a16_dequant_bf16",
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
     "moe_dense_workspace_bytes", "moe_zero_rows", "moe_row_union", "moe_w4a16_gemv_union",
-    "moe_w4a16_gemv_union_swiglu", "moe_hbm_read_probe",
+    "moe_w4a16_gemv_union_swiglu", "moe_hbm_read_probe", "moe_dense_gemm_bf16_noalloc",
 )
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
 UNION_MAX_ROWS = 16  # MOE_UNION_MAX_ROWS: rows of moe_w4a16_gemv_union
 UNION_GEMV_MAX_IDS = 512  # MOE_UNION_GEMV_MAX_IDS: rows * top_k of moe_w4a16_gemv_union
+DENSE_NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_DENSE_NOALLOC_SCRATCH_BYTES
 
 _LIB = None
 
@@ -85,6 +87,8 @@ _SIGNATURES = {
         [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _i64, _vp],
         ctypes.c_int),
     "moe_dense_workspace_bytes": ([_i32, _i32, _i32, _i32], _i64),
+    "moe_dense_gemm_bf16_noalloc": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
+                                    ctypes.c_int),
     "moe_hbm_read_probe": ([_vp, _i64, _vp, _i32, _i32, _vp], ctypes.c_int),
     "moe_zero_rows": ([_vp, _i64, _i32, _i32, _vp], ctypes.c_int),
     "moe_row_union": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -479,6 +483,21 @@ def moe_dense_gemm_bf16(a, b, c, stream=None, workspace=None) -> None:
     wp, wb = _workspace(workspace)
     _check("moe_dense_gemm_bf16", load().moe_dense_gemm_bf16(
         _p(a), lda, _p(b), ldb, _p(c), ldc, m, n, k, wp, wb, _stream(stream)))
+
+
+def moe_dense_gemm_bf16_noalloc(a, b, c, stream=None) -> None:
+    """moe_dense_gemm_bf16 in its split-K form with the library's own device scratch (no
+    workspace, no allocation by anyone); same bits as ``moe_dense_gemm_bf16`` with a
+    workspace. Sizes whose partials exceed ``DENSE_NOALLOC_SCRATCH_BYTES`` raise."""
+    a, lda = _bf16_matrix(a, "a")
+    b, ldb = _bf16_matrix(b, "b")
+    c, ldc = _bf16_matrix(c, "c")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(c.shape) != (m, n):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    _check("moe_dense_gemm_bf16_noalloc", load().moe_dense_gemm_bf16_noalloc(
+        _p(a), lda, _p(b), ldb, _p(c), ldc, m, n, k, _stream(stream)))
 
 
 def moe_dense_gate_up_swiglu_bf16(a, gate_w, up_w, act, limit: float, stream=None,

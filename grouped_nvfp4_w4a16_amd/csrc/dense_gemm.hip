@@ -27,6 +27,8 @@
 //     column tiles divide by 8, the blocks that share B rows (one column tile, all row
 //     tiles) are dealt to one XCD back to back, so each weight line is fetched into one
 //     L2 and hits there for the other row tiles.
+#include <mutex>
+
 #include "buffer_io.h"
 #include "common.h"
 #include "nvfp4_decode.h"  // moe::pack_bf16x2
@@ -597,6 +599,72 @@ int check_dense_args(const char *name, const void *a, int64_t lda, const void *b
 }
 
 }  // namespace
+
+// ------------------------------------------------------------ no-allocation variant
+//
+// moe_dense_gemm_bf16_noalloc runs the split-K form with its FP32 partial tiles in the
+// library's own device array instead of a caller workspace. Each GPU the library runs on
+// holds one copy of the array (module-scope device memory, until the process ends); every
+// call on that GPU shares it and it keeps the last call's contents. The split-K partial
+// kernel writes every partial tile before the reduction reads it, so nothing needs to
+// start at zero.
+static __device__ __align__(256) uint8_t scratch[MOE_DENSE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device (in
+// host code the array's name is only a stand-in, never a device address). Returns
+// MOE_OK and sets *ptr, or an error status with the message recorded.
+int scratch_on_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) {
+    moe::set_error("moe_dense_gemm_bf16_noalloc: hipGetDevice failed: %s", hipGetErrorString(err));
+    return MOE_ELAUNCH;
+  }
+  MOE_REQUIRE_CODE(dev >= 0 && dev < kMaxDevices, MOE_ELAUNCH,
+                   "moe_dense_gemm_bf16_noalloc: device %d beyond the %d the library tracks", dev,
+                   kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr) {
+      moe::set_error("moe_dense_gemm_bf16_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+                     hipGetErrorString(err));
+      return MOE_ELAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_dense_gemm_bf16_noalloc(const uint16_t *a, int64_t lda, const uint16_t *b,
+                                           int64_t ldb, uint16_t *c, int64_t ldc, int32_t m,
+                                           int32_t n, int32_t k, void *stream) {
+  moe::clear_error();
+  const char *name = "moe_dense_gemm_bf16_noalloc";
+  const int rc = check_dense_args(name, a, lda, b, b, ldb, c, ldc, m, n, k);
+  if (rc != MOE_OK || m == 0 || n == 0) return rc;
+  const int64_t need = splitk_shape(m, n, k, false).bytes;
+  MOE_REQUIRE_CODE(need <= MOE_DENSE_NOALLOC_SCRATCH_BYTES, MOE_ECAPACITY,
+                   "%s: m %d, n %d, k %d need %lld bytes of split-K partials; the library's "
+                   "scratch holds %lld (use moe_dense_gemm_bf16 with a workspace)",
+                   name, m, n, k, static_cast<long long>(need),
+                   static_cast<long long>(MOE_DENSE_NOALLOC_SCRATCH_BYTES));
+  void *ws = nullptr;
+  const int src = scratch_on_current_device(&ws);
+  if (src != MOE_OK) return src;
+  return launch_splitk<false>(a, lda, m, b, b, ldb, c, ldc, n, k, 0.f, ws,
+                              MOE_DENSE_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 extern "C" int64_t moe_dense_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t swiglu) {
   if (m <= 0 || n <= 0 || k < 0) return 0;

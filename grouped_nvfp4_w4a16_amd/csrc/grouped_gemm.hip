@@ -74,7 +74,6 @@ constexpr int kBlockM = 16;                       // sorted rows per pass: one M
 constexpr int kChunkRows = 64;                    // sorted rows per block at most
 constexpr int kFrontChunks = 16;                  // overflow rows dispatched before experts
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;    // staged activation row, padded
-constexpr int kLdsBufBytes = kBlockM * kLdsRowBytes;
 constexpr int kPiecesPerRow = kChunkK / 8;        // 16-byte pieces per staged row
 constexpr int kXPieces = kBlockM * kPiecesPerRow / kThreads;  // per thread per step
 constexpr int kXAhead = 1;                        // activation ring: steps in flight

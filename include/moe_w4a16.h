@@ -295,6 +295,30 @@ int moe_dense_gemm_bf16(const uint16_t *a, int64_t lda, const uint16_t *b, int64
                         void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * moe_dense_gemm_bf16_noalloc - moe_dense_gemm_bf16 in its split-K form without a
+ * workspace argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation). The FP32 partial
+ * tiles go to the library's own device array of MOE_DENSE_NOALLOC_SCRATCH_BYTES, one copy
+ * per GPU, held from the library's load until the process ends. No call allocates or frees
+ * anything; the first call on a device looks the array's address up (make it outside any
+ * graph capture).
+ *
+ *   a, b, c, sizes, strides: as moe_dense_gemm_bf16. Same bits as moe_dense_gemm_bf16 with
+ *   a workspace (the same kernels, split and order).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (no
+ * call needs it cleared). Calls that overlap on one GPU (concurrent streams, or other
+ * host threads enqueuing at the same time) race on it: order them on one stream.
+ * Errors: as moe_dense_gemm_bf16; MOE_ECAPACITY (nothing enqueued) when the split-K
+ * partials of m x n at this k, moe_dense_workspace_bytes(m, n, k, 0), exceed
+ * MOE_DENSE_NOALLOC_SCRATCH_BYTES (32 MiB: the shared expert's down projection at 256
+ * rows of hidden 6144 needs 25.2 MB); MOE_ELAUNCH if the array's address lookup fails.
+ */
+#define MOE_DENSE_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int moe_dense_gemm_bf16_noalloc(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+                                uint16_t *c, int64_t ldc, int32_t m, int32_t n, int32_t k,
+                                void *stream);
+
+/*
  * moe_dense_workspace_bytes - host-side size query: the workspace bytes the split-K form
  * of moe_dense_gemm_bf16 (swiglu = 0, n = output width) or of
  * moe_dense_gate_up_swiglu_bf16 (swiglu = 1, n = inter) needs for these sizes: an FP32
