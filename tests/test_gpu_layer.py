@@ -307,3 +307,27 @@ def test_layer_from_router_logits_vs_oracle(hip):
     ref = _oracle_rows(w, ids, wts, x_bits, gu, dn, "bf16w")
     assert np.array_equal(ws.topk_ids.cpu().numpy(), ids)
     assert rel_err(f64(out), ref) <= GATE
+
+
+def test_hbm_read_probe_streams_every_byte(hip):
+    """The bench's HBM ceiling probe and cache-evicting stream: every launch shape reads
+    the whole buffer (the per-block XOR folds of a buffer of ones are the XOR of an even or
+    odd count of ones per word, so they depend on how many words each block saw)."""
+    nbytes = 1 << 22
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32)[::4].fill_(1)  # the first word of every 16-byte piece is 1
+    for blocks, unroll in ((8, 4), (64, 8), (1024, 16), (3, 8)):
+        sink = torch.full((blocks,), -5, dtype=torch.int32, device="cuda")
+        hip.moe_hbm_read_probe(buf, sink, blocks, unroll)
+        torch.cuda.synchronize()
+        # block b reads pieces b*256*U + t + u*256 (+ stride multiples): count them per block
+        n16 = nbytes // 16
+        want = []
+        for b in range(blocks):
+            cnt = 0
+            for base in range(b * 256 * unroll, n16, blocks * 256 * unroll):
+                cnt += min(256 * unroll, n16 - base)
+            want.append(cnt & 1)
+        assert sink.cpu().numpy().tolist() == want, (blocks, unroll)
+    with pytest.raises(hip.MoeError):
+        hip.moe_hbm_read_probe(buf, torch.zeros(8, dtype=torch.int32, device="cuda"), 8, 5)

@@ -107,6 +107,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
                                    _bad(), need - 1, n) == 2
     assert lib.moe_dense_gemm_bf16(_bad(), 1024, _bad(), 1024, _bad(), 128, 64, 128, 1024,
                                    _bad(0x1010), need, n) == 1
+    # no-allocation dense GEMM: partials beyond the library's scratch (capacity), bad n
+    big = lib.moe_dense_workspace_bytes(1024, 8320, 4096, 0)
+    assert big > (32 << 20)
+    assert lib.moe_dense_gemm_bf16_noalloc(_bad(), 4096, _bad(), 4096, _bad(), 8320, 1024, 8320,
+                                           4096, n) == 2
+    assert b"scratch" in lib.moe_w4a16_last_error()
+    assert lib.moe_dense_gemm_bf16_noalloc(_bad(), 1024, _bad(), 1024, _bad(), 128, 64, 120,
+                                           1024, n) == 1
+    # HBM read probe: NULL buffer, bytes not a multiple of 16, misaligned, bad unroll
+    assert lib.moe_hbm_read_probe(n, 1024, _bad(), 8, 8, n) == 1
+    assert lib.moe_hbm_read_probe(_bad(), 1000, _bad(), 8, 8, n) == 1
+    assert lib.moe_hbm_read_probe(_bad(0x1008), 1024, _bad(), 8, 8, n) == 1
+    assert lib.moe_hbm_read_probe(_bad(), 1024, _bad(), 8, 5, n) == 1
+    assert b"unroll" in lib.moe_w4a16_last_error()
 
 
 def _splitk_bytes(m, n, k, swiglu):
