@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_kernel(
 // shapes).
 //   1. Partial GEMM. 4 waves as 2 x 2, each owning 64 A rows x 64 B rows (16 MFMA tiles,
 //      64 accumulator VGPRs). A and B tiles of 64 k are staged in LDS, double buffered,
-//      one barrier per step; the global loads run two steps ahead in registers. LDS rows
+//      one barrier per step; the global loads run three steps ahead in registers. LDS rows
 //      are 128 bytes with the 16-byte pieces XOR-swizzled by the row (piece c of row r
 //      at c ^ (r & 7)), so the 16 rows x 4 pieces an MFMA operand read touches fall in
 //      distinct banks. Each block writes its FP32 partial tile to the workspace in
@@ -269,16 +269,21 @@ constexpr int kLMaxWays = 4;
 static_assert(kLPieces == 4, "four pieces of each operand per thread and step");
 
 // Split count for K: the largest power of two up to 4, and up to 8 / (row tiles), that
-// divides the 64-k steps evenly and leaves each split at least 8 of them. (At the shared
-// expert's gate/up, 8 ways gave two blocks per CU but twice the partial-tile bytes: no
-// faster; 16 ways was slower. With many row tiles the tiles alone fill the chip and each
-// split only adds partial-tile bytes.) It depends on m and k, not n, so the gate/up form
-// and the plain GEMM of the same rows split alike.
+// divides the 64-k steps evenly and leaves each split at least 8 steps per row tile.
+// Every split adds M x N FP32 partials that are written at the block's end and read back
+// by the reduction, and at the shared expert's shapes those bytes cost about as much as
+// the weights (the writes run at ~2.5 TB/s, all blocks at once after their last step).
+// With more row tiles there are more blocks per split, so fewer splits fill the chip: at
+// 256 rows the gate/up GEMM (K = 6144) splits 4 ways (256 blocks) and the down GEMM
+// (K = 2048) 2 ways (192 blocks; 4 ways filled the chip but doubled the partials and was
+// 2.7 us slower); at 128 rows the down GEMM keeps 4 ways. 8 ways at the gate/up gave two
+// blocks per CU but twice the partial bytes: no faster. It depends on m and k, not n, so
+// the gate/up form and the plain GEMM of the same rows split alike.
 int splitk_ways(int32_t m, int32_t k) {
   const int steps = k / kLK;
   const int row_tiles = (m + kLT - 1) / kLT;
   for (int s = kLMaxWays; s > 1; s /= 2)
-    if (s * row_tiles <= 8 && steps % s == 0 && steps / s >= 8) return s;
+    if (s * row_tiles <= 8 && steps % s == 0 && steps / s >= 8 * row_tiles) return s;
   return 1;
 }
 
@@ -343,15 +348,18 @@ __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
   const __amdgpu_buffer_rsrc_t br1 =
       kSwiglu ? make_rsrc(b1 + static_cast<int64_t>(n0) * ldb, b_valid) : br0;
 
-  // This thread's staging pieces: piece p = tid + 256 i is row p / 8, 16-byte column p % 8.
+  // This thread's staging pieces: piece p = tid + 256 i is row p / 8, 16-byte column p % 8,
+  // so pieces i < 2 are rows [0, 64) and pieces i >= 2 rows [64, 128): in the gate/up form
+  // the up rows. That split is fixed per i, which keeps each load's buffer resource uniform
+  // across the wave (a per-lane choice would make the compiler loop over the distinct
+  // resources for every load).
+  static_assert(kThreads / 8 * (kLPieces / 2) == kLT / 2, "the up rows are pieces i >= 2");
   uint32_t a_voff[kLPieces], b_voff[kLPieces], st_off[kLPieces];
-  bool b_up[kLPieces];
 #pragma unroll
   for (int i = 0; i < kLPieces; ++i) {
     const int p = tid + kThreads * i, row = p >> 3, col = p & 7;
     a_voff[i] = static_cast<uint32_t>(row) * arow + 16u * col;
     const int brow_i = kSwiglu ? (row & (kLT / 2 - 1)) : row;
-    b_up[i] = kSwiglu && row >= kLT / 2;
     b_voff[i] = static_cast<uint32_t>(brow_i) * brow + 16u * col;
     st_off[i] = static_cast<uint32_t>(row) * kLRowBytes + 16u * (col ^ (row & 7));
   }
@@ -361,14 +369,19 @@ __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
   struct Regs {
     u32x4_t a[kLPieces], b[kLPieces];
   };
-  const auto load_step = [&](Regs &r, int j) {  // j >= steps loads nothing
+  // One operand of step j (A rows, or B rows when b_half); j >= steps loads nothing.
+  const auto load_half = [&](Regs &r, int j, bool b_half) {
     const uint32_t dead = j < steps ? 0u : kNoLoad;
     const uint32_t soff = j < steps ? static_cast<uint32_t>(k_first + j) * kLRowBytes : 0u;
 #pragma unroll
     for (int i = 0; i < kLPieces; ++i) {
-      r.a[i] = load16(ar, a_voff[i] | dead, soff);
-      r.b[i] = load16(b_up[i] ? br1 : br0, b_voff[i] | dead, soff);
+      if (!b_half) r.a[i] = load16(ar, a_voff[i] | dead, soff);
+      else r.b[i] = load16(kSwiglu && i >= kLPieces / 2 ? br1 : br0, b_voff[i] | dead, soff);
     }
+  };
+  const auto load_step = [&](Regs &r, int j) {
+    load_half(r, j, false);
+    load_half(r, j, true);
   };
   const auto stage_step = [&](const Regs &r, int buf) {
     uint8_t *sa = lds + buf * kLStage, *sb = sa + kLOperand;
@@ -385,43 +398,54 @@ __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const auto compute = [&](int buf) {
+  // The products of one 32-k half h of the step in LDS buffer buf.
+  const auto compute_half = [&](int buf, int h) {
     const uint8_t *sa = lds + buf * kLStage, *sb = sa + kLOperand;
+    const int piece = 4 * h + kb;
+    bf16x8_t wf[4], xf[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int piece = 4 * h + kb;
-      bf16x8_t wf[4], xf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int rw = 64 * wn + 16 * t + r16, rx = 64 * wm + 16 * t + r16;
-        wf[t] = *reinterpret_cast<const bf16x8_t *>(sb + rw * kLRowBytes + 16 * (piece ^ (rw & 7)));
-        xf[t] = *reinterpret_cast<const bf16x8_t *>(sa + rx * kLRowBytes + 16 * (piece ^ (rx & 7)));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], xf[mt], acc[mt][nt], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      const int rw = 64 * wn + 16 * t + r16, rx = 64 * wm + 16 * t + r16;
+      wf[t] = *reinterpret_cast<const bf16x8_t *>(sb + rw * kLRowBytes + 16 * (piece ^ (rw & 7)));
+      xf[t] = *reinterpret_cast<const bf16x8_t *>(sa + rx * kLRowBytes + 16 * (piece ^ (rx & 7)));
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], xf[mt], acc[mt][nt], 0, 0, 0);
   };
 
-  // Steps j (LDS buffer j & 1) with the global loads two steps ahead in two register
-  // sets: set j & 1 is free once step j is staged, and takes step j + 2.
-  Regs r0, r1;
-  load_step(r0, 0);
-  load_step(r1, 1);
-  stage_step(r0, 0);
+  // Step s reads LDS buffer s & 1. The global loads run kDepth steps ahead in kDepth
+  // register sets: set s % kDepth holds step s from its load until it is staged (at the
+  // end of step s - 1), then takes step s + kDepth during step s, so staging step s + 1
+  // waits only for loads issued two steps earlier. The refill is split over the step, the
+  // A rows before the first 32-k half of the products and the B rows before the second
+  // (one burst of all eight loads at the top measured 1-2 us slower at the shared
+  // expert's gate/up, and two or four register sets slower than three), and pinned there
+  // with scheduling barriers. The stages are unconditional (past the last step the loads
+  // read nothing and the stage writes zeros to a buffer no step reads): a stage behind a
+  // branch lets the compiler sink the loads into it, next to their wait.
+  constexpr int kDepth = 3, kUnroll = 6;  // kUnroll: a multiple of kDepth and of 2
+  Regs r[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) load_step(r[i], i);
+  stage_step(r[0], 0);
   __syncthreads();
-  for (int j = 0; j < steps; j += 2) {
-    load_step(r0, j + 2);
-    compute(0);
-    if (j + 1 < steps) stage_step(r1, 1);
-    __syncthreads();
-    if (j + 1 >= steps) break;
-    load_step(r1, j + 3);
-    compute(1);
-    if (j + 2 < steps) stage_step(r0, 0);
-    __syncthreads();
+  for (int j = 0; j < steps; j += kUnroll) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = j + u;  // u % kDepth == s % kDepth, u & 1 == s & 1
+      if (s >= steps) break;
+      load_half(r[u % kDepth], s + kDepth, false);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_half(u & 1, 0);
+      load_half(r[u % kDepth], s + kDepth, true);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_half(u & 1, 1);
+      stage_step(r[(u + 1) % kDepth], (u + 1) & 1);
+      __syncthreads();
+    }
   }
 
   // The partial tile in fragment order: [split][tile][wave][mt * 4 + nt][lane].

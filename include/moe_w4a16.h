@@ -323,8 +323,8 @@ int moe_dense_gemm_bf16_noalloc(const uint16_t *a, int64_t lda, const uint16_t *
  * of moe_dense_gemm_bf16 (swiglu = 0, n = output width) or of
  * moe_dense_gate_up_swiglu_bf16 (swiglu = 1, n = inter) needs for these sizes: an FP32
  * partial tile (128 x 128) per 128-row x 128-weight-row tile and K split (K splits 4, 2
- * or 1 ways: the most that divide the 64-k steps evenly with at least 8 per split and at
- * most 8 / ceil(m / 128) ways).
+ * or 1 ways: the most that divide the 64-k steps evenly with at least 8 per split and per
+ * 128-row tile, and at most 8 / ceil(m / 128) ways).
  * Returns 0 when m <= 0, n <= 0 or k < 0. Enqueues nothing.
  */
 int64_t moe_dense_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t swiglu);

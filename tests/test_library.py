@@ -126,11 +126,13 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
 def _splitk_bytes(m, n, k, swiglu):
     """The split-K workspace size from its definition: 128 x 128 FP32 per tile of 128 rows
     x 128 weight rows (64 output columns in the gate/up form) and K split; K splits 4 or
-    2 ways (the most with every split at least 8 steps of 64 k, the steps dividing evenly
-    and at most 8 ways per row tile group: ways * ceil(m / 128) <= 8), else 1."""
+    2 ways (the most with every split at least 8 steps of 64 k per 128-row tile, the steps
+    dividing evenly and at most 8 ways per row tile group: ways * ceil(m / 128) <= 8),
+    else 1."""
     steps = k // 64
     row_tiles = -(-m // 128)
-    ways = next((s for s in (4, 2) if s * row_tiles <= 8 and steps % s == 0 and steps // s >= 8), 1)
+    ways = next((s for s in (4, 2)
+                 if s * row_tiles <= 8 and steps % s == 0 and steps // s >= 8 * row_tiles), 1)
     tiles = row_tiles * -(-n // (64 if swiglu else 128))
     return tiles * ways * 128 * 128 * 4
 
