@@ -139,7 +139,8 @@ def _splitk_bytes(m, n, k, swiglu):
 
 @pytest.mark.parametrize("m,n,k,swiglu", [
     (256, 2048, 6144, 1), (256, 6144, 2048, 0), (1, 16, 64, 0), (130, 272, 1024, 0),
-    (300, 4096, 512, 1), (8, 48, 0, 0), (4096, 16, 2560, 1)])
+    (300, 4096, 512, 1), (8, 48, 0, 0), (4096, 16, 2560, 1), (40, 96, 320, 0),
+    (70, 160, 704, 0)])
 def test_dense_workspace_size_query(lib, m, n, k, swiglu):
     assert lib.moe_dense_workspace_bytes(m, n, k, swiglu) == _splitk_bytes(m, n, k, swiglu)
     assert lib.moe_dense_workspace_bytes(0, n, k, swiglu) == 0
