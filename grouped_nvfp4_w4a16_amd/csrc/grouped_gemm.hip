@@ -102,15 +102,20 @@ struct WeightRegs {
   u32x4_t b[kTiles];  // k in [128 + 32 kb, 128 + 32 kb + 32)
 };
 
-// Loads of a step past the last one get kNoLoad, so every load stays unconditional (see
-// the main loop) without re-reading data that L2 may already have evicted.
+// Loads of a step past the last one get bit 31 set in their offset (past the end of any
+// buffer below 2 GiB: zeros, no traffic), so every load stays unconditional (see the main
+// loop) without re-reading data that L2 may already have evicted. The bit is set
+// arithmetically: written as a select on the (uniform) step count, the compiler turned it
+// into a branch around the loads, and its wait counting then assumed two more loads in
+// flight after the join than there are, so each step's first decode also waited for the
+// activation loads just issued for the next step (1-2 % of the launch).
 __device__ __forceinline__ void load_weights(WeightRegs &w, __amdgpu_buffer_rsrc_t r,
                                              const uint32_t *voff, int step, int n_steps) {
   const uint32_t soff = static_cast<uint32_t>(step) * (kChunkK / 2);
-  const bool live = step < n_steps;
+  const uint32_t dead = static_cast<uint32_t>(step >= n_steps) << 31;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
-    const uint32_t v = live ? voff[t] : kNoLoad;
+    const uint32_t v = voff[t] | dead;
     w.a[t] = load16(r, v, soff);
     w.b[t] = load16(r, v + 64, soff);
   }
