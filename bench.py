@@ -417,15 +417,22 @@ def time_decode_leg(hip, torch, steps, probe):
                for j, (n, _) in enumerate(stages)}
         res[name] = {"step_us": round(step_us, 2), "GBps": round(wbytes / step_us / 1e3, 1),
                      "kernel_us": kus}
-    gu_us = res["union"]["kernel_us"]["gemv_union_gate_up_swiglu"]
-    achieved = gu_alg / gu_us / 1e3
+    def roof(kernel, us):
+        achieved = gu_alg / us / 1e3
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "alg_bytes_per_launch": int(gu_alg), "avg_launch_us": us}
+
+    # The union GEMV is what moe_layer_decode runs; the sorted path's grouped GEMM on the
+    # same rows is reported beside it.
     return {"workload": w.name, "rows": rows, "live_experts": len(live),
             "unique_weight_bytes": int(wbytes),
             "timing": "each step after a 2 GiB cache-evicting read", **res,
-            "roofline": {"kernel": "moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)",
-                         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "alg_bytes_per_launch": int(gu_alg)}}
+            "faster_path": min(res, key=lambda k: res[k]["step_us"]),
+            "roofline": roof("moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)",
+                             res["union"]["kernel_us"]["gemv_union_gate_up_swiglu"]),
+            "roofline_sorted": roof("moe_w4a16_grouped_gemm_swiglu (gate_up + SwiGLU)",
+                                    res["sorted"]["kernel_us"]["grouped_gemm_gate_up_swiglu"])}
 
 
 def measure_workload(hip, torch, w, args, probe, steps: int, warmup: int):

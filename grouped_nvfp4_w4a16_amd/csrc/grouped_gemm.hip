@@ -19,11 +19,9 @@
 //     overflow block of its own, so a hot expert (skewed routing) is spread over several
 //     blocks instead of making one block run many passes while the rest of the chip
 //     idles. Three blocks share a CU.
-//     Workgroups are dealt to the 8 XCDs round-robin by linear id; the block index is
-//     remapped so that each XCD runs whole experts (XCD x: experts x, x + 8, ...), and an
-//     expert's activation rows are fetched into one L2 only (measured L2-to-memory reads
-//     then equal the algorithmic bytes). Interleaving the experts keeps every XCD busy
-//     when a contiguous range of them is absent or idle.
+//     Workgroups are dealt to the 8 XCDs round-robin by linear id, and the grid runs in
+//     its natural order: an expert's weight-row tiles are spread over all eight XCDs, so
+//     every XCD gets the same share of the work however skewed the routing.
 //   - Each wave owns two MFMA tiles of 16 weight rows: block rows [16w, 16w + 16) and
 //     [64 + 16w, 64 + 16w + 16). Both tiles multiply the same activation operands, so a
 //     wave reads each staged activation once per 32 weight rows.
@@ -198,12 +196,14 @@ __global__ __launch_bounds__(kThreads, kMT == 1 ? 3 : 2) void grouped_gemm_kerne
   __shared__ __attribute__((aligned(16))) uint8_t ss[2][kScaleBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut[256 * 16];
 
-  // Workgroups go to the 8 XCDs round-robin by linear id. Remap (a bijection on the
-  // grid) so that each XCD runs whole grid rows, an expert's activation rows then being
-  // fetched into one L2 only; with the row count a multiple of 8, an XCD runs every
-  // eighth row, so a contiguous range of empty or absent experts (an expert-parallel
-  // rank's share, a cold part of the expert range) is spread over all XCDs instead of
-  // idling some.
+  // Workgroups go to the 8 XCDs round-robin by linear id, so in grid order the N tiles
+  // of one grid row (one expert or overflow chunk) are spread over all eight XCDs and
+  // every XCD gets an eighth of every row's work, however the rows are routed. (Giving
+  // each XCD whole rows, so that an expert's activation rows are fetched into one L2
+  // only, left the XCDs up to 14 % apart in work under Zipf(1.1) routing, where a few
+  // experts hold most rows, and made that launch 7 % slower; with uniform routing it
+  // measured the same as grid order. The activation rows are small next to the weights
+  // and come from the last-level cache.)
   //
   // Grid rows [0, num_experts) are the experts with at most chunk_rows rows; rows past
   // them are overflow chunks (the chunk_rows-row pieces of the more heavily routed
@@ -216,20 +216,10 @@ __global__ __launch_bounds__(kThreads, kMT == 1 ? 3 : 2) void grouped_gemm_kerne
   // The room for overflow chunks is a worst-case bound; the rows past the actual chunks
   // exit after one scan of the offsets, and dispatching only a few of them first keeps
   // that cost off the start of a launch whose experts are all light.
-  int e = blockIdx.y, tile = blockIdx.x;
+  const int tile = blockIdx.x;
+  int e = blockIdx.y;
   {
-    const int T = gridDim.x, Y = gridDim.y;
-    const int lin = blockIdx.y * T + blockIdx.x;
-    if ((Y & 7) == 0) {
-      const int q = lin >> 3, el = q / T;
-      tile = q - el * T;
-      e = el * 8 + (lin & 7);
-    } else if (((T * Y) & 7) == 0) {
-      const int r = (lin & 7) * ((T * Y) >> 3) + (lin >> 3);
-      e = r / T;
-      tile = r - e * T;
-    }
-    const int front = min(Y - num_experts, kFrontChunks);
+    const int front = min(static_cast<int>(gridDim.y) - num_experts, kFrontChunks);
     e = e < front ? num_experts + e : (e < front + num_experts ? e - front : e);
   }
   int chunk = 0;
@@ -548,17 +538,15 @@ int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_
 // with r > C = kChunkRows rows has ceil(r / C) <= 2 r / (C + 1) chunks (the left side steps
 // to k + 1 at r = k C + 1, where 2 (k C + 1) >= (k + 1)(C + 1) because (k - 1)(C - 1) >= 0),
 // so all experts together (at most max_rows rows) have at most 2 max_rows / (C + 1), and
-// none when max_rows <= C. The total is rounded up to a multiple of 8 (whole experts per
-// XCD). Where that would pass the grid's row limit, blocks take all of their expert's rows
-// (no overflow chunks).
+// none when max_rows <= C. Where that would pass the grid's row limit, blocks take all of
+// their expert's rows (no overflow chunks).
 int grid_rows(int32_t num_experts, int32_t max_rows, int *chunk_rows) {
   const int64_t chunks =
       max_rows > kChunkRows ? 2 * static_cast<int64_t>(max_rows) / (kChunkRows + 1) : 0;
   const int64_t rows = num_experts + chunks;
-  const int64_t padded = (rows + 7) & ~static_cast<int64_t>(7);
-  if (padded <= 65535) {
+  if (rows <= 65535) {
     *chunk_rows = kChunkRows;
-    return static_cast<int>(padded);
+    return static_cast<int>(rows);
   }
   *chunk_rows = INT32_MAX;
   return num_experts;
