@@ -23,9 +23,14 @@
 //     step ahead in a two-slot register ring, decoded in registers by the exact per-code
 //     byte tables (nvfp4_decode.h, one 256-code LUT per block) straight into A.
 //   - Lane (r16, kb) takes k in [64 kb, 64 kb + 64) of each step, so its four block
-//     scales are one aligned dword of the row's 16 scale bytes, and its activation bytes
-//     are 128 contiguous bytes loaded straight from the input row (no LDS staging: each
-//     wave reads different steps), one step ahead, put in the decoder's k order.
+//     scales are one aligned dword of the row's 16 scale bytes, and its B operand is 128
+//     contiguous bytes of the entry's token r16, put in the decoder's k order. The
+//     activations are loaded one step ahead. With at most 16 rows a launch loads them
+//     straight into the B layout (8 loads per lane and step); with at most 8 rows each
+//     wave stages its step's tokens in a private piece of LDS instead: one 16-byte load
+//     per lane covers two tokens' 512 bytes, so a step takes rows / 2 loads (rounded up
+//     to 1, 2 or 4), and the B operands are read back from LDS. Each wave reads different
+//     steps, so the staging is per wave, with no barrier.
 //   - SwiGLU-fused form: a wave's two tiles are 16 gate rows and the matching 16 up rows,
 //     rounded to BF16 and passed through the clamped SwiGLU in the epilogue (as the grouped
 //     GEMM's fused form).
@@ -34,6 +39,8 @@
 #include "nvfp4_decode.h"
 #include "swiglu.h"
 #include "w4a16_mma.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -191,11 +198,16 @@ static_assert(kThreads == 256, "build_code_table_lut: one E4M3 code per thread")
 // One lane's data of one step: packed weights of its two tiles (k in [64 kb, 64 kb + 32)
 // and [64 kb + 32, 64 kb + 64)), the four block-scale codes of each tile, and its
 // activation row's 64 k in eight 16-byte pieces.
+// kNQ = activation loads per lane and step when staged (two tokens each), 0 = direct.
+template <int kNQ>
 struct StepRegs {
   u32x4_t wa[2], wb[2];
   uint32_t sc[2];
-  u32x4_t x[8];
+  u32x4_t x[kNQ ? kNQ : 8];
 };
+// Staged activations: a token's 256 k of a step (512 bytes), rows padded to 528 bytes so
+// that the 16 lanes of a B read that differ in token start on different banks.
+constexpr int kXsRowBytes = kChunkK * 2 + 16;
 
 // A live union entry (its expert present in the table), as the block's waves read it.
 struct LiveEntry {
@@ -218,6 +230,7 @@ struct Item {
   bool on[2];
   uint32_t x_voff;  // per lane, kNoLoad if the lane has no token
   int32_t dst_row;  // per lane, -1 if the lane has no token
+  uint32_t xq[4];   // staged: offset of this lane's 16 bytes of token 2 q + lane / 32
 };
 
 // The work of a launch is (live entry, group of 32 * kGroups weight rows) items, dealt to
@@ -225,7 +238,7 @@ struct Item {
 // deal is balanced, and a block streams its items back to back: the waves load the next
 // item's first step while computing the current item's last one, and each item's decode
 // table is built during the item before it (double-buffered), so no item pays a start-up.
-template <bool kSwiglu, int kKSplit>
+template <bool kSwiglu, int kKSplit, int kNQ>
 __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
     const uint64_t *__restrict__ packed_ptrs, const uint64_t *__restrict__ scale_ptrs,
@@ -236,6 +249,7 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
   constexpr int kItemRows = kSwiglu ? 16 * kGroups : 32 * kGroups;  // gate rows if fused
   __shared__ __attribute__((aligned(16))) uint8_t lut[2][256 * 16];
   __shared__ __attribute__((aligned(16))) f32x4_t red[2][kWaves][2][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kNQ ? kWaves * 2 * kNQ * kXsRowBytes : 16];
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   __shared__ int32_t n_live_s;
   const int n_ids = rows * top_k;
@@ -324,6 +338,18 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
     m.x_voff = (src >= 0 && src < a_rows)
                    ? (static_cast<uint32_t>(src) * static_cast<uint32_t>(lda) + 64u * kb) * 2u
                    : kNoLoad;
+    if (kNQ) {
+      // Staged: the lane loads bytes [16 (lane % 32), + 16) of each step of token
+      // 2 q + lane / 32 (zeros past the entry's tokens).
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        const int tq = tok[li * 16 + 2 * q + (lane >> 5)];
+        const int sq = tq < 0 ? -1 : (a_per_slot ? tq : tq / top_k);
+        uint32_t row_off = static_cast<uint32_t>(sq) * static_cast<uint32_t>(lda);
+        asm volatile("" : "+v"(row_off));
+        m.xq[q] = (sq >= 0 && sq < a_rows) ? row_off * 2u + 16u * (lane & 31) : kNoLoad;
+      }
+    }
   };
   // The whole Item of it: its entry's buffers (uniform), its rows, this lane's token.
   const auto make_item = [&](int it) {
@@ -333,7 +359,7 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
   };
   // Step i of this wave's share of an item (steps kw, kw + kKSplit, ...); live = false
   // loads nothing, so every load stays unconditional.
-  const auto load_w = [&](StepRegs &st, const Item &m, int i, bool live_step) {
+  const auto load_w = [&](StepRegs<kNQ> &st, const Item &m, int i, bool live_step) {
     const int step = kw + i * kKSplit;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -347,14 +373,19 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
           static_cast<int>(m.s_base[t] + static_cast<uint32_t>(step) * 16u), 0);
     }
   };
-  const auto load_x = [&](StepRegs &st, const Item &m, int i, bool live_step) {
+  const auto load_x = [&](StepRegs<kNQ> &st, const Item &m, int i, bool live_step) {
     const int step = kw + i * kKSplit;
-    const uint32_t xv = live_step ? m.x_voff : kNoLoad;
     const uint32_t xsoff = static_cast<uint32_t>(step) * (kChunkK * 2);
+    if (kNQ) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) st.x[q] = load16(x_rsrc, xv + 16u * q, xsoff);
+      for (int q = 0; q < kNQ; ++q) st.x[q] = load16(x_rsrc, live_step ? m.xq[q] : kNoLoad, xsoff);
+    } else {
+      const uint32_t xv = live_step ? m.x_voff : kNoLoad;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st.x[q] = load16(x_rsrc, xv + 16u * q, xsoff);
+    }
   };
-  const auto load_step = [&](StepRegs &st, const Item &m, int i, bool live_step) {
+  const auto load_step = [&](StepRegs<kNQ> &st, const Item &m, int i, bool live_step) {
     load_w(st, m, i, live_step);
     load_x(st, m, i, live_step);
   };
@@ -373,7 +404,19 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
       blk[g].hi47 = t[3];
     }
   };
-  const auto run_step = [&](const StepRegs &st, const uint8_t *tab, bool t1_on) {
+  // Staged form: this wave's piece of LDS holds the step's 2 kNQ tokens. Lane l writes its
+  // 16 bytes of token 2 q + l / 32 and reads its B operand from token r16; a lane past
+  // the staged tokens (r16 >= 2 kNQ >= rows) has no token and reads token r16 mod 2 kNQ,
+  // a column that is never stored. Writes of a step follow the reads of the step before
+  // in the wave's program order, so one piece per wave suffices.
+  uint8_t *xs_w = xs + wave * (2 * (kNQ ? kNQ : 1) * kXsRowBytes);
+  const int xs_tok = kNQ ? r16 % (2 * (kNQ ? kNQ : 1)) : 0;
+  const auto run_step = [&](const StepRegs<kNQ> &st, const uint8_t *tab, bool t1_on) {
+    if (kNQ) {
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q)
+        *reinterpret_cast<u32x4_t *>(xs_w + (2 * q + (lane >> 5)) * kXsRowBytes + 16 * (lane & 31)) = st.x[q];
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       moe::Fp4Table blk0[2], blk1[2];
@@ -381,7 +424,12 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
       tables_of(st.sc[1], h, tab, blk1);
       bf16x8_t B[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) B[q] = __builtin_bit_cast(bf16x8_t, moe::permute_k8(st.x[4 * h + q]));
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t xv = kNQ ? *reinterpret_cast<const u32x4_t *>(
+                                     xs_w + xs_tok * kXsRowBytes + 128 * kb + 16 * (4 * h + q))
+                               : st.x[(4 * h + q) % (kNQ ? kNQ : 8)];
+        B[q] = __builtin_bit_cast(bf16x8_t, moe::permute_k8(xv));
+      }
       const u32x4_t &x0 = h ? st.wb[0] : st.wa[0];
       const uint32_t w0w[4] = {x0[0], x0[1], x0[2], x0[3]};
       moe::mfma4(w0w, blk0[0], blk0[1], B, acc[0]);
@@ -397,7 +445,7 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
   // entry), its activations after.
   int item = blockIdx.x;
   Item cur = make_item_w(item);
-  StepRegs sA, sB;
+  StepRegs<kNQ> sA, sB;
   load_w(sA, cur, 0, true);
 
   // Each live entry's tokens: its routed rows (u_slot[p, r] >= 0) in order of r, as
@@ -504,8 +552,8 @@ int k_split(int32_t k) {
   return n_steps >= 16 ? 4 : (n_steps >= 8 ? 2 : 1);
 }
 
-template <bool kSwiglu>
-int launch_gemv_union(const char *name, int split, int32_t item_rows, void *stream,
+template <bool kSwiglu, int kNQ>
+int launch_gemv_union_nq(const char *name, int split, int32_t item_rows, void *stream,
                       const uint16_t *a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
                       const uint64_t *packed_ptrs, const uint64_t *scale_ptrs,
                       const float *scale2, const int32_t *u_eid, const int32_t *u_slot,
@@ -522,9 +570,29 @@ int launch_gemv_union(const char *name, int split, int32_t item_rows, void *stre
                        packed_ptrs, scale_ptrs, scale2, u_eid, u_slot, rows, top_k, num_experts,
                        c, ldc, n, k, limit);
   };
-  if (split == 4) return go(gemv_union_kernel<kSwiglu, 4>);
-  if (split == 2) return go(gemv_union_kernel<kSwiglu, 2>);
-  return go(gemv_union_kernel<kSwiglu, 1>);
+  if (split == 4) return go(gemv_union_kernel<kSwiglu, 4, kNQ>);
+  if (split == 2) return go(gemv_union_kernel<kSwiglu, 2, kNQ>);
+  return go(gemv_union_kernel<kSwiglu, 1, kNQ>);
+}
+
+// Activations staged through LDS per wave when a launch has at most 8 rows, loaded
+// straight into the B layout above that.
+template <bool kSwiglu>
+int launch_gemv_union(const char *name, int split, int32_t item_rows, void *stream,
+                      const uint16_t *a, int64_t lda, int32_t a_rows, int32_t a_per_slot,
+                      const uint64_t *packed_ptrs, const uint64_t *scale_ptrs,
+                      const float *scale2, const int32_t *u_eid, const int32_t *u_slot,
+                      int32_t rows, int32_t top_k, int32_t num_experts, uint16_t *c,
+                      int64_t ldc, int32_t n, int32_t k, float limit) {
+  const auto go = [&](auto nq) {
+    return launch_gemv_union_nq<kSwiglu, decltype(nq)::value>(
+        name, split, item_rows, stream, a, lda, a_rows, a_per_slot, packed_ptrs, scale_ptrs,
+        scale2, u_eid, u_slot, rows, top_k, num_experts, c, ldc, n, k, limit);
+  };
+  if (rows <= 2) return go(std::integral_constant<int, 1>{});
+  if (rows <= 4) return go(std::integral_constant<int, 2>{});
+  if (rows <= 8) return go(std::integral_constant<int, 4>{});
+  return go(std::integral_constant<int, 0>{});
 }
 
 int check_union_gemv_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_rows,

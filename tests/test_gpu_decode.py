@@ -159,6 +159,10 @@ def _check(got, ref, bound):
     (3, 4, 9, 48, 6144, False),      # 24 steps: four waves split K; N not a block multiple
     (16, 2, 40, 160, 2304, True),    # 16 rows, 9 steps, ragged groups
     (1, 8, 300, 64, 768, False),     # one row: every entry has one token
+    # at most 8 rows: activations staged per wave in LDS, 2 tokens per load (1, 2, 4 loads)
+    (2, 8, 64, 96, 6144, True),      # one load per step, four waves split K
+    (4, 8, 16, 128, 1024, True),     # two loads per step, no K split
+    (5, 6, 20, 80, 4096, False),     # four loads per step, an odd token count
 ])
 def test_gemv_union_vs_oracle(hip, rows, top_k, num_experts, n, k, per_slot):
     rng, ids, experts, s2 = _problem(rows * 100 + k, rows, top_k, num_experts, n, k,
@@ -301,14 +305,17 @@ def test_decode_layer_matches_sorted_layer_ragged(hip):
     assert rel_err(f64(out), ref) <= GATE
 
 
-def test_gemv_union_row_result_independent_of_sharing(hip):
+@pytest.mark.parametrize("rows,cut", [(8, 3), (12, 4), (16, 2)])
+def test_gemv_union_row_result_independent_of_sharing(hip, rows, cut):
     """Which rows share a sweep never changes what a row gets: the same rows run as one
-    union and split into two unions give the same bits for every (row, slot)."""
-    rng, ids, experts, s2 = _problem(71, 8, 8, 24, 256, 2048)
-    a_bits = wl.bf16_normal(rng, (8, 2048))
+    union and split into two unions give the same bits for every (row, slot). The cuts
+    also cross the launch forms (activations staged in LDS for at most 8 rows, with 1, 2
+    or 4 loads per step; loaded directly above 8)."""
+    rng, ids, experts, s2 = _problem(71 + rows, rows, 8, 24, 256, 2048)
+    a_bits = wl.bf16_normal(rng, (rows, 2048))
     whole, _, _, _ = _gemv_gpu(hip, a_bits, False, experts, s2, ids, 256, 2048)
-    lo, _, _, _ = _gemv_gpu(hip, a_bits[:3], False, experts, s2, ids[:3], 256, 2048)
-    hi, _, _, _ = _gemv_gpu(hip, a_bits[3:], False, experts, s2, ids[3:], 256, 2048)
+    lo, _, _, _ = _gemv_gpu(hip, a_bits[:cut], False, experts, s2, ids[:cut], 256, 2048)
+    hi, _, _, _ = _gemv_gpu(hip, a_bits[cut:], False, experts, s2, ids[cut:], 256, 2048)
     split = np.concatenate([lo, hi])
     assert np.array_equal(np.isnan(whole), np.isnan(split))
     assert np.array_equal(whole, split)
