@@ -723,7 +723,7 @@ def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: Expe
     ``fused=False`` runs the gate_up GEMV and swiglu_clamp as two calls (same bits).
     Slots of experts absent from the down table are left out of the union (the combine
     skips them), so unlike the sorted path no zero-first step is needed. On MI355X the
-    sorted path (``moe_layer``) is faster from about 4 rows on; this path wins below."""
+    sorted path (``moe_layer``) is faster above about 4 rows; this path wins below."""
     _same_experts(gate_up, down)
     rows, top_k = topk_ids.shape
     t = rows * top_k
