@@ -197,8 +197,8 @@ static_assert(kThreads == 256, "build_code_table_lut: one E4M3 code per thread")
 
 // One lane's data of one step: packed weights of its two tiles (k in [64 kb, 64 kb + 32)
 // and [64 kb + 32, 64 kb + 64)), the four block-scale codes of each tile, and its
-// activation row's 64 k in eight 16-byte pieces.
-// kNQ = activation loads per lane and step when staged (two tokens each), 0 = direct.
+// activations: loaded directly (kNQ = 0), its token's 64 k in eight 16-byte pieces;
+// staged, kNQ 16-byte pieces, each of a pair of tokens' step, on their way to LDS.
 template <int kNQ>
 struct StepRegs {
   u32x4_t wa[2], wb[2];
