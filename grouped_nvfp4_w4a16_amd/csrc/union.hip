@@ -192,6 +192,7 @@ constexpr int kChunkK = 256;       // k per step
 constexpr int kMaxRows = 16;       // routed rows a launch may have: one MFMA tile of B
 constexpr int kSlotsPerCu = 3;     // resident blocks per CU (VGPR-limited)
 constexpr int kCus = 256;
+constexpr int64_t kLdsPerCu = 160 * 1024;
 constexpr int kGemvMaxIds = 512;   // rows * top_k: the entries' metadata live in LDS
 static_assert(kThreads == 256, "build_code_table_lut: one E4M3 code per thread");
 
@@ -559,10 +560,16 @@ int launch_gemv_union_nq(const char *name, int split, int32_t item_rows, void *s
                       const float *scale2, const int32_t *u_eid, const int32_t *u_slot,
                       int32_t rows, int32_t top_k, int32_t num_experts, uint16_t *c,
                       int64_t ldc, int32_t n, int32_t k, float limit) {
-  // At most every union entry is live: one block per item up to a full chip of blocks.
+  // At most every union entry is live: one block per item up to a full chip of resident
+  // blocks. Three fit a CU unless the entries' metadata make the LDS the limit (with the
+  // most ids a launch takes, 512, the staged forms fit two).
   const int64_t items =
       static_cast<int64_t>(rows) * top_k * (((kSwiglu ? n / 2 : n) + item_rows - 1) / item_rows);
-  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(items, int64_t{kSlotsPerCu} * kCus)));
+  constexpr int64_t kStaticLds = 2 * 256 * 16 + 2 * kWaves * 2 * 64 * 16 +
+                                 (kNQ ? kWaves * 2 * kNQ * kXsRowBytes : 16) + 64;
+  const int64_t lds = kStaticLds + static_cast<int64_t>(rows) * top_k * kEntryLdsBytes;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kSlotsPerCu, kLdsPerCu / lds));
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(items, per_cu * kCus)));
   const auto go = [&](auto kern) {
     return moe::launch(name, kern, grid, dim3(kThreads),
                        static_cast<size_t>(rows) * top_k * kEntryLdsBytes, stream, a, lda, a_rows,

@@ -163,6 +163,9 @@ def _check(got, ref, bound):
     (2, 8, 64, 96, 6144, True),      # one load per step, four waves split K
     (4, 8, 16, 128, 1024, True),     # two loads per step, no K split
     (5, 6, 20, 80, 4096, False),     # four loads per step, an odd token count
+    # the most ids a launch takes (512 entries' metadata in LDS), staged and direct
+    (8, 64, 600, 32, 512, False),
+    (16, 32, 560, 32, 256, True),
 ])
 def test_gemv_union_vs_oracle(hip, rows, top_k, num_experts, n, k, per_slot):
     rng, ids, experts, s2 = _problem(rows * 100 + k, rows, top_k, num_experts, n, k,
