@@ -322,3 +322,38 @@ def test_gemv_union_row_result_independent_of_sharing(hip, rows, cut):
     split = np.concatenate([lo, hi])
     assert np.array_equal(np.isnan(whole), np.isnan(split))
     assert np.array_equal(whole, split)
+
+
+@pytest.mark.parametrize("rows,a_rows,per_slot", [(6, 4, False), (12, 9, False), (5, 11, True)])
+def test_gemv_union_source_rows_past_a_read_zeros(hip, rows, a_rows, per_slot):
+    """Through the C ABI (the binding refuses a short ``a``): a source row at or past
+    a_rows reads zeros, so its covered outputs are exactly 0 and the others are those of
+    the full problem. Six and five rows take the LDS-staged activations, twelve the
+    direct loads."""
+    import ctypes
+
+    top_k, num_experts, n, k = 4, 10, 64, 512
+    rng, ids, experts, s2 = _problem(300 + rows, rows, top_k, num_experts, n, k)
+    src_rows = rows * top_k if per_slot else rows
+    assert a_rows < src_rows
+    a_bits = wl.bf16_normal(rng, (src_rows, k))
+    a_bits[a_rows:] = 0  # what the kernel must read past a_rows
+    table = upload_table(hip, experts, s2, n, k)
+    u_eid, u_slot, _, _ = _union_gpu(hip, ids, num_experts)
+    a_dev = bf16_dev(np.ascontiguousarray(a_bits[:a_rows]))
+    u_eid_d, u_slot_d = dev(u_eid), dev(u_slot.reshape(-1))
+    c = torch.full((rows * top_k, n), -3.0, dtype=torch.bfloat16, device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    lib = hip.load()
+    rc = lib.moe_w4a16_gemv_union(
+        p(a_dev), k, a_rows, int(per_slot), p(table.packed_ptrs), p(table.scale_ptrs),
+        p(table.scale2), p(u_eid_d), p(u_slot_d), rows, top_k, num_experts, p(c), n, n, k,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, lib.moe_w4a16_last_error().decode()
+    torch.cuda.synchronize()
+    got = f64(c)
+    ref = _oracle_gemv(a_bits, per_slot, experts, s2, ids, n)
+    _check(got, ref, _abs_bound(a_bits, per_slot, experts, s2, ids, n, k))
+    srcs = np.array([t if per_slot else t // top_k for t in range(rows * top_k)])
+    zero = (srcs >= a_rows) & ~np.isnan(ref[:, 0])
+    assert zero.any() and np.all(got[zero] == 0.0)
