@@ -131,6 +131,71 @@ __global__ __launch_bounds__(kUnionMaxIds) void row_union_kernel(
   }
 }
 
+// The same table for 65 to 1024 ids when the expert ids fit a table in LDS: instead of
+// pairwise scans, each expert's lowest covered slot comes from an LDS atomic minimum (the
+// minimum does not depend on the order of the atomics), the openers are numbered by a
+// block-wide count in slot order, and every covered slot writes its one u_slot entry
+// over a table first filled with -1.
+constexpr int kUnionMapExperts = 8192;  // experts an LDS map covers (32 KB)
+
+__global__ __launch_bounds__(kUnionMaxIds) void row_union_map_kernel(
+    const int32_t *__restrict__ ids, int32_t rows, int32_t top_k, int32_t num_experts,
+    const uint64_t *__restrict__ present, int32_t *__restrict__ u_eid,
+    int32_t *__restrict__ u_slot, int32_t *__restrict__ slot_perm,
+    int32_t *__restrict__ counters) {
+  __shared__ int32_t s_id[kUnionMaxIds];          // valid id of a slot, else -1
+  __shared__ int32_t s_map[kUnionMapExperts];     // expert -> lowest covered slot -> entry
+  __shared__ int32_t s_wave_open[kUnionMaxIds / 64], s_wave_cov[kUnionMaxIds / 64];
+  const int n_ids = rows * top_k;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n_waves = static_cast<int>(blockDim.x >> 6);
+  const int r = t / top_k, j = t - r * top_k;
+
+  int id = -1;
+  if (t < n_ids) {
+    const int v = ids[t];
+    if (v >= 0 && v < num_experts && (present == nullptr || present[v] != 0)) id = v;
+  }
+  s_id[t] = id;
+  for (int e = t; e < num_experts; e += blockDim.x) s_map[e] = INT32_MAX;
+  __syncthreads();
+  // 1. Covered: valid and no lower slot of the row holds the same id.
+  bool covered = id >= 0;
+  for (int jj = 0; covered && jj < j; ++jj) covered = s_id[r * top_k + jj] != id;
+  if (covered) atomicMin(&s_map[id], t);
+  __syncthreads();
+  // 2. An opener is its expert's lowest covered slot; entries are numbered in slot order.
+  const bool opens = covered && s_map[id] == t;
+  const uint64_t m_open = __ballot(opens), m_cov = __ballot(covered);
+  if (lane == 0) {
+    s_wave_open[wave] = __popcll(m_open);
+    s_wave_cov[wave] = __popcll(m_cov);
+  }
+  __syncthreads();
+  int base = 0, n_union = 0, n_cov = 0;
+  for (int w = 0; w < n_waves; ++w) {
+    if (w < wave) base += s_wave_open[w];
+    n_union += s_wave_open[w];
+    n_cov += s_wave_cov[w];
+  }
+  const int p_open = base + __popcll(m_open & ((1ull << lane) - 1ull));
+  if (opens) s_map[id] = p_open;  // the expert's entry, for every covered slot
+  // 3. Outputs: u_eid and slot_perm directly; u_slot filled with -1, then each covered
+  //    slot's entry (the barrier orders the two writes of an element).
+  if (t < n_ids) {
+    if (opens) u_eid[p_open] = id;
+    if (t >= n_union) u_eid[t] = -1;
+    if (slot_perm != nullptr) slot_perm[t] = covered ? t : -1;
+  }
+  for (int q = t; q < n_ids * rows; q += blockDim.x) u_slot[q] = -1;
+  __syncthreads();
+  if (covered) u_slot[static_cast<int64_t>(s_map[id]) * rows + r] = j;
+  if (counters != nullptr && t == 0) {
+    counters[0] = n_union;
+    counters[1] = n_ids - n_cov;
+  }
+}
+
 // The same table for at most 64 ids, in one wave and without scans: lane t holds slot t.
 // The lanes holding the same valid id are found with one ballot per id bit; a slot is
 // covered when no lower lane of its row has its id, and opens an entry when no lower
@@ -651,6 +716,10 @@ extern "C" int moe_row_union(const int32_t *topk_ids, int32_t rows, int32_t top_
                        topk_ids, rows, top_k, num_experts, present, u_eid, u_slot, slot_perm,
                        counters);
   const int threads = (n_ids + 63) / 64 * 64;
+  if (num_experts <= kUnionMapExperts)
+    return moe::launch("moe_row_union", row_union_map_kernel, dim3(1), dim3(threads), 0,
+                       stream, topk_ids, rows, top_k, num_experts, present, u_eid, u_slot,
+                       slot_perm, counters);
   return moe::launch("moe_row_union", row_union_kernel, dim3(1), dim3(threads), 0, stream,
                      topk_ids, rows, top_k, num_experts, present, u_eid, u_slot, slot_perm,
                      counters);

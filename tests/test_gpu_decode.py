@@ -40,6 +40,8 @@ def _union_gpu(hip, ids, num_experts, present=None):
 @pytest.mark.parametrize("rows,top_k,num_experts,seed", [
     (1, 8, 256, 0), (8, 8, 256, 1), (8, 8, 16, 2), (5, 3, 7, 3), (16, 8, 64, 4),
     (128, 8, 256, 5), (1024, 1, 40, 6), (64, 16, 2048, 7),
+    # more than 64 ids with expert ids past the LDS map (8192): the pairwise-scan kernel
+    (100, 2, 1 << 20, 13), (9, 8, 9000, 14),
     # at most 64 ids (the one-wave kernel): one id per row, one row of 64, a single
     # expert, heavy repeats, ids of 20 bits
     (64, 1, 3, 8), (1, 64, 100, 9), (2, 32, 1, 10), (7, 9, 5, 11), (4, 16, 1 << 20, 12)])
