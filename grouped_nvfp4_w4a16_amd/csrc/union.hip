@@ -5,9 +5,10 @@
 // u_eid (union expert ids, -1 = entry unused) and u_slot (slot per union entry per row, -1
 // = row absent), the row-batched GEMV that sweeps each expert of the rows' union once and
 // writes C[rows, top_k, N], and moe_row_groups' statement that which rows share a sweep
-// never changes what a row adds. The union is found by pairwise scans in one workgroup, no
-// sort; the outputs are laid out by (row, slot), so the combine reads them back through
-// slot_perm without an expert-sorted permutation.
+// never changes what a row adds. The union is found in one workgroup without a sort (one
+// wave's ballots up to 64 ids; above, a per-expert LDS map, or pairwise scans for expert
+// ids past the map); the outputs are laid out by (row, slot), so the combine reads them
+// back through slot_perm without an expert-sorted permutation.
 //
 // gfx950 design of the GEMV (the pages' mma-less GEMV tiers are not used):
 //   - A union entry has at most one activation row per routed row, so with rows <= 16 all

@@ -391,7 +391,7 @@ int moe_hbm_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int32_t b
 
 /*
  * moe_row_union - the union of the experts a few rows selected ([FWD] workspace fields
- * u_eid, u_slot; the union is found by pairwise scans in one workgroup, no sort).
+ * u_eid, u_slot; the union is found in one workgroup, without a sort).
  *
  * Slot t = r * top_k + j is covered when topk_ids[t] is in [0, num_experts), the expert
  * is present (below) and no lower slot of row r holds the same id (a proper top-k never
