@@ -171,6 +171,80 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
   }
 }
 
+// The same sort for at most 64 slots (a few decode rows), in one wave with no block-wide
+// scans: lane t holds slot t; the lanes of one expert come from same_id_lanes, a lane's
+// rank among them is its stable position, and the expert offsets are a wave scan over
+// the per-expert counts, each lane summing a contiguous range of experts.
+__global__ __launch_bounds__(64) void moe_align_wave_kernel(
+    const int32_t *__restrict__ ids, int32_t n_slots, int32_t top_k, int32_t num_experts,
+    int32_t *__restrict__ sorted_token_ids, int32_t *__restrict__ sorted_expert_ids,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ token_to_perm,
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ counters) {
+  extern __shared__ int lds[];
+  const int E = num_experts;
+  int *cnt = lds;  // [E]: slots per expert, then each expert's first position
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  const bool in = lane < n_slots;
+  const int id = in ? ids[lane] : -1;
+  const bool valid = in && id >= 0 && id < E;
+  const int bits = E > 1 ? 32 - __clz(E - 1) : 1;
+  const uint64_t lower = (1ull << lane) - 1ull;
+  const uint64_t grp = same_id_lanes(id, valid, bits);
+  const int n_invalid = __popcll(__ballot(in && !valid));
+  __syncthreads();
+  if (valid && (grp & lower) == 0) cnt[id] = __popcll(grp);  // one writer per expert
+  __syncthreads();
+  // Lane l owns experts [l per, (l + 1) per): its slot and active-expert counts, then
+  // their exclusive wave prefix sums.
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int n_mine = 0, act_mine = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    const int c = e < E ? cnt[e] : 0;
+    n_mine += c;
+    act_mine += c > 0;
+  }
+  const int run0 = wave_inclusive_scan(n_mine) - n_mine;
+  const int act0 = wave_inclusive_scan(act_mine) - act_mine;
+  const int n_valid = __shfl(run0 + n_mine, 63, 64);
+  const int n_active = __shfl(act0 + act_mine, 63, 64);
+  int run = run0, act = act0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = cnt[e];
+      expert_offsets[e] = run;
+      cnt[e] = run;
+      if (active_experts != nullptr && c > 0) active_experts[act++] = e;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (in) {
+    const int pos = valid ? cnt[id] + __popcll(grp & lower) : -1;
+    token_to_perm[lane] = pos;
+    if (valid) {
+      sorted_token_ids[pos] = lane / top_k;
+      sorted_expert_ids[pos] = id;
+    }
+  }
+  for (int p = n_valid + lane; p < n_slots; p += 64) {
+    sorted_token_ids[p] = -1;
+    sorted_expert_ids[p] = -1;
+  }
+  if (active_experts != nullptr)
+    for (int i = n_active + lane; i < E; i += 64) active_experts[i] = -1;
+  if (lane == 0) {
+    expert_offsets[E] = n_valid;
+    if (counters != nullptr) {
+      counters[0] = n_active;
+      counters[1] = n_invalid;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k,
@@ -191,6 +265,12 @@ extern "C" int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k,
     MOE_REQUIRE(topk_ids && sorted_token_ids && sorted_expert_ids && token_to_perm,
                 "moe_align: a required pointer is NULL");
   }
+  if (n_slots > 0 && n_slots <= 64)
+    return moe::launch("moe_align", moe_align_wave_kernel, dim3(1), dim3(64),
+                       static_cast<size_t>(num_experts) * sizeof(int), stream, topk_ids,
+                       static_cast<int32_t>(n_slots), top_k, num_experts, sorted_token_ids,
+                       sorted_expert_ids, expert_offsets, token_to_perm, active_experts,
+                       counters);
   const size_t lds = (static_cast<size_t>(kWaves) * num_experts + kWaves + 2) * sizeof(int);
   // Histograms of large expert counts exceed the default 64 KiB of dynamic LDS.
   static const hipError_t attr_err = hipFuncSetAttribute(

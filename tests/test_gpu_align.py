@@ -48,7 +48,11 @@ def test_align_workload_routing(hip, name):
 @pytest.mark.parametrize("rows,top_k,num_experts,bad,seed", [
     (1, 1, 1, 0.0, 0), (3, 2, 5, 0.3, 1), (37, 3, 5, 0.1, 2), (64, 8, 16, 0.0, 3),
     (200, 6, 300, 0.05, 4), (16, 8, 256, 0.2, 5), (1000, 8, 2048, 0.01, 6),
-    (4097, 8, 256, 0.0, 7), (513, 4, 1025, 0.02, 8), (129, 8, 7, 0.5, 9)])
+    (4097, 8, 256, 0.0, 7), (513, 4, 1025, 0.02, 8), (129, 8, 7, 0.5, 9),
+    # at most 64 slots (the one-wave kernel): decode-sized batches, one row of 64, one
+    # slot, a single expert, the largest expert count, mostly invalid ids
+    (8, 8, 256, 0.1, 10), (1, 64, 300, 0.0, 11), (64, 1, 2048, 0.2, 12), (1, 1, 2048, 0.0, 13),
+    (5, 7, 1, 0.0, 14), (2, 3, 2000, 0.5, 15), (9, 7, 64, 0.0, 16)])
 def test_align_random_with_invalid_ids(hip, rows, top_k, num_experts, bad, seed):
     rng = np.random.default_rng(seed)
     ids = rng.integers(0, num_experts, size=(rows, top_k)).astype(np.int32)  # repeats allowed
