@@ -17,6 +17,7 @@
 //      sort is stable and the result is deterministic (no atomics decide an order).
 //      The group's lowest lane advances the wave's running position of that expert.
 //   The first two chunks of 64 ids of a wave stay in registers between passes 1 and 3.
+// At most 64 slots (a few decode rows) take a one-wave form of the same steps.
 #include "common.h"
 
 namespace {
