@@ -16,8 +16,8 @@ import workloads as wl
 # The parity gate: max |gpu - oracle| / max |oracle| against the BF16-weight oracle.
 GATE = 5e-3
 
-# Host threads for the oracle's per-expert loop at full size (the GPU machine gives a process
-# 16 CPUs; its count of the host's cores may be larger).
+# Host threads for the oracle's per-expert loop at full size: at most 16 (a process may be
+# given fewer CPUs than os.cpu_count() reports for the host).
 ORACLE_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
