@@ -471,18 +471,20 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
       blk[g].hi47 = t[3];
     }
   };
-  // Staged form: this wave's piece of LDS holds the step's 2 kNQ tokens. Lane l writes its
-  // 16 bytes of token 2 q + l / 32 and reads its B operand from token r16; a lane past
-  // the staged tokens (r16 >= 2 kNQ >= rows) has no token and reads token r16 mod 2 kNQ,
-  // a column that is never stored. Writes of a step follow the reads of the step before
-  // in the wave's program order, so one piece per wave suffices.
+  // Staged form: this wave's piece of LDS holds the step's 2 kNQ tokens, each group of 8 k
+  // already in the decoder's order. Lane l writes its 16 bytes of token 2 q + l / 32 and
+  // reads its B operand from token r16; a lane past the staged tokens (r16 >= 2 kNQ >=
+  // rows) has no token and reads token r16 mod 2 kNQ, a column that is never stored.
+  // Writes of a step follow the reads of the step before in the wave's program order, so
+  // one piece per wave suffices.
   uint8_t *xs_w = xs + wave * (2 * (kNQ ? kNQ : 1) * kXsRowBytes);
   const int xs_tok = kNQ ? r16 % (2 * (kNQ ? kNQ : 1)) : 0;
   const auto run_step = [&](const StepRegs<kNQ> &st, const uint8_t *tab, bool t1_on) {
     if (kNQ) {
 #pragma unroll
       for (int q = 0; q < kNQ; ++q)
-        *reinterpret_cast<u32x4_t *>(xs_w + (2 * q + (lane >> 5)) * kXsRowBytes + 16 * (lane & 31)) = st.x[q];
+        *reinterpret_cast<u32x4_t *>(xs_w + (2 * q + (lane >> 5)) * kXsRowBytes + 16 * (lane & 31)) =
+            moe::permute_k8(st.x[q]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -494,8 +496,8 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
       for (int q = 0; q < 4; ++q) {
         const u32x4_t xv = kNQ ? *reinterpret_cast<const u32x4_t *>(
                                      xs_w + xs_tok * kXsRowBytes + 128 * kb + 16 * (4 * h + q))
-                               : st.x[(4 * h + q) % (kNQ ? kNQ : 8)];
-        B[q] = __builtin_bit_cast(bf16x8_t, moe::permute_k8(xv));
+                               : moe::permute_k8(st.x[(4 * h + q) % (kNQ ? kNQ : 8)]);
+        B[q] = __builtin_bit_cast(bf16x8_t, xv);
       }
       const u32x4_t &x0 = h ? st.wb[0] : st.wa[0];
       const uint32_t w0w[4] = {x0[0], x0[1], x0[2], x0[3]};
