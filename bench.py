@@ -2,11 +2,11 @@
 
 One step = one pass of the whole path over one 256-row batch of the prefill sub-chunk
 workload (256 experts, top_k 8, hidden 6144, moe_intermediate 2048, NVFP4 weights):
-moe_align -> zero expert_out -> grouped GEMM gate_up with the SwiGLU clamp fused into its
-epilogue (``--unfused``: the GEMM and swiglu_clamp as two calls) -> grouped GEMM down
--> moe_combine, all enqueued on one HIP stream with every input already in HBM. The zeroing
-runs only when the down table has null entries (otherwise every row the combine reads is
-written by the down GEMM).
+moe_align -> grouped GEMM gate_up with the SwiGLU clamp fused into its epilogue
+(``--unfused``: the GEMM and swiglu_clamp as two calls) -> grouped GEMM down ->
+moe_combine, all enqueued on one HIP stream with every input already in HBM. When the down
+table has null entries, expert_out is zeroed first, in the sort's launch (moe_align_zero);
+otherwise every row the combine reads is written by the down GEMM.
 
 After the W warm-up steps, untimed steps continue until 0.15 s of warm-up has passed (the
 GPU's clock ramps over the first tens of milliseconds of load); their number is reported as
@@ -348,7 +348,7 @@ def time_decode_leg(hip, torch, steps, probe):
     """The decode / verify path on the small-M workload (8 rows over 256 experts, experts
     [128, 256) absent), timed per stage with HIP events: the union path (moe_row_union ->
     union GEMV gate_up with the SwiGLU -> union GEMV down -> combine) and the sorted path
-    (moe_align -> zero -> grouped GEMMs -> combine) on the same rows. Its weights (0.68 GB)
+    (moe_align_zero -> grouped GEMMs -> combine) on the same rows. Its weights (0.68 GB)
     would partly stay in the 256 MB last-level cache from one step to the next, so every
     timed step follows a cache-evicting stream outside its events. GB/s is unique weight
     bytes (live experts, both projections) per step."""
@@ -382,11 +382,10 @@ def time_decode_leg(hip, torch, steps, probe):
             ("moe_combine", lambda: hip.moe_combine(dws.expert_out[:s], dws.slot_perm[:s], wts,
                                                     out))],
         "sorted": [
-            ("moe_align", lambda: hip.moe_align(ids, w.num_experts, ws.sorted_token_ids,
-                                                ws.sorted_expert_ids, ws.expert_offsets,
-                                                ws.token_to_perm, ws.active_experts,
-                                                ws.counters)),
-            ("zero_expert_out", lambda: hip.moe_zero_rows(ws.expert_out[:s])),
+            ("moe_align_zero", lambda: hip.moe_align(ids, w.num_experts, ws.sorted_token_ids,
+                                                     ws.sorted_expert_ids, ws.expert_offsets,
+                                                     ws.token_to_perm, ws.active_experts,
+                                                     ws.counters, zero=ws.expert_out[:s])),
             ("grouped_gemm_gate_up_swiglu", lambda: hip.moe_w4a16_grouped_gemm_swiglu(
                 x, gt, ws.expert_offsets, ws.act, w.limit, ws.sorted_token_ids, max_rows=s)),
             ("grouped_gemm_down", lambda: hip.moe_w4a16_grouped_gemm(
@@ -505,11 +504,11 @@ def measure_workload(hip, torch, w, args, probe, steps: int, warmup: int):
                             ws.topk_weights)
 
     def st_align(x, ids, wts):
+        # null down entries: their rows must read as zero in the combine, zeroed in the
+        # sort's launch (moe_align_zero)
         hip.moe_align(ids, w.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
-                      ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters)
-
-    def st_zero(x, ids, wts):  # null down entries: their rows must read as zero in the combine
-        hip.moe_zero_rows(ws.expert_out[:s], stream)
+                      ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters,
+                      zero=ws.expert_out[:s] if need_zero else None)
 
     c_single = (torch.empty((max(s, 1), n_gu), dtype=torch.bfloat16, device="cuda")
                 if single else None)
@@ -567,9 +566,7 @@ def measure_workload(hip, torch, w, args, probe, steps: int, warmup: int):
         stages += [("moe_align", st_align), ("grouped_gemm", st_single)]
         gu_name, dn_name = "grouped_gemm", None
     else:
-        stages.append(("moe_align", st_align))
-        if need_zero:
-            stages.append(("zero_expert_out", st_zero))
+        stages.append(("moe_align_zero" if need_zero else "moe_align", st_align))
         if args.unfused:
             stages += [("grouped_gemm_gate_up", st_gate_up), ("swiglu_clamp", st_swiglu)]
             gu_name = "grouped_gemm_gate_up"

@@ -34,7 +34,7 @@ __all__ = [
     "moe_w4a16_grouped_gemm_swiglu", "moe_w4a16_dequant_bf16", "moe_router_topk",
     "moe_layer_from_logits", "ExpertTable", "Workspace", "moe_layer", "EXPORTS", "LIB_PATH",
     "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16", "moe_dense_workspace_bytes",
-    "dense_workspace", "SharedExpert", "moe_zero_rows",
+    "dense_workspace", "SharedExpert", "moe_zero_rows", "moe_align_zero",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
     "moe_layer_decode", "UNION_MAX_ROWS", "source_sha256", "moe_hbm_read_probe",
     "moe_dense_gemm_bf16_noalloc", "DENSE_NOALLOC_SCRATCH_BYTES",
@@ -50,6 +50,7 @@ EXPORTS = (
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
     "moe_dense_workspace_bytes", "moe_zero_rows", "moe_row_union", "moe_w4a16_gemv_union",
     "moe_w4a16_gemv_union_swiglu", "moe_hbm_read_probe", "moe_dense_gemm_bf16_noalloc",
+    "moe_align_zero",
 )
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
@@ -69,6 +70,8 @@ _SIGNATURES = {
     "moe_w4a16_last_error": ([], ctypes.c_char_p),
     "moe_w4a16_source_sha256": ([], ctypes.c_char_p),
     "moe_align": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_align_zero": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
+                        _vp], ctypes.c_int),
     "moe_w4a16_grouped_gemm": (
         [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp],
         ctypes.c_int),
@@ -185,8 +188,10 @@ def _bf16_matrix(t, name):
 # ------------------------------------------------------------------------------- calls
 
 def moe_align(topk_ids, num_experts: int, sorted_token_ids, sorted_expert_ids, expert_offsets,
-              token_to_perm, active_experts=None, counters=None, stream=None) -> None:
-    """Expert-sorted slot order of ``topk_ids`` (int32 ``[rows, top_k]``); see the header."""
+              token_to_perm, active_experts=None, counters=None, stream=None, zero=None) -> None:
+    """Expert-sorted slot order of ``topk_ids`` (int32 ``[rows, top_k]``); see the header.
+    With ``zero`` (a BF16 ``[rows * top_k, cols]`` view, e.g. ``expert_out``), the same
+    launch also zeroes it: moe_align_zero, the sort and the zero-first step together."""
     import torch
 
     for t, n in ((topk_ids, "topk_ids"), (sorted_token_ids, "sorted_token_ids"),
@@ -205,6 +210,15 @@ def moe_align(topk_ids, num_experts: int, sorted_token_ids, sorted_expert_ids, e
                        (active_experts, num_experts, "active_experts"), (counters, 2, "counters")):
         if t is not None and (t.numel() < need or not t.is_contiguous()):
             raise ValueError(f"{n}: needs {need} contiguous elements")
+    if zero is not None:
+        zero, ldz = _bf16_matrix(zero, "zero")
+        if zero.shape[0] != s:
+            raise ValueError("zero: needs rows * top_k rows")
+        _check("moe_align_zero", load().moe_align_zero(
+            _p(topk_ids), rows, top_k, num_experts, _p(sorted_token_ids),
+            _p(sorted_expert_ids), _p(expert_offsets), _p(token_to_perm), _p(active_experts),
+            _p(counters), _p(zero), ldz, zero.shape[1], _stream(stream)))
+        return
     _check("moe_align", load().moe_align(
         _p(topk_ids), rows, top_k, num_experts, _p(sorted_token_ids), _p(sorted_expert_ids),
         _p(expert_offsets), _p(token_to_perm), _p(active_experts), _p(counters),
@@ -645,22 +659,23 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
               moe_intermediate: int, limit: float, ws: Workspace, out, shared=None,
               stream=None, fused: bool = True) -> None:
     """One routed MoE layer over the rows of ``x``, all on the device, in the order of the
-    grouped-prefill arm: align -> zero expert_out -> grouped GEMM gate_up (rows gathered
+    grouped-prefill arm: align (and zero expert_out) -> grouped GEMM gate_up (rows gathered
     through sorted_token_ids) with the SwiGLU clamp fused into its epilogue -> grouped GEMM
     down -> indexed combine. ``fused=False`` runs the gate_up GEMM and swiglu_clamp as two
     calls (same bits).
-    ``ws.expert_out`` is zeroed first so experts that are not present add zero. When every
-    down-projection entry is present the down GEMM writes every row the combine reads
-    (each valid slot's row lies in its expert's segment), so the zeroing is skipped.
+    ``ws.expert_out`` is zeroed first, in the sort's launch (moe_align_zero), so experts
+    that are not present add zero. When every down-projection entry is present the down
+    GEMM writes every row the combine reads (each valid slot's row lies in its expert's
+    segment), so the zeroing is skipped.
     ``shared`` is the combine's shared term: a ``[rows, H]`` BF16 tensor, or a
     ``SharedExpert``, which is then run over ``x`` after the routed experts."""
     _same_experts(gate_up, down)
     rows, top_k = topk_ids.shape
     s = rows * top_k
+    # absent down experts: their expert_out rows are zeroed in the sort's launch
     moe_align(topk_ids, gate_up.num_experts, ws.sorted_token_ids, ws.sorted_expert_ids,
-              ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters, stream)
-    if not all(down.present):
-        moe_zero_rows(ws.expert_out[:s], stream)
+              ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters, stream,
+              zero=None if all(down.present) else ws.expert_out[:s])
     mi = moe_intermediate
     if fused:
         moe_w4a16_grouped_gemm_swiglu(x, gate_up, ws.expert_offsets, ws.act, limit,
@@ -723,7 +738,7 @@ def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: Expe
     ``fused=False`` runs the gate_up GEMV and swiglu_clamp as two calls (same bits).
     Slots of experts absent from the down table are left out of the union (the combine
     skips them), so unlike the sorted path no zero-first step is needed. On MI355X the
-    sorted path (``moe_layer``) is faster above about 4 rows; this path wins below."""
+    sorted path (``moe_layer``) is faster from about 4 rows on; this path wins below."""
     _same_experts(gate_up, down)
     rows, top_k = topk_ids.shape
     t = rows * top_k

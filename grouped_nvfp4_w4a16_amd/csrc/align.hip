@@ -20,6 +20,8 @@
 // At most 64 slots (a few decode rows) take a one-wave form of the same steps.
 #include "common.h"
 
+#include <algorithm>
+
 namespace {
 
 constexpr int kThreads = 1024;
@@ -67,11 +69,29 @@ __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
   return res;
 }
 
+// Workgroups past the first of a moe_align_zero launch: forward_moe's zero-first step on
+// rows [0, n_rows) x columns [0, cols) of `zero`, 16 bytes per thread, beside the sort.
+__device__ __forceinline__ void zero_rows_part(uint16_t *__restrict__ zero, int64_t ld,
+                                               int32_t n_rows, int32_t cols) {
+  const int64_t per_row = cols / 8, units = per_row * n_rows;
+  const int64_t stride = static_cast<int64_t>(gridDim.x - 1) * blockDim.x;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x; u < units;
+       u += stride) {
+    const int64_t row = u / per_row, col8 = u - row * per_row;
+    *reinterpret_cast<uint4 *>(zero + row * ld + col8 * 8) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     const int32_t *__restrict__ ids, int32_t n_slots, int32_t top_k, int32_t num_experts,
     int32_t *__restrict__ sorted_token_ids, int32_t *__restrict__ sorted_expert_ids,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ token_to_perm,
-    int32_t *__restrict__ active_experts, int32_t *__restrict__ counters) {
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ counters,
+    uint16_t *__restrict__ zero, int64_t ld_zero, int32_t zero_cols) {
+  if (blockIdx.x != 0) {  // uniform: a zeroing workgroup
+    zero_rows_part(zero, ld_zero, n_slots, zero_cols);
+    return;
+  }
   extern __shared__ int lds[];
   const int E = num_experts;
   int *hist = lds;                        // [kWaves][E]
@@ -180,7 +200,12 @@ __global__ __launch_bounds__(64) void moe_align_wave_kernel(
     const int32_t *__restrict__ ids, int32_t n_slots, int32_t top_k, int32_t num_experts,
     int32_t *__restrict__ sorted_token_ids, int32_t *__restrict__ sorted_expert_ids,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ token_to_perm,
-    int32_t *__restrict__ active_experts, int32_t *__restrict__ counters) {
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ counters,
+    uint16_t *__restrict__ zero, int64_t ld_zero, int32_t zero_cols) {
+  if (blockIdx.x != 0) {  // uniform: a zeroing workgroup
+    zero_rows_part(zero, ld_zero, n_slots, zero_cols);
+    return;
+  }
   extern __shared__ int lds[];
   const int E = num_experts;
   int *cnt = lds;  // [E]: slots per expert, then each expert's first position
@@ -248,41 +273,83 @@ __global__ __launch_bounds__(64) void moe_align_wave_kernel(
 
 }  // namespace
 
-extern "C" int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k,
-                         int32_t num_experts, int32_t *sorted_token_ids,
-                         int32_t *sorted_expert_ids, int32_t *expert_offsets,
-                         int32_t *token_to_perm, int32_t *active_experts, int32_t *counters,
-                         void *stream) {
-  moe::clear_error();
-  MOE_REQUIRE(rows >= 0, "moe_align: rows must be >= 0 (got %d)", rows);
-  MOE_REQUIRE(top_k >= 1, "moe_align: top_k must be >= 1 (got %d)", top_k);
+namespace {
+
+// moe_align, with the zeroing workgroups of moe_align_zero when `zero` is given.
+int align_launch(const char *name, const int32_t *topk_ids, int32_t rows, int32_t top_k,
+                 int32_t num_experts, int32_t *sorted_token_ids, int32_t *sorted_expert_ids,
+                 int32_t *expert_offsets, int32_t *token_to_perm, int32_t *active_experts,
+                 int32_t *counters, uint16_t *zero, int64_t ld_zero, int32_t zero_cols,
+                 void *stream) {
+  MOE_REQUIRE(rows >= 0, "%s: rows must be >= 0 (got %d)", name, rows);
+  MOE_REQUIRE(top_k >= 1, "%s: top_k must be >= 1 (got %d)", name, top_k);
   MOE_REQUIRE(num_experts >= 1 && num_experts <= MOE_ALIGN_MAX_EXPERTS,
-              "moe_align: num_experts must be in [1, %d] (got %d)", MOE_ALIGN_MAX_EXPERTS,
+              "%s: num_experts must be in [1, %d] (got %d)", name, MOE_ALIGN_MAX_EXPERTS,
               num_experts);
   const int64_t n_slots = static_cast<int64_t>(rows) * top_k;
-  MOE_REQUIRE(n_slots <= INT32_MAX, "moe_align: rows * top_k overflows int32");
-  MOE_REQUIRE(expert_offsets != nullptr, "moe_align: expert_offsets is NULL");
+  MOE_REQUIRE(n_slots <= INT32_MAX, "%s: rows * top_k overflows int32", name);
+  MOE_REQUIRE(expert_offsets != nullptr, "%s: expert_offsets is NULL", name);
   if (n_slots > 0) {
     MOE_REQUIRE(topk_ids && sorted_token_ids && sorted_expert_ids && token_to_perm,
-                "moe_align: a required pointer is NULL");
+                "%s: a required pointer is NULL", name);
   }
-  if (n_slots > 0 && n_slots <= 64)
-    return moe::launch("moe_align", moe_align_wave_kernel, dim3(1), dim3(64),
-                       static_cast<size_t>(num_experts) * sizeof(int), stream, topk_ids,
-                       static_cast<int32_t>(n_slots), top_k, num_experts, sorted_token_ids,
-                       sorted_expert_ids, expert_offsets, token_to_perm, active_experts,
-                       counters);
+  // Zeroing workgroups: enough to cover the rows in a few passes, none without a buffer.
+  int64_t zero_blocks = 0;
+  const bool wave_form = n_slots > 0 && n_slots <= 64;
+  const int threads = wave_form ? 64 : kThreads;
+  if (zero != nullptr && n_slots > 0 && zero_cols > 0) {
+    const int64_t units = n_slots * (zero_cols / 8);
+    zero_blocks = std::min<int64_t>((units + threads - 1) / threads, wave_form ? 4096 : 1024);
+  }
+  if (wave_form)
+    return moe::launch(name, moe_align_wave_kernel, dim3(static_cast<unsigned>(1 + zero_blocks)),
+                       dim3(64), static_cast<size_t>(num_experts) * sizeof(int), stream,
+                       topk_ids, static_cast<int32_t>(n_slots), top_k, num_experts,
+                       sorted_token_ids, sorted_expert_ids, expert_offsets, token_to_perm,
+                       active_experts, counters, zero, ld_zero, zero_cols);
   const size_t lds = (static_cast<size_t>(kWaves) * num_experts + kWaves + 2) * sizeof(int);
   // Histograms of large expert counts exceed the default 64 KiB of dynamic LDS.
   static const hipError_t attr_err = hipFuncSetAttribute(
       reinterpret_cast<const void *>(moe_align_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>((kWaves * MOE_ALIGN_MAX_EXPERTS + kWaves + 2) * sizeof(int)));
   if (lds > 65536 && attr_err != hipSuccess) {
-    moe::set_error("moe_align: cannot raise the LDS limit: %s", hipGetErrorString(attr_err));
+    moe::set_error("%s: cannot raise the LDS limit: %s", name, hipGetErrorString(attr_err));
     return MOE_ELAUNCH;
   }
-  return moe::launch("moe_align", moe_align_kernel, dim3(1), dim3(kThreads), lds, stream,
-                     topk_ids, static_cast<int32_t>(n_slots), top_k, num_experts,
-                     sorted_token_ids, sorted_expert_ids, expert_offsets, token_to_perm,
-                     active_experts, counters);
+  return moe::launch(name, moe_align_kernel, dim3(static_cast<unsigned>(1 + zero_blocks)),
+                     dim3(kThreads), lds, stream, topk_ids, static_cast<int32_t>(n_slots), top_k,
+                     num_experts, sorted_token_ids, sorted_expert_ids, expert_offsets,
+                     token_to_perm, active_experts, counters, zero, ld_zero, zero_cols);
+}
+
+}  // namespace
+
+extern "C" int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k,
+                         int32_t num_experts, int32_t *sorted_token_ids,
+                         int32_t *sorted_expert_ids, int32_t *expert_offsets,
+                         int32_t *token_to_perm, int32_t *active_experts, int32_t *counters,
+                         void *stream) {
+  moe::clear_error();
+  return align_launch("moe_align", topk_ids, rows, top_k, num_experts, sorted_token_ids,
+                      sorted_expert_ids, expert_offsets, token_to_perm, active_experts, counters,
+                      nullptr, 0, 0, stream);
+}
+
+extern "C" int moe_align_zero(const int32_t *topk_ids, int32_t rows, int32_t top_k,
+                              int32_t num_experts, int32_t *sorted_token_ids,
+                              int32_t *sorted_expert_ids, int32_t *expert_offsets,
+                              int32_t *token_to_perm, int32_t *active_experts,
+                              int32_t *counters, uint16_t *zero, int64_t ld_zero,
+                              int32_t zero_cols, void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(zero_cols >= 0 && zero_cols % 8 == 0,
+              "moe_align_zero: zero_cols must be >= 0 and a multiple of 8 (got %d)", zero_cols);
+  MOE_REQUIRE(ld_zero >= zero_cols && ld_zero % 8 == 0,
+              "moe_align_zero: ld_zero must be >= zero_cols and a multiple of 8");
+  if (static_cast<int64_t>(rows) * top_k > 0 && zero_cols > 0)
+    MOE_REQUIRE(zero != nullptr && moe::aligned16(zero),
+                "moe_align_zero: zero must be non-NULL and 16-byte aligned");
+  return align_launch("moe_align_zero", topk_ids, rows, top_k, num_experts, sorted_token_ids,
+                      sorted_expert_ids, expert_offsets, token_to_perm, active_experts, counters,
+                      zero, ld_zero, zero_cols, stream);
 }

@@ -8,6 +8,7 @@
  *   swiglu_clamp            silu(min(gate, L)) * clamp(up, -L, L)
  *   moe_combine             top-k weighted sum of the expert-sorted rows per token
  *   moe_zero_rows           the zero-first step on expert_out (absent experts add zero)
+ *   moe_align_zero          moe_align and moe_zero_rows in one launch
  *   moe_w4a16_grouped_gemm_swiglu  the gate_up grouped GEMM with swiglu_clamp fused into
  *                           its epilogue (same bits as the two calls in sequence)
  *   moe_router_topk         router logits -> top-k expert ids and weights (feeds moe_align
@@ -144,6 +145,25 @@ int moe_align(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_
               int32_t *sorted_token_ids, int32_t *sorted_expert_ids, int32_t *expert_offsets,
               int32_t *token_to_perm, int32_t *active_experts, int32_t *counters,
               void *stream);
+
+/*
+ * moe_align_zero - moe_align and moe_zero_rows(zero, ld_zero, rows * top_k, zero_cols) in
+ * one launch: forward_moe's routing sort and its zero-first step on expert_out ([FWD]
+ * forward_moe). The zeroing runs in workgroups of its own beside the sort, so a layer whose
+ * down table has absent experts pays one launch for the two steps. Outputs are those of
+ * the two calls.
+ *
+ *   zero  bf16 [rows * top_k, ld_zero] or NULL (NULL or zero_cols == 0: moe_align alone)
+ *
+ * Errors: those of moe_align; MOE_EINVAL unless zero_cols >= 0 and zero_cols % 8 == 0,
+ * ld_zero >= zero_cols and a multiple of 8, and zero non-NULL and 16-byte aligned when
+ * rows * top_k * zero_cols > 0.
+ */
+int moe_align_zero(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                   int32_t *sorted_token_ids, int32_t *sorted_expert_ids,
+                   int32_t *expert_offsets, int32_t *token_to_perm, int32_t *active_experts,
+                   int32_t *counters, uint16_t *zero, int64_t ld_zero, int32_t zero_cols,
+                   void *stream);
 
 /*
  * moe_w4a16_grouped_gemm - one launch over all experts ([FPG] "What this replaces" and

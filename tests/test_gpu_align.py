@@ -99,3 +99,26 @@ def test_align_rejects_bad_arguments(hip):
         hip.moe_align(ids, 4096, **{**b, "expert_offsets": torch.zeros(4097, dtype=torch.int32,
                                                                         device="cuda"),
                                     "active_experts": None})
+
+
+@pytest.mark.parametrize("rows,top_k,num_experts,cols,ld,seed", [
+    (8, 8, 256, 6144, 6144, 30),    # the one-wave form over the small-M expert_out
+    (256, 8, 256, 2048, 2056, 31),  # the block form, a padded leading dimension
+    (3, 2, 5, 8, 16, 32),           # tiny
+    (37, 3, 5, 0, 8, 33)])          # no columns: moe_align alone
+def test_align_zero(hip, rows, top_k, num_experts, cols, ld, seed):
+    """moe_align_zero: the sort's outputs as moe_align's (bit-exact against the oracle), and
+    exactly rows [0, rows * top_k) x columns [0, cols) of the buffer zeroed: the padding
+    columns and the rows past them keep their values."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, num_experts, size=(rows, top_k)).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.1] = -1
+    s = rows * top_k
+    b = align_buffers(rows, top_k, num_experts)
+    buf = torch.full((s + 3, ld), 7.0, dtype=torch.bfloat16, device="cuda")
+    hip.moe_align(dev(ids), num_experts, **b, zero=buf[:s, :cols])
+    torch.cuda.synchronize()
+    _check({k: v.cpu().numpy() for k, v in b.items()}, ids, num_experts)
+    host = buf.float().cpu().numpy()
+    assert np.all(host[:s, :cols] == 0.0)
+    assert np.all(host[:s, cols:] == 7.0) and np.all(host[s:] == 7.0)
