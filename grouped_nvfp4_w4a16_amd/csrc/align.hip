@@ -9,14 +9,17 @@
 // Design (gfx950, wave64): the slots are split into 16 contiguous ranges, one per wave.
 //   1. Each wave counts its range into a private LDS histogram: per chunk of 64 slots,
 //      the lowest lane of each group of equal ids adds the group's size.
-//   2. Per expert, the 16 per-wave counts become per-wave starting positions; a block
-//      scan over experts gives expert_offsets (and the active-expert list).
+//   2. Per expert (a thread each), the 16 per-wave counts become per-wave starting
+//      positions within the expert; then one wave scans the experts' counts, each lane
+//      summing a contiguous range of experts, for expert_offsets and the active-expert
+//      list (two barriers in all, where a block-wide scan needs three per scan).
 //   3. Each wave walks its range again in order, 64 slots at a time. The lanes holding
 //      the same expert id are found with one ballot per id bit; a lane's rank in its
 //      group is the number of lower lanes in it, so positions follow slot order: the
 //      sort is stable and the result is deterministic (no atomics decide an order).
 //      The group's lowest lane advances the wave's running position of that expert.
-//   The first two chunks of 64 ids of a wave stay in registers between passes 1 and 3.
+//   The ids and group masks of the first two chunks of 64 slots of a wave stay in
+//   registers between passes 1 and 3.
 // At most 64 slots (a few decode rows) take a one-wave form of the same steps.
 #include "common.h"
 
@@ -49,26 +52,6 @@ __device__ inline int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Exclusive scan of one value per thread over the block; *total receives the sum.
-// Every thread of the block must call it (it holds barriers).
-__device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int inc = wave_inclusive_scan(v);
-  if (lane == 63) wave_tot[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    const int t = lane < kWaves ? wave_tot[lane] : 0;
-    const int ti = wave_inclusive_scan(t);
-    if (lane < kWaves) wave_tot[lane] = ti - t;
-    if (lane == kWaves - 1) wave_tot[kWaves] = ti;
-  }
-  __syncthreads();
-  const int res = wave_tot[wave] + inc - v;
-  *total = wave_tot[kWaves];
-  __syncthreads();  // wave_tot is reused by the next call
-  return res;
-}
-
 // Workgroups past the first of a moe_align_zero launch: forward_moe's zero-first step on
 // rows [0, n_rows) x columns [0, cols) of `zero`, 16 bytes per thread, beside the sort.
 __device__ __forceinline__ void zero_rows_part(uint16_t *__restrict__ zero, int64_t ld,
@@ -94,13 +77,13 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
   }
   extern __shared__ int lds[];
   const int E = num_experts;
-  int *hist = lds;                        // [kWaves][E]
-  int *wave_tot = lds + kWaves * E;       // [kWaves + 1]
-  int *n_invalid = wave_tot + kWaves + 1;  // [1]
+  int *hist = lds;                  // [kWaves][E]: counts, then positions within the expert
+  int *first = lds + kWaves * E;    // [E]: slots per expert, then the expert's first row
+  int *misc = first + E;            // [0] invalid slots, [1] valid slots, [2] active experts
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
-  if (tid == 0) *n_invalid = 0;
+  if (tid == 0) misc[0] = 0;
   __syncthreads();
 
   // Contiguous slot range of this wave, a multiple of 64 long.
@@ -113,69 +96,90 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
   const uint64_t lower = (1ull << lane) - 1ull;
 
   // 1. per-wave histograms: each group's lowest lane adds the group size (the groups of
-  //    a chunk have distinct ids, so the updates do not collide).
-  int cache0 = -1, cache1 = -1;
+  //    a chunk have distinct ids, so the updates do not collide). The ids and group masks
+  //    of the first two chunks stay in registers for step 3.
+  int cache_id[2] = {-1, -1};
+  uint64_t cache_grp[2] = {0ull, 0ull};
   int invalid = 0;
   for (int c = 0, base = begin; base < end; ++c, base += 64) {
     const int t = base + lane;
     const bool in = t < end;
     const int id = in ? ids[t] : -1;
-    if (c == 0) cache0 = id;
-    if (c == 1) cache1 = id;
     const bool valid = in && id >= 0 && id < E;
     const uint64_t grp = same_id_lanes(id, valid, bits);
+    if (c < 2) {
+      cache_id[c] = id;
+      cache_grp[c] = grp;
+    }
     if (valid && (grp & lower) == 0) my_hist[id] += __popcll(grp);
     invalid += __popcll(__ballot(in && !valid));
   }
-  if (lane == 0 && invalid) atomicAdd(n_invalid, invalid);
+  if (lane == 0 && invalid) atomicAdd(&misc[0], invalid);
   __syncthreads();
 
-  // 2. per-wave start positions and expert offsets
-  int carry = 0, active_carry = 0;
-  for (int e0 = 0; e0 < E; e0 += kThreads) {
-    const int e = e0 + tid;
+  // 2. Each expert's count and its waves' starting positions within the expert (a
+  //    thread per expert), then the experts' first rows: one wave scans the counts,
+  //    each lane taking a contiguous range of experts (no block-wide scan).
+  for (int e = tid; e < E; e += kThreads) {
     int cnt = 0;
-    if (e < E) {
-      for (int w = 0; w < kWaves; ++w) {
-        const int h = hist[w * E + e];
-        hist[w * E + e] = cnt;
-        cnt += h;
+    for (int w = 0; w < kWaves; ++w) {
+      const int h = hist[w * E + e];
+      hist[w * E + e] = cnt;
+      cnt += h;
+    }
+    first[e] = cnt;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int n_mine = 0, act_mine = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      const int c = e < E ? first[e] : 0;
+      n_mine += c;
+      act_mine += c > 0;
+    }
+    const int run0 = wave_inclusive_scan(n_mine) - n_mine;
+    const int act0 = wave_inclusive_scan(act_mine) - act_mine;
+    int run = run0, act = act0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        const int c = first[e];
+        expert_offsets[e] = run;
+        first[e] = run;
+        if (active_experts != nullptr && c > 0) active_experts[act++] = e;
+        run += c;
       }
     }
-    int total, act_total;
-    const int excl = block_exclusive_scan(cnt, wave_tot, &total);
-    const int act_excl = block_exclusive_scan(cnt > 0 ? 1 : 0, wave_tot, &act_total);
-    if (e < E) {
-      const int off = carry + excl;
-      expert_offsets[e] = off;
-      for (int w = 0; w < kWaves; ++w) hist[w * E + e] += off;
-      if (active_experts != nullptr && cnt > 0) active_experts[active_carry + act_excl] = e;
-    }
-    carry += total;
-    active_carry += act_total;
-  }
-  if (tid == 0) {
-    expert_offsets[E] = carry;
-    if (counters != nullptr) {
-      counters[0] = active_carry;
-      counters[1] = *n_invalid;
+    if (lane == 63) {
+      misc[1] = run;
+      misc[2] = act;
+      expert_offsets[E] = run;
+      if (counters != nullptr) {
+        counters[0] = act;
+        counters[1] = misc[0];
+      }
     }
   }
-  if (active_experts != nullptr)
-    for (int i = active_carry + tid; i < E; i += kThreads) active_experts[i] = -1;
   __syncthreads();
+  const int n_valid = misc[1], n_active = misc[2];
+  if (active_experts != nullptr)
+    for (int i = n_active + tid; i < E; i += kThreads) active_experts[i] = -1;
 
-  // 3. stable scatter
+  // 3. stable scatter: an expert's first row, plus the wave's start within the expert,
+  //    plus the lane's rank in its group.
   for (int c = 0, base = begin; base < end; ++c, base += 64) {
     const int t = base + lane;
     const bool in = t < end;
-    const int id = c == 0 ? cache0 : c == 1 ? cache1 : (in ? ids[t] : -1);
+    const int id = c < 2 ? cache_id[c] : (in ? ids[t] : -1);
     const bool valid = in && id >= 0 && id < E;
-    const uint64_t grp = same_id_lanes(id, valid, bits);
+    const uint64_t grp = c < 2 ? cache_grp[c] : same_id_lanes(id, valid, bits);
     int pos = -1;
     if (valid) {
       const int start = my_hist[id];  // read by every lane of the group first
-      pos = start + __popcll(grp & lower);
+      pos = first[id] + start + __popcll(grp & lower);
       if ((grp & lower) == 0) my_hist[id] = start + __popcll(grp);
     }
     if (in) {
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
       }
     }
   }
-  for (int p = carry + tid; p < n_slots; p += kThreads) {
+  for (int p = n_valid + tid; p < n_slots; p += kThreads) {
     sorted_token_ids[p] = -1;
     sorted_expert_ids[p] = -1;
   }
@@ -307,11 +311,11 @@ int align_launch(const char *name, const int32_t *topk_ids, int32_t rows, int32_
                        topk_ids, static_cast<int32_t>(n_slots), top_k, num_experts,
                        sorted_token_ids, sorted_expert_ids, expert_offsets, token_to_perm,
                        active_experts, counters, zero, ld_zero, zero_cols);
-  const size_t lds = (static_cast<size_t>(kWaves) * num_experts + kWaves + 2) * sizeof(int);
+  const size_t lds = ((static_cast<size_t>(kWaves) + 1) * num_experts + 4) * sizeof(int);
   // Histograms of large expert counts exceed the default 64 KiB of dynamic LDS.
   static const hipError_t attr_err = hipFuncSetAttribute(
       reinterpret_cast<const void *>(moe_align_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>((kWaves * MOE_ALIGN_MAX_EXPERTS + kWaves + 2) * sizeof(int)));
+      static_cast<int>(((kWaves + 1) * MOE_ALIGN_MAX_EXPERTS + 4) * sizeof(int)));
   if (lds > 65536 && attr_err != hipSuccess) {
     moe::set_error("%s: cannot raise the LDS limit: %s", name, hipGetErrorString(attr_err));
     return MOE_ELAUNCH;
