@@ -20,8 +20,9 @@ CPU oracle on a bounded sample of the same workload.
 
 ``shared_expert`` times the shared expert (a BF16 SwiGLU MLP of width moe_intermediate
 over the same rows: moe_dense_gate_up_swiglu_bf16 then moe_dense_gemm_bf16) after the
-timed steps, outside ``value``; ``--with-shared`` runs it inside each step instead and
-feeds its output to the combine.
+timed steps, outside ``value``, and the down projection's split-K partials alone (the
+layer's form, their reduction inside the combine); ``--with-shared`` runs it inside each
+step instead and feeds it to the combine (as split-K partials when it runs split).
 
 ``decode`` times the decode / verify path on the small-M workload (8 rows, 256 experts,
 half of them absent) after the timed steps, outside ``value``: the union path
@@ -317,6 +318,20 @@ def time_shared_expert(se, x, w, steps, torch, stream, probe):
     # single-pass form for comparison
     (gu, dn), (gu_w, dn_w) = timed(se.workspace)
     (gu1, dn1), _ = timed(None)
+    # the down projection as the layer runs it: its split-K partials alone, their
+    # reduction done by the combine (moe_combine_partials)
+    part = se.workspace.view(torch.float32)
+    pairs = []
+    for _ in range(steps):
+        probe.flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        hip.moe_dense_gemm_bf16_partials(act, se.down_w, part)
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    dn_part = float(np.median([a.elapsed_time(b) for a, b in pairs])) / 1000.0
 
     def roof(name, secs, wbytes, in_bytes, out_bytes, flops):
         nbytes = wbytes + in_bytes + out_bytes
@@ -336,6 +351,12 @@ def time_shared_expert(se, x, w, steps, torch, stream, probe):
                                    2.0 * rows * 2 * inter * hidden),
             "down": roof("moe_dense_gemm_bf16", dn, hidden * inter * 2, rows * inter * 2,
                          rows * hidden * 2, 2.0 * rows * hidden * inter),
+            "down_partials_us": round(dn_part * 1e6, 2),
+            "down_partials_note": ("moe_dense_gemm_bf16_partials alone: the layer's form, whose "
+                                   "split-K reduction runs inside the combine "
+                                   "(moe_combine_partials), which then reads "
+                                   f"{4 * hip.moe_dense_splitk_ways(rows, inter)} bytes of "
+                                   "partials per shared-term element instead of 2"),
             "total_us": round((gu + dn) * 1e6, 2), "form": "split-K (workspace)",
             "timing": "each launch after a 2 GiB cache-evicting read, median",
             "mall_warm_us": {"gate_up_swiglu": round(gu_w * 1e6, 2),
@@ -532,8 +553,8 @@ def measure_workload(hip, torch, w, args, probe, steps: int, warmup: int):
         hip.moe_w4a16_grouped_gemm(ws.act, dt, ws.expert_offsets, ws.expert_out, None,
                                    max_rows=s)
 
-    def st_shared(x, ids, wts):
-        shared_out[0] = se(x, w.limit)
+    def st_shared(x, ids, wts):  # split-K: the down reduction runs in the combine
+        shared_out[0] = se.for_combine(x, w.limit)
 
     def st_combine(x, ids, wts):
         hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts, out, shared_out[0])

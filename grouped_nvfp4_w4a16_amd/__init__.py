@@ -37,7 +37,8 @@ __all__ = [
     "dense_workspace", "SharedExpert", "moe_zero_rows", "moe_align_zero",
     "moe_row_union", "moe_w4a16_gemv_union", "moe_w4a16_gemv_union_swiglu", "DecodeWorkspace",
     "moe_layer_decode", "UNION_MAX_ROWS", "source_sha256", "moe_hbm_read_probe",
-    "moe_dense_gemm_bf16_noalloc", "DENSE_NOALLOC_SCRATCH_BYTES",
+    "moe_dense_gemm_bf16_noalloc", "DENSE_NOALLOC_SCRATCH_BYTES", "moe_dense_splitk_ways",
+    "moe_dense_gemm_bf16_partials", "moe_combine_partials", "SharedPartials",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
@@ -50,7 +51,8 @@ EXPORTS = (
     "moe_router_topk", "moe_dense_gemm_bf16", "moe_dense_gate_up_swiglu_bf16",
     "moe_dense_workspace_bytes", "moe_zero_rows", "moe_row_union", "moe_w4a16_gemv_union",
     "moe_w4a16_gemv_union_swiglu", "moe_hbm_read_probe", "moe_dense_gemm_bf16_noalloc",
-    "moe_align_zero",
+    "moe_align_zero", "moe_dense_splitk_ways", "moe_dense_gemm_bf16_partials",
+    "moe_combine_partials",
 )
 
 UNION_MAX_IDS = 1024  # MOE_UNION_MAX_IDS: rows * top_k of moe_row_union
@@ -79,6 +81,11 @@ _SIGNATURES = {
         [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _f32, _vp],
         ctypes.c_int),
     "swiglu_clamp": ([_vp, _vp, _i64, _vp, _i64, _i32, _i32, _f32, _vp], ctypes.c_int),
+    "moe_combine_partials": ([_vp, _i64, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32,
+                              _vp], ctypes.c_int),
+    "moe_dense_splitk_ways": ([_i32, _i32], ctypes.c_int32),
+    "moe_dense_gemm_bf16_partials": ([_vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32, _i64, _vp],
+                                     ctypes.c_int),
     "moe_combine": ([_vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
                     ctypes.c_int),
     "moe_w4a16_dequant_bf16": ([_vp, _vp, _f32, _vp, _i32, _i32, _vp], ctypes.c_int),
@@ -396,8 +403,25 @@ def swiglu_clamp(gate, up, out, limit: float, stream=None) -> None:
         _p(gate), _p(up), ld_in, _p(out), ld_out, rows, n, float(limit), _stream(stream)))
 
 
+class SharedPartials:
+    """The shared expert's down projection as FP32 split-K partial sums: ``partials`` a
+    contiguous float32 ``[ways, rows, hidden]`` device tensor (moe_dense_gemm_bf16_partials).
+    Passed as moe_combine's ``shared``, it is reduced inside the combine
+    (moe_combine_partials), with the bits of the BF16 output moe_dense_gemm_bf16 writes."""
+
+    def __init__(self, partials):
+        import torch
+
+        _want(partials, torch.float32, "partials")
+        if partials.dim() != 3 or not partials.is_contiguous() or not partials.is_cuda:
+            raise ValueError("partials: expected a contiguous [ways, rows, hidden] device tensor")
+        self.partials = partials
+        self.ways = partials.shape[0]
+
+
 def moe_combine(expert_out, token_to_perm, topk_weights, out, shared=None, stream=None) -> None:
-    """``out[r] = sum_j w[r, j] * expert_out[token_to_perm[r, j]] (+ shared[r])``."""
+    """``out[r] = sum_j w[r, j] * expert_out[token_to_perm[r, j]] (+ shared[r])``. ``shared``
+    is a BF16 ``[rows, H]`` view, a ``SharedPartials`` (moe_combine_partials) or None."""
     import torch
 
     expert_out, ld_e = _bf16_matrix(expert_out, "expert_out")
@@ -412,12 +436,30 @@ def moe_combine(expert_out, token_to_perm, topk_weights, out, shared=None, strea
     hidden = out.shape[1]
     if expert_out.shape[1] < hidden or out.shape[0] < rows:
         raise ValueError("shape mismatch")
+    if isinstance(shared, SharedPartials):
+        if tuple(shared.partials.shape[1:]) != (rows, hidden):
+            raise ValueError(f"shared partials {tuple(shared.partials.shape)} do not match "
+                             f"{rows} rows x {hidden}")
+        _check("moe_combine_partials", load().moe_combine_partials(
+            _p(expert_out), ld_e, expert_out.shape[0], _p(token_to_perm), _p(topk_weights),
+            _p(shared.partials), shared.ways, _p(out), ld_out, rows, hidden, top_k,
+            _stream(stream)))
+        return
     ld_s = 0
     if shared is not None:
         shared, ld_s = _bf16_matrix(shared, "shared")
     _check("moe_combine", load().moe_combine(
         _p(expert_out), ld_e, expert_out.shape[0], _p(token_to_perm), _p(topk_weights),
         _p(shared), ld_s, _p(out), ld_out, rows, hidden, top_k, _stream(stream)))
+
+
+def moe_combine_partials(expert_out, token_to_perm, topk_weights, out, partials: SharedPartials,
+                         stream=None) -> None:
+    """moe_combine with the shared term reduced from split-K partials (same bits as the
+    BF16 output of the split-K down projection)."""
+    if not isinstance(partials, SharedPartials):
+        raise TypeError("partials: expected a SharedPartials")
+    moe_combine(expert_out, token_to_perm, topk_weights, out, partials, stream)
 
 
 def moe_w4a16_dequant_bf16(packed, scales, scale2: float, out, stream=None) -> None:
@@ -497,6 +539,33 @@ def moe_dense_gemm_bf16(a, b, c, stream=None, workspace=None) -> None:
     wp, wb = _workspace(workspace)
     _check("moe_dense_gemm_bf16", load().moe_dense_gemm_bf16(
         _p(a), lda, _p(b), ldb, _p(c), ldc, m, n, k, wp, wb, _stream(stream)))
+
+
+def moe_dense_splitk_ways(m: int, k: int) -> int:
+    """The K split count of the split-K form for m rows at this k."""
+    return int(load().moe_dense_splitk_ways(int(m), int(k)))
+
+
+def moe_dense_gemm_bf16_partials(a, b, partials, stream=None) -> SharedPartials:
+    """The split-K form's FP32 partial sums of ``a [M, K] @ b [N, K]^T`` into the front of
+    the contiguous float32 device tensor ``partials`` (at least ways x M x N elements,
+    ways = moe_dense_splitk_ways(M, K)); returns them as a ``[ways, M, N]``
+    ``SharedPartials`` view."""
+    import torch
+
+    a, lda = _bf16_matrix(a, "a")
+    b, ldb = _bf16_matrix(b, "b")
+    _want(partials, torch.float32, "partials")
+    if not partials.is_contiguous():
+        raise ValueError("partials must be contiguous")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    ways = moe_dense_splitk_ways(m, k)
+    _check("moe_dense_gemm_bf16_partials", load().moe_dense_gemm_bf16_partials(
+        _p(a), lda, _p(b), ldb, _p(partials), m, n, k, partials.numel() * 4, _stream(stream)))
+    return SharedPartials(partials.view(-1)[:ways * m * n].view(ways, m, n))
 
 
 def moe_dense_gemm_bf16_noalloc(a, b, c, stream=None) -> None:
@@ -579,6 +648,26 @@ class SharedExpert:
         moe_dense_gate_up_swiglu_bf16(x, self.gate_w, self.up_w, act, limit, stream, ws)
         moe_dense_gemm_bf16(act, self.down_w, out, stream, ws)
         return out
+
+    def for_combine(self, x, limit: float, stream=None):
+        """The combine's shared term for the rows of ``x``: in the split-K form, the down
+        projection's FP32 partial sums (a ``SharedPartials`` in the workspace, which
+        moe_combine reduces: the same bits as __call__'s output, one launch fewer); else
+        __call__'s BF16 output. The partials stay valid until the next call on this
+        shared expert is enqueued."""
+        import torch
+
+        rows = x.shape[0]
+        if rows > self.act.shape[0]:
+            raise ValueError(f"{rows} rows exceed the {self.act.shape[0]} the buffers hold")
+        ws = self.workspace if rows >= self.SPLIT_K_MIN_ROWS else None
+        if ws is None:
+            return self(x, limit, stream)
+        act = self.act[:rows]
+        moe_dense_gate_up_swiglu_bf16(x, self.gate_w, self.up_w, act, limit, stream, ws)
+        # the workspace's partial tiles are read by the gate/up reduction before (stream
+        # order) the down projection's partials overwrite them
+        return moe_dense_gemm_bf16_partials(act, self.down_w, ws.view(torch.float32), stream)
 
 
 class ExpertTable:
@@ -667,8 +756,10 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     that are not present add zero. When every down-projection entry is present the down
     GEMM writes every row the combine reads (each valid slot's row lies in its expert's
     segment), so the zeroing is skipped.
-    ``shared`` is the combine's shared term: a ``[rows, H]`` BF16 tensor, or a
-    ``SharedExpert``, which is then run over ``x`` after the routed experts."""
+    ``shared`` is the combine's shared term: a ``[rows, H]`` BF16 tensor, a
+    ``SharedPartials``, or a ``SharedExpert``, which is then run over ``x`` after the routed
+    experts (its down projection's split-K reduction inside the combine when it runs in
+    the split-K form: same bits)."""
     _same_experts(gate_up, down)
     rows, top_k = topk_ids.shape
     s = rows * top_k
@@ -687,7 +778,7 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
     moe_w4a16_grouped_gemm(ws.act, down, ws.expert_offsets, ws.expert_out, None, max_rows=s,
                            stream=stream)
     if isinstance(shared, SharedExpert):
-        shared = shared(x, limit, stream)
+        shared = shared.for_combine(x, limit, stream)
     moe_combine(ws.expert_out[:s], ws.token_to_perm, topk_weights, out, shared, stream)
 
 
@@ -760,5 +851,5 @@ def moe_layer_decode(x, topk_ids, topk_weights, gate_up: ExpertTable, down: Expe
     moe_w4a16_gemv_union(ws.act, down, ws.u_eid, u_slot, ws.expert_out, rows, top_k,
                          a_per_slot=True, stream=stream)
     if isinstance(shared, SharedExpert):
-        shared = shared(x, limit, stream)
+        shared = shared.for_combine(x, limit, stream)
     moe_combine(ws.expert_out[:t], ws.slot_perm[:t], topk_weights, out, shared, stream)

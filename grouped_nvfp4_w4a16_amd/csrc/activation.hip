@@ -12,6 +12,7 @@
 // stores and compute in FP32; a block of 256 threads covers 2048 columns of one row.
 #include "buffer_io.h"
 #include "common.h"
+#include "nvfp4_decode.h"  // moe::pack_bf16x2: the rounding the dense GEMM's output uses
 #include "swiglu.h"
 
 namespace {
@@ -39,6 +40,38 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
 }
 
+// The shared term of 8 columns: BF16 values of `shared`, or, with `sp` (FP32 split-K
+// partials [ways][rows][hidden] of the shared expert's down projection), their sum in split
+// order rounded to BF16 as the dense GEMM rounds its output, so both give the same bits.
+__device__ __forceinline__ void add_shared(float (&acc)[8], const uint16_t *__restrict__ shared,
+                                           int64_t ld_s, const float *__restrict__ sp,
+                                           int32_t sp_ways, int64_t sp_stride, int row, int col,
+                                           int32_t hidden) {
+  if (sp != nullptr) {  // uniform
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const f32x4_t *q =
+        reinterpret_cast<const f32x4_t *>(sp + static_cast<int64_t>(row) * hidden + col);
+    f32x4_t s0 = q[0], s1 = q[1];
+    for (int w = 1; w < sp_ways; ++w) {
+      const f32x4_t *qw = reinterpret_cast<const f32x4_t *>(
+          sp + w * sp_stride + static_cast<int64_t>(row) * hidden + col);
+      s0 += qw[0];
+      s1 += qw[1];
+    }
+    const uint4 v = make_uint4(moe::pack_bf16x2(s0[0], s0[1]), moe::pack_bf16x2(s0[2], s0[3]),
+                               moe::pack_bf16x2(s1[0], s1[1]), moe::pack_bf16x2(s1[2], s1[3]));
+    float sh[8];
+    unpack8(v, sh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += sh[i];
+  } else if (shared != nullptr) {
+    float sh[8];
+    unpack8(*reinterpret_cast<const uint4 *>(shared + static_cast<size_t>(row) * ld_s + col), sh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += sh[i];
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void swiglu_clamp_kernel(
     const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up, int64_t ld_in,
     uint16_t *__restrict__ out, int64_t ld_out, int32_t n, float limit) {
@@ -57,8 +90,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_clamp_kernel(
 __global__ __launch_bounds__(kThreads) void moe_combine_kernel(
     const uint16_t *__restrict__ expert_out, int64_t ld_e, int32_t expert_rows,
     const int32_t *__restrict__ token_to_perm, const float *__restrict__ weights,
-    const uint16_t *__restrict__ shared, int64_t ld_s, uint16_t *__restrict__ out,
-    int64_t ld_out, int32_t hidden, int32_t top_k) {
+    const uint16_t *__restrict__ shared, int64_t ld_s, const float *__restrict__ sp,
+    int32_t sp_ways, int64_t sp_stride, uint16_t *__restrict__ out, int64_t ld_out,
+    int32_t hidden, int32_t top_k) {
   const int row = blockIdx.y;
   const int col = (blockIdx.x * kThreads + threadIdx.x) * 8;
   if (col >= hidden) return;
@@ -72,12 +106,7 @@ __global__ __launch_bounds__(kThreads) void moe_combine_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
   }
-  if (shared != nullptr) {
-    float s[8];
-    unpack8(*reinterpret_cast<const uint4 *>(shared + static_cast<size_t>(row) * ld_s + col), s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += s[i];
-  }
+  add_shared(acc, shared, ld_s, sp, sp_ways, sp_stride, row, col, hidden);
   *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(acc);
 }
 
@@ -99,8 +128,9 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint16_t *__restric
 __global__ __launch_bounds__(kThreads) void moe_combine8_kernel(
     const uint16_t *__restrict__ expert_out, int64_t ld_e, int32_t expert_rows,
     const int32_t *__restrict__ token_to_perm, const float *__restrict__ weights,
-    const uint16_t *__restrict__ shared, int64_t ld_s, uint16_t *__restrict__ out,
-    int64_t ld_out, int32_t hidden) {
+    const uint16_t *__restrict__ shared, int64_t ld_s, const float *__restrict__ sp,
+    int32_t sp_ways, int64_t sp_stride, uint16_t *__restrict__ out, int64_t ld_out,
+    int32_t hidden) {
   constexpr int kK = 8;
   const int row = blockIdx.y;
   const int col = (blockIdx.x * kThreads + threadIdx.x) * 8;
@@ -132,12 +162,7 @@ __global__ __launch_bounds__(kThreads) void moe_combine8_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += w[j] * f[i];
   }
-  if (shared != nullptr) {
-    float sh[8];
-    unpack8(*reinterpret_cast<const uint4 *>(shared + static_cast<size_t>(row) * ld_s + col), sh);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += sh[i];
-  }
+  add_shared(acc, shared, ld_s, sp, sp_ways, sp_stride, row, col, hidden);
   *reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * ld_out + col) = pack8(acc);
 }
 
@@ -179,33 +204,64 @@ extern "C" int swiglu_clamp(const uint16_t *gate, const uint16_t *up, int64_t ld
                      up, ld_in, out, ld_out, n, limit);
 }
 
+namespace {
+
+int combine_launch(const char *name, const uint16_t *expert_out, int64_t ld_e,
+                   int32_t expert_rows, const int32_t *token_to_perm,
+                   const float *topk_weights, const uint16_t *shared, int64_t ld_s,
+                   const float *sp, int32_t sp_ways, uint16_t *out, int64_t ld_out, int32_t rows,
+                   int32_t hidden, int32_t top_k, void *stream) {
+  MOE_REQUIRE(rows >= 0 && hidden >= 0 && hidden % 8 == 0,
+              "%s: need rows >= 0 and hidden >= 0 a multiple of 8", name);
+  MOE_REQUIRE(top_k >= 1 && expert_rows >= 0, "%s: need top_k >= 1, expert_rows >= 0", name);
+  MOE_REQUIRE(ld_e >= hidden && ld_e % 8 == 0 && ld_out >= hidden && ld_out % 8 == 0,
+              "%s: leading dimensions must be >= hidden and multiples of 8", name);
+  MOE_REQUIRE(shared == nullptr || (ld_s >= hidden && ld_s % 8 == 0),
+              "%s: ld_s must be >= hidden and a multiple of 8", name);
+  MOE_REQUIRE(rows <= 65535, "%s: rows must be <= 65535 (got %d)", name, rows);
+  if (rows == 0 || hidden == 0) return MOE_OK;
+  MOE_REQUIRE(expert_out && token_to_perm && topk_weights && out,
+              "%s: a required pointer is NULL", name);
+  MOE_REQUIRE(moe::aligned16(expert_out) && moe::aligned16(out) &&
+                  (shared == nullptr || moe::aligned16(shared)) &&
+                  (sp == nullptr || moe::aligned16(sp)),
+              "%s: BF16 and FP32 pointers must be 16-byte aligned", name);
+  const int64_t sp_stride = static_cast<int64_t>(rows) * hidden;
+  const dim3 grid((hidden + kColsPerBlock - 1) / kColsPerBlock, rows);
+  // top_k 8 with expert rows below 2 GiB (buffer offsets are 32-bit; an excluded slot's
+  // offset 2^31 must lie past the end): all slot rows in flight at once.
+  if (top_k == 8 && static_cast<uint64_t>(expert_rows) * ld_e * 2 < (1ull << 31))
+    return moe::launch(name, moe_combine8_kernel, grid, dim3(kThreads), 0, stream, expert_out,
+                       ld_e, expert_rows, token_to_perm, topk_weights, shared, ld_s, sp, sp_ways,
+                       sp_stride, out, ld_out, hidden);
+  return moe::launch(name, moe_combine_kernel, grid, dim3(kThreads), 0, stream, expert_out,
+                     ld_e, expert_rows, token_to_perm, topk_weights, shared, ld_s, sp, sp_ways,
+                     sp_stride, out, ld_out, hidden, top_k);
+}
+
+}  // namespace
+
 extern "C" int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
                            const int32_t *token_to_perm, const float *topk_weights,
                            const uint16_t *shared, int64_t ld_s, uint16_t *out, int64_t ld_out,
                            int32_t rows, int32_t hidden, int32_t top_k, void *stream) {
   moe::clear_error();
-  MOE_REQUIRE(rows >= 0 && hidden >= 0 && hidden % 8 == 0,
-              "moe_combine: need rows >= 0 and hidden >= 0 a multiple of 8");
-  MOE_REQUIRE(top_k >= 1 && expert_rows >= 0, "moe_combine: need top_k >= 1, expert_rows >= 0");
-  MOE_REQUIRE(ld_e >= hidden && ld_e % 8 == 0 && ld_out >= hidden && ld_out % 8 == 0,
-              "moe_combine: leading dimensions must be >= hidden and multiples of 8");
-  MOE_REQUIRE(shared == nullptr || (ld_s >= hidden && ld_s % 8 == 0),
-              "moe_combine: ld_s must be >= hidden and a multiple of 8");
-  MOE_REQUIRE(rows <= 65535, "moe_combine: rows must be <= 65535 (got %d)", rows);
-  if (rows == 0 || hidden == 0) return MOE_OK;
-  MOE_REQUIRE(expert_out && token_to_perm && topk_weights && out,
-              "moe_combine: a required pointer is NULL");
-  MOE_REQUIRE(moe::aligned16(expert_out) && moe::aligned16(out) &&
-                  (shared == nullptr || moe::aligned16(shared)),
-              "moe_combine: BF16 pointers must be 16-byte aligned");
-  const dim3 grid((hidden + kColsPerBlock - 1) / kColsPerBlock, rows);
-  // top_k 8 with expert rows below 2 GiB (buffer offsets are 32-bit; an excluded slot's
-  // offset 2^31 must lie past the end): all slot rows in flight at once.
-  if (top_k == 8 && static_cast<uint64_t>(expert_rows) * ld_e * 2 < (1ull << 31))
-    return moe::launch("moe_combine", moe_combine8_kernel, grid, dim3(kThreads), 0, stream,
-                       expert_out, ld_e, expert_rows, token_to_perm, topk_weights, shared,
-                       ld_s, out, ld_out, hidden);
-  return moe::launch("moe_combine", moe_combine_kernel, grid, dim3(kThreads), 0, stream,
-                     expert_out, ld_e, expert_rows, token_to_perm, topk_weights, shared, ld_s,
-                     out, ld_out, hidden, top_k);
+  return combine_launch("moe_combine", expert_out, ld_e, expert_rows, token_to_perm,
+                        topk_weights, shared, ld_s, nullptr, 0, out, ld_out, rows, hidden, top_k,
+                        stream);
+}
+
+extern "C" int moe_combine_partials(const uint16_t *expert_out, int64_t ld_e,
+                                    int32_t expert_rows, const int32_t *token_to_perm,
+                                    const float *topk_weights, const float *shared_partials,
+                                    int32_t ways, uint16_t *out, int64_t ld_out, int32_t rows,
+                                    int32_t hidden, int32_t top_k, void *stream) {
+  moe::clear_error();
+  MOE_REQUIRE(ways >= 1 && ways <= 64, "moe_combine_partials: ways must be in [1, 64] (got %d)",
+              ways);
+  if (rows > 0 && hidden > 0)
+    MOE_REQUIRE(shared_partials != nullptr, "moe_combine_partials: shared_partials is NULL");
+  return combine_launch("moe_combine_partials", expert_out, ld_e, expert_rows, token_to_perm,
+                        topk_weights, nullptr, 0, shared_partials, ways, out, ld_out, rows,
+                        hidden, top_k, stream);
 }

@@ -304,8 +304,9 @@ SplitKShape splitk_shape(int32_t m, int32_t n, int32_t k, bool swiglu) {
 
 // Phase 1: the partial tile of (row tile, column tile, split) for rows A and B rows over
 // the split's K range. Fused: B tile rows [0, 64) are gate rows n0 + r of b0 and [64, 128)
-// the same rows of b1 (up).
-template <bool kSwiglu>
+// the same rows of b1 (up). kRowMajor (plain form only): the partials go to an FP32
+// [split][M][N] array instead, for a consumer that reads whole rows (the combine).
+template <bool kSwiglu, bool kRowMajor = false>
 __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t M, const uint16_t *__restrict__ b0,
     const uint16_t *__restrict__ b1, int64_t ldb, int32_t N, int32_t K,
@@ -448,13 +449,30 @@ __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
     }
   }
 
-  // The partial tile in fragment order: [split][tile][wave][mt * 4 + nt][lane].
-  f32x4_t *mine = partials + (static_cast<int64_t>(ks) * TM * TN + tm * TN + tn) * kLFrags +
-                  wave * 1024;
+  if constexpr (kRowMajor) {
+    static_assert(!kSwiglu, "row-major partials: plain form only");
+    // acc[mt][nt][i]: row m0 + 64 wm + 16 mt + r16, column n0 + 64 wn + 16 nt + 4 kb + i
+    // (N is a multiple of 16, so a fragment's four columns are all in range or all out).
+    float *mine = reinterpret_cast<float *>(partials) + static_cast<int64_t>(ks) * M * N;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = m0 + 64 * wm + 16 * mt + r16;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) mine[(mt * 4 + nt) * 64 + lane] = acc[mt][nt];
+      for (int nt = 0; nt < 4; ++nt) {
+        const int col = n0 + 64 * wn + 16 * nt + 4 * kb;
+        if (row < M && col < N)
+          *reinterpret_cast<f32x4_t *>(mine + static_cast<int64_t>(row) * N + col) = acc[mt][nt];
+      }
+    }
+  } else {
+    // The partial tile in fragment order: [split][tile][wave][mt * 4 + nt][lane].
+    f32x4_t *mine = partials + (static_cast<int64_t>(ks) * TM * TN + tm * TN + tn) * kLFrags +
+                    wave * 1024;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) mine[(mt * 4 + nt) * 64 + lane] = acc[mt][nt];
+  }
 }
 
 // Phase 2: output fragment g of the tile grid (fragment f = g % kOutFrags of tile
@@ -532,6 +550,27 @@ int launch_splitk(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0,
                      dim3(static_cast<unsigned>((frags + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, stream, partials, sh.tiles_n, sh.tiles, sh.ways, c, ldc,
                      m, n, limit);
+}
+
+// Phase 1 alone with row-major partials: ways x m x n FP32 (ways = splitk_ways(m, k)).
+int launch_partials_row_major(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b,
+                              int64_t ldb, int32_t n, int32_t k, float *partials,
+                              void *stream) {
+  const char *name = "moe_dense_gemm_bf16_partials";
+  const SplitKShape sh = splitk_shape(m, n, k, false);
+  MOE_REQUIRE(sh.tiles_n <= 65535 && sh.tiles_m <= 65535,
+              "%s: too many tiles for the split-K form", name);
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(dense_partial_kernel<false, true>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLLds);
+  if (attr_err != hipSuccess) {
+    moe::set_error("%s: cannot raise the LDS limit: %s", name, hipGetErrorString(attr_err));
+    return MOE_ELAUNCH;
+  }
+  const dim3 grid(static_cast<unsigned>(sh.tiles_n), static_cast<unsigned>(sh.tiles_m),
+                  static_cast<unsigned>(sh.ways));
+  return moe::launch(name, dense_partial_kernel<false, true>, grid, dim3(kThreads), kLLds,
+                     stream, a, lda, m, b, b, ldb, n, k, reinterpret_cast<f32x4_t *>(partials));
 }
 
 struct Tile {
@@ -726,4 +765,26 @@ extern "C" int moe_dense_gate_up_swiglu_bf16(const uint16_t *a, int64_t lda,
     return launch_splitk<true>(a, lda, m, gate_w, up_w, ldw, act, ld_act, inter, k, limit,
                                workspace, workspace_bytes, stream);
   return dispatch<true>(a, lda, m, gate_w, up_w, ldw, act, ld_act, inter, k, limit, stream);
+}
+
+extern "C" int32_t moe_dense_splitk_ways(int32_t m, int32_t k) {
+  if (m <= 0 || k <= 0 || k % kLK != 0) return 1;
+  return splitk_ways(m, k);
+}
+
+extern "C" int moe_dense_gemm_bf16_partials(const uint16_t *a, int64_t lda, const uint16_t *b,
+                                            int64_t ldb, float *partials, int32_t m, int32_t n,
+                                            int32_t k, int64_t partials_bytes, void *stream) {
+  moe::clear_error();
+  const char *name = "moe_dense_gemm_bf16_partials";
+  // c is not written: the partials stand in for it in the shared checks.
+  const int rc = check_dense_args(name, a, lda, b, b, ldb, partials, n, m, n, k);
+  if (rc != MOE_OK || m == 0 || n == 0) return rc;
+  const int64_t need = static_cast<int64_t>(splitk_ways(m, k)) * m * n * 4;
+  MOE_REQUIRE_CODE(partials_bytes >= need, MOE_ECAPACITY,
+                   "%s: the partials buffer holds %lld bytes, m %d, n %d, k %d need %lld", name,
+                   static_cast<long long>(partials_bytes), m, n, k,
+                   static_cast<long long>(need));
+  MOE_REQUIRE(moe::aligned16(partials), "%s: partials must be 16-byte aligned", name);
+  return launch_partials_row_major(a, lda, m, b, ldb, n, k, partials, stream);
 }

@@ -16,6 +16,9 @@
  *   moe_dense_gate_up_swiglu_bf16, moe_dense_gemm_bf16
  *                           the shared expert (a BF16 SwiGLU MLP over all rows), whose
  *                           output is moe_combine's `shared` term
+ *   moe_dense_gemm_bf16_partials, moe_combine_partials
+ *                           the shared expert's down projection left as split-K partial
+ *                           sums, reduced inside the combine (same bits, one launch less)
  *   moe_row_union, moe_w4a16_gemv_union, moe_w4a16_gemv_union_swiglu
  *                           the decode / verify path for a few rows: the union of the
  *                           rows' experts (no sort) and one sweep of each union expert,
@@ -276,6 +279,27 @@ int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
                 int32_t rows, int32_t hidden, int32_t top_k, void *stream);
 
 /*
+ * moe_combine_partials - moe_combine with the shared term taken from the shared expert's
+ * down projection in its split-K partial form (moe_dense_gemm_bf16_partials) instead of
+ * its BF16 output: shared[r, h] = bf16( sum_{s < ways} shared_partials[s, r, h] ), summed
+ * in FP32 in split order and rounded as moe_dense_gemm_bf16 rounds its output, so the
+ * result has the bits of moe_dense_gemm_bf16 (split-K form) followed by moe_combine. The
+ * down projection's split-K reduction runs inside the combine ([FWD] forward_moe adds
+ * the shared expert's output in this launch), which saves that reduction's launch.
+ *
+ *   shared_partials  float [ways, rows, hidden], contiguous (hidden fastest)
+ *   ways             the split count the partials were written with, in [1, 64]
+ *   the other arguments as moe_combine (no shared, ld_s).
+ * Requirements (else MOE_EINVAL): those of moe_combine; 1 <= ways <= 64; shared_partials
+ * non-NULL and 16-byte aligned when rows * hidden > 0.
+ */
+int moe_combine_partials(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
+                         const int32_t *token_to_perm, const float *topk_weights,
+                         const float *shared_partials, int32_t ways, uint16_t *out,
+                         int64_t ld_out, int32_t rows, int32_t hidden, int32_t top_k,
+                         void *stream);
+
+/*
  * moe_zero_rows - c[r, j] = 0 for r < rows, j < cols: forward_moe's zero-first step on
  * expert_out ([FWD] forward_moe), so that the rows of experts absent from the table
  * (never written by the down GEMM) add zero in moe_combine. A kernel, not a memset, so
@@ -348,6 +372,32 @@ int moe_dense_gemm_bf16_noalloc(const uint16_t *a, int64_t lda, const uint16_t *
  * Returns 0 when m <= 0, n <= 0 or k < 0. Enqueues nothing.
  */
 int64_t moe_dense_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t swiglu);
+
+/*
+ * moe_dense_splitk_ways - host-side query: the number of K splits the split-K form uses
+ * for m rows at this k (the count in moe_dense_workspace_bytes). Returns 1 when m <= 0,
+ * k <= 0 or k is not a multiple of 64. Enqueues nothing.
+ */
+int32_t moe_dense_splitk_ways(int32_t m, int32_t k);
+
+/*
+ * moe_dense_gemm_bf16_partials - the first launch of moe_dense_gemm_bf16's split-K form
+ * alone, its FP32 partial sums written row-major for moe_combine_partials:
+ *
+ *   partials[s, i, j] = sum over split s's K range of a[i, k] * b[j, k]   (FP32)
+ *
+ * with ways = moe_dense_splitk_ways(m, k) splits of equal length in K order. The
+ * per-element values are the ones moe_dense_gemm_bf16's split-K reduction sums.
+ *
+ *   a, b, sizes, strides  as moe_dense_gemm_bf16 (n = output width)
+ *   partials              float [ways, m, n], contiguous; partials_bytes its size in bytes
+ * Requirements (else MOE_EINVAL / MOE_ECAPACITY): those of moe_dense_gemm_bf16 with c =
+ * partials and ldc = n; partials 16-byte aligned; partials_bytes >= ways * m * n * 4
+ * (MOE_ECAPACITY, nothing enqueued).
+ */
+int moe_dense_gemm_bf16_partials(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+                                 float *partials, int32_t m, int32_t n, int32_t k,
+                                 int64_t partials_bytes, void *stream);
 
 /*
  * moe_dense_gate_up_swiglu_bf16 - the gate and up projections of forward_dense and its

@@ -68,6 +68,15 @@ def test_align_all_slots_one_expert_and_all_invalid(hip):
     got = _run(hip, bad, 16)
     _check(got, bad, 16)
     assert np.all(got["sorted_token_ids"] == -1) and got["counters"][1] == 40
+    # the same past 64 slots (the 1024-thread form): every id invalid, and one expert only
+    bad = np.full((300, 8), 64, np.int32)
+    got = _run(hip, bad, 64)
+    _check(got, bad, 64)
+    assert np.all(got["sorted_token_ids"] == -1) and got["counters"].tolist() == [0, 2400]
+    one = np.zeros((100, 8), np.int32)
+    got = _run(hip, one, 1)
+    _check(got, one, 1)
+    assert got["expert_offsets"].tolist() == [0, 800]
 
 
 def test_align_empty_input(hip):
