@@ -263,6 +263,7 @@ constexpr int kLRowBytes = kLK * 2;             // 128: staged rows are not padd
 constexpr int kLOperand = kLT * kLRowBytes;     // 16 KB: one operand's stage
 constexpr int kLStage = 2 * kLOperand;          // A and B
 constexpr int kLLds = 2 * kLStage;              // double buffered: 64 KB
+constexpr int kLDmaStages = 3;                   // LDS-direct stages (96 KB, one block per CU)
 constexpr int kLPieces = kLT * (kLRowBytes / 16) / kThreads;  // 16-byte pieces per thread
 constexpr int kLFrags = kWaves * 16 * 64;       // f32x4 fragments per tile partial
 constexpr int kLMaxWays = 4;
@@ -306,7 +307,9 @@ SplitKShape splitk_shape(int32_t m, int32_t n, int32_t k, bool swiglu) {
 // the split's K range. Fused: B tile rows [0, 64) are gate rows n0 + r of b0 and [64, 128)
 // the same rows of b1 (up). kRowMajor (plain form only): the partials go to an FP32
 // [split][M][N] array instead, for a consumer that reads whole rows (the combine).
-template <bool kSwiglu, bool kRowMajor = false>
+// kStages = 0: staged through registers, double-buffered LDS (64 KB: two blocks per CU);
+// kStages > 0: loaded straight into LDS, kStages stages (one block per CU).
+template <bool kSwiglu, bool kRowMajor, int kStages>
 __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
     const uint16_t *__restrict__ a, int64_t lda, int32_t M, const uint16_t *__restrict__ b0,
     const uint16_t *__restrict__ b1, int64_t ldb, int32_t N, int32_t K,
@@ -417,36 +420,87 @@ __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], xf[mt], acc[mt][nt], 0, 0, 0);
   };
 
-  // Step s reads LDS buffer s & 1. The global loads run kDepth steps ahead in kDepth
-  // register sets: set s % kDepth holds step s from its load until it is staged (at the
-  // end of step s - 1), then takes step s + kDepth during step s, so staging step s + 1
-  // waits only for loads issued two steps earlier. The refill is split over the step, the
-  // A rows before the first 32-k half of the products and the B rows before the second
-  // (one burst of all eight loads at the top measured 1-2 us slower at the shared
-  // expert's gate/up, and two or four register sets slower than three), and pinned there
-  // with scheduling barriers. The stages are unconditional (past the last step the loads
-  // read nothing and the stage writes zeros to a buffer no step reads): a stage behind a
-  // branch lets the compiler sink the loads into it, next to their wait.
-  constexpr int kDepth = 3, kUnroll = 6;  // kUnroll: a multiple of kDepth and of 2
-  Regs r[kDepth];
-#pragma unroll
-  for (int i = 0; i < kDepth; ++i) load_step(r[i], i);
-  stage_step(r[0], 0);
-  __syncthreads();
-  for (int j = 0; j < steps; j += kUnroll) {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int s = j + u;  // u % kDepth == s % kDepth, u & 1 == s & 1
-      if (s >= steps) break;
-      load_half(r[u % kDepth], s + kDepth, false);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_half(u & 1, 0);
-      load_half(r[u % kDepth], s + kDepth, true);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_half(u & 1, 1);
-      stage_step(r[(u + 1) % kDepth], (u + 1) & 1);
-      __syncthreads();
+  if constexpr (kStages == 0) {
+    // Step s reads LDS buffer s & 1. The global loads run kDepth steps ahead in kDepth
+    // register sets: set s % kDepth holds step s from its load until it is staged (at the
+    // end of step s - 1), then takes step s + kDepth during step s, so staging step s + 1
+    // waits only for loads issued two steps earlier. The refill is split over the step, the
+    // A rows before the first 32-k half of the products and the B rows before the second
+    // (one burst of all eight loads at the top measured 1-2 us slower at the shared
+    // expert's gate/up, and two or four register sets slower than three), and pinned there
+    // with scheduling barriers. The stages are unconditional (past the last step the loads
+    // read nothing and the stage writes zeros to a buffer no step reads): a stage behind a
+    // branch lets the compiler sink the loads into it, next to their wait.
+    constexpr int kDepth = 3, kUnroll = 6;  // kUnroll: a multiple of kDepth and of 2
+    Regs r[kDepth];
+  #pragma unroll
+    for (int i = 0; i < kDepth; ++i) load_step(r[i], i);
+    stage_step(r[0], 0);
+    __syncthreads();
+    for (int j = 0; j < steps; j += kUnroll) {
+  #pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int s = j + u;  // u % kDepth == s % kDepth, u & 1 == s & 1
+        if (s >= steps) break;
+        load_half(r[u % kDepth], s + kDepth, false);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(u & 1, 0);
+        load_half(r[u % kDepth], s + kDepth, true);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(u & 1, 1);
+        stage_step(r[(u + 1) % kDepth], (u + 1) & 1);
+        __syncthreads();
+      }
     }
+  } else {
+    // Straight into LDS (buffer_load ... lds): a wave instruction fills 8 rows x 128 bytes
+    // of a stage, lane l writing row 8 w + 32 i + l / 8 at physical piece l % 8, so it
+    // loads logical piece (l % 8) ^ (l / 8) of that row (the swizzle of the register
+    // path). Stage s goes to buffer s % kStages; stages run kStages - 1 steps ahead. The
+    // waits are explicit (the wave's own loads of stage s, then a barrier for the other
+    // waves'); a plain s_barrier, not __syncthreads, so that the compiler does not add a
+    // full vmcnt(0) wait for the loads still in flight. With the registers free of
+    // staging, a block needs ~100 VGPRs.
+    uint32_t a_dma[kLPieces], b_dma[kLPieces];
+#pragma unroll
+    for (int i = 0; i < kLPieces; ++i) {
+      const int row = 8 * wave + 32 * i + (lane >> 3);
+      const int col = (lane & 7) ^ (lane >> 3);
+      a_dma[i] = static_cast<uint32_t>(row) * arow + 16u * col;
+      const int brow_i = kSwiglu ? (row & (kLT / 2 - 1)) : row;
+      b_dma[i] = static_cast<uint32_t>(brow_i) * brow + 16u * col;
+    }
+    const auto dma_step = [&](int j) {
+      const uint32_t dead = j < steps ? 0u : kNoLoad;
+      const int soff = j < steps ? (k_first + j) * kLRowBytes : 0;
+      uint8_t *sa = lds + (j % kStages) * kLStage, *sb = sa + kLOperand;
+#pragma unroll
+      for (int i = 0; i < kLPieces; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ar, (__attribute__((address_space(3))) void *)(sa + 1024 * wave + 4096 * i), 16,
+            static_cast<int>(a_dma[i] | dead), soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kSwiglu && i >= kLPieces / 2 ? br1 : br0,
+            (__attribute__((address_space(3))) void *)(sb + 1024 * wave + 4096 * i), 16,
+            static_cast<int>(b_dma[i] | dead), soff, 0, 0);
+      }
+    };
+    // s_waitcnt immediate for vmcnt(N), no expcnt or lgkmcnt wait: N = the loads of the
+    // kStages - 2 stages issued after stage s.
+    constexpr int kWaitN = 2 * kLPieces * (kStages - 2);
+    static_assert(kStages >= 2 && kWaitN < 64, "vmcnt holds 6 bits");
+    constexpr int kWaitImm = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+    for (int j = 0; j < kStages - 1; ++j) dma_step(j);
+    for (int s = 0; s < steps; ++s) {
+      __builtin_amdgcn_s_waitcnt(kWaitImm);  // this wave's loads of stage s are in LDS
+      __builtin_amdgcn_s_barrier();           // every wave's; and stage s - 1 is read
+      dma_step(s + kStages - 1);              // into stage s - 1's buffer
+      compute_half(s % kStages, 0);
+      compute_half(s % kStages, 1);
+    }
+    // The past-the-end stages' loads write LDS (zeros) too: they finish before the block.
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   if constexpr (kRowMajor) {
@@ -518,6 +572,46 @@ __global__ __launch_bounds__(kThreads) void dense_reduce_kernel(
   *reinterpret_cast<uint2 *>(c + static_cast<int64_t>(row) * ldc + col) = v;
 }
 
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus > 0 ? cus : 256;
+}
+
+// Phase 1 of the split-K form: the LDS-direct kernel when the grid fits one block per CU
+// (its 96 KB of LDS allow no second), else the register-staged one at two per CU.
+// Measured at the shared expert's shapes (H 6144, width 2048): 256 rows, 256 and 192
+// blocks, gate/up 31.4 -> 30.8 us and down 23.3 -> 22.0 us from cold caches; 1024 rows,
+// gate/up (256 blocks) 77.8 -> 73.8 us, but down (384 blocks) 52.4 -> 59.0 us, so the
+// larger grids keep the register-staged kernel.
+template <bool kSwiglu, bool kRowMajor>
+int launch_partial(const char *name, const SplitKShape &sh, const uint16_t *a, int64_t lda,
+                   int32_t m, const uint16_t *b0, const uint16_t *b1, int64_t ldb, int32_t n,
+                   int32_t k, f32x4_t *partials, void *stream) {
+  MOE_REQUIRE(sh.tiles_n <= 65535 && sh.tiles_m <= 65535,
+              "%s: too many tiles for the split-K form", name);
+  const dim3 grid(static_cast<unsigned>(sh.tiles_n), static_cast<unsigned>(sh.tiles_m),
+                  static_cast<unsigned>(sh.ways));
+  const bool direct = sh.tiles * sh.ways <= device_cus();
+  const auto kern = direct ? dense_partial_kernel<kSwiglu, kRowMajor, kLDmaStages>
+                           : dense_partial_kernel<kSwiglu, kRowMajor, 0>;
+  const int lds = direct ? kLDmaStages * kLStage : kLLds;
+  static const hipError_t attr_err[2] = {
+      hipFuncSetAttribute(reinterpret_cast<const void *>(dense_partial_kernel<kSwiglu, kRowMajor, 0>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLLds),
+      hipFuncSetAttribute(
+          reinterpret_cast<const void *>(dense_partial_kernel<kSwiglu, kRowMajor, kLDmaStages>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, kLDmaStages * kLStage)};
+  if (attr_err[direct ? 1 : 0] != hipSuccess) {
+    moe::set_error("%s: cannot raise the LDS limit: %s", name,
+                   hipGetErrorString(attr_err[direct ? 1 : 0]));
+    return MOE_ELAUNCH;
+  }
+  return moe::launch(name, kern, grid, dim3(kThreads), lds, stream, a, lda, m, b0, b1, ldb, n,
+                     k, partials);
+}
+
 template <bool kSwiglu>
 int launch_splitk(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0,
                   const uint16_t *b1, int64_t ldb, uint16_t *c, int64_t ldc, int32_t n,
@@ -530,20 +624,9 @@ int launch_splitk(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0,
                    static_cast<long long>(workspace_bytes), static_cast<long long>(sh.bytes));
   MOE_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
               "%s: the workspace must be 256-byte aligned", name);
-  MOE_REQUIRE(sh.tiles_n <= 65535 && sh.tiles_m <= 65535,
-              "%s: too many tiles for the split-K form", name);
-  static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(dense_partial_kernel<kSwiglu>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLLds);
-  if (attr_err != hipSuccess) {
-    moe::set_error("%s: cannot raise the LDS limit: %s", name, hipGetErrorString(attr_err));
-    return MOE_ELAUNCH;
-  }
   f32x4_t *partials = static_cast<f32x4_t *>(workspace);
-  const dim3 grid(static_cast<unsigned>(sh.tiles_n), static_cast<unsigned>(sh.tiles_m),
-                  static_cast<unsigned>(sh.ways));
-  const int rc = moe::launch(name, dense_partial_kernel<kSwiglu>, grid, dim3(kThreads), kLLds,
-                             stream, a, lda, m, b0, b1, ldb, n, k, partials);
+  const int rc = launch_partial<kSwiglu, false>(name, sh, a, lda, m, b0, b1, ldb, n, k,
+                                                partials, stream);
   if (rc != MOE_OK) return rc;
   const int64_t frags = sh.tiles * (kSwiglu ? kLFrags / 2 : kLFrags);
   return moe::launch(name, dense_reduce_kernel<kSwiglu>,
@@ -556,21 +639,9 @@ int launch_splitk(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b0,
 int launch_partials_row_major(const uint16_t *a, int64_t lda, int32_t m, const uint16_t *b,
                               int64_t ldb, int32_t n, int32_t k, float *partials,
                               void *stream) {
-  const char *name = "moe_dense_gemm_bf16_partials";
-  const SplitKShape sh = splitk_shape(m, n, k, false);
-  MOE_REQUIRE(sh.tiles_n <= 65535 && sh.tiles_m <= 65535,
-              "%s: too many tiles for the split-K form", name);
-  static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(dense_partial_kernel<false, true>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLLds);
-  if (attr_err != hipSuccess) {
-    moe::set_error("%s: cannot raise the LDS limit: %s", name, hipGetErrorString(attr_err));
-    return MOE_ELAUNCH;
-  }
-  const dim3 grid(static_cast<unsigned>(sh.tiles_n), static_cast<unsigned>(sh.tiles_m),
-                  static_cast<unsigned>(sh.ways));
-  return moe::launch(name, dense_partial_kernel<false, true>, grid, dim3(kThreads), kLLds,
-                     stream, a, lda, m, b, b, ldb, n, k, reinterpret_cast<f32x4_t *>(partials));
+  return launch_partial<false, true>("moe_dense_gemm_bf16_partials", splitk_shape(m, n, k, false),
+                                     a, lda, m, b, b, ldb, n, k,
+                                     reinterpret_cast<f32x4_t *>(partials), stream);
 }
 
 struct Tile {
@@ -597,13 +668,6 @@ Tile pick_tile(int M, int N, bool swiglu, int cus) {
     }
   }
   return best;
-}
-
-int device_cus() {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus > 0 ? cus : 256;
 }
 
 template <int kMT, int kNT, bool kSwiglu>
