@@ -503,7 +503,32 @@ __global__ __launch_bounds__(kThreads, 2) void dense_partial_kernel(
     __builtin_amdgcn_s_waitcnt(0);
   }
 
-  if constexpr (kRowMajor) {
+  if constexpr (kRowMajor && kStages >= 3) {
+    static_assert(!kSwiglu, "row-major partials: plain form only");
+    // The tile goes through LDS (free after the last step; 128 rows of 132 floats, the
+    // padding spreading a fragment's 16 rows over the banks), so that each store
+    // instruction writes two 512-byte row pieces instead of 16 rows x 64 bytes.
+    constexpr int kTS = kLT + 4;
+    static_assert(kLT * kTS * 4 <= kStages * kLStage, "the tile fits the stages");
+    float *t = reinterpret_cast<float *>(lds);
+    __builtin_amdgcn_s_barrier();  // every wave's operand reads are done (waited above)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        *reinterpret_cast<f32x4_t *>(t + (64 * wm + 16 * mt + r16) * kTS + 64 * wn + 16 * nt +
+                                     4 * kb) = acc[mt][nt];
+    __syncthreads();
+    float *mine = reinterpret_cast<float *>(partials) + static_cast<int64_t>(ks) * M * N;
+#pragma unroll
+    for (int i = 0; i < kLT * kLT / 4 / kThreads; ++i) {
+      const int q = tid + kThreads * i, r = q / (kLT / 4), c = 4 * (q % (kLT / 4));
+      const int row = m0 + r, col = n0 + c;
+      if (row < M && col < N)
+        *reinterpret_cast<f32x4_t *>(mine + static_cast<int64_t>(row) * N + col) =
+            *reinterpret_cast<const f32x4_t *>(t + r * kTS + c);
+    }
+  } else if constexpr (kRowMajor) {
     static_assert(!kSwiglu, "row-major partials: plain form only");
     // acc[mt][nt][i]: row m0 + 64 wm + 16 mt + r16, column n0 + 64 wn + 16 nt + 4 kb + i
     // (N is a multiple of 16, so a fragment's four columns are all in range or all out).
