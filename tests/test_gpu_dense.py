@@ -165,11 +165,14 @@ def test_gate_up_swiglu_bits_and_oracle(hip, m, inter, k, w_scale):
 
 # Split-K form (with a workspace): (m, n, k) with K split 4, 2 and 1 ways, ragged row and
 # column tiles, a column-tile count that does not divide by 8, the shared expert's shapes,
-# and 64-k steps per split of every remainder modulo 6 (the main loop runs six steps per
-# trip with three register sets; 1, 3, 5, 8, 11, 12, 16 and 24 steps here).
+# and 64-k steps per split of every remainder modulo 6 (the register-staged loop runs six
+# steps per trip with three register sets; 1, 3, 5, 8, 11, 12, 16 and 24 steps here).
+# Grids of at most one block per CU take the LDS-direct kernel; (520, 8192, 512) has 320
+# blocks and takes the register-staged one.
 SPLITK_SHAPES = [
     (1, 16, 64), (17, 80, 192), (130, 272, 1024), (100, 2048, 768), (300, 4096, 512),
     (256, 2048, 6144), (256, 6144, 2048), (33, 48, 4096), (40, 96, 320), (70, 160, 704),
+    (520, 8192, 512),
 ]
 
 

@@ -38,7 +38,8 @@ def _routed(seed, rows, top_k, hidden, excluded=0.1):
     (256, 6144, 2048, 8, 2),   # the prefill sub-chunk's shared expert
     (200, 1024, 512, 8, 1),    # ragged rows; K too short to split
     (130, 512, 4096, 6, 4),    # two row tiles, four splits, the generic combine kernel
-    (384, 2048, 4096, 8, 2)])  # three row tiles
+    (384, 2048, 4096, 8, 2),   # three row tiles
+    (520, 8192, 512, 8, 1)])   # 320 blocks: the register-staged kernel's row-major stores
 def test_combine_partials_bits(hip, rows, hidden, inter, top_k, ways):
     rng = np.random.default_rng(rows + hidden)
     act = bf16_dev(wl.bf16_normal(rng, (rows, inter)))
