@@ -81,8 +81,8 @@ _SIGNATURES = {
         [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _f32, _vp],
         ctypes.c_int),
     "swiglu_clamp": ([_vp, _vp, _i64, _vp, _i64, _i32, _i32, _f32, _vp], ctypes.c_int),
-    "moe_combine_partials": ([_vp, _i64, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32,
-                              _vp], ctypes.c_int),
+    "moe_combine_partials": ([_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i64, _i32, _i32,
+                              _i32, _vp], ctypes.c_int),
     "moe_dense_splitk_ways": ([_i32, _i32], ctypes.c_int32),
     "moe_dense_gemm_bf16_partials": ([_vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32, _i64, _vp],
                                      ctypes.c_int),
@@ -442,8 +442,8 @@ def moe_combine(expert_out, token_to_perm, topk_weights, out, shared=None, strea
                              f"{rows} rows x {hidden}")
         _check("moe_combine_partials", load().moe_combine_partials(
             _p(expert_out), ld_e, expert_out.shape[0], _p(token_to_perm), _p(topk_weights),
-            _p(shared.partials), shared.ways, _p(out), ld_out, rows, hidden, top_k,
-            _stream(stream)))
+            _p(shared.partials), shared.ways, shared.partials.numel() * 4, _p(out), ld_out,
+            rows, hidden, top_k, _stream(stream)))
         return
     ld_s = 0
     if shared is not None:

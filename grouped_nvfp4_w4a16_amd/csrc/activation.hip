@@ -254,13 +254,20 @@ extern "C" int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t exp
 extern "C" int moe_combine_partials(const uint16_t *expert_out, int64_t ld_e,
                                     int32_t expert_rows, const int32_t *token_to_perm,
                                     const float *topk_weights, const float *shared_partials,
-                                    int32_t ways, uint16_t *out, int64_t ld_out, int32_t rows,
-                                    int32_t hidden, int32_t top_k, void *stream) {
+                                    int32_t ways, int64_t partials_bytes, uint16_t *out,
+                                    int64_t ld_out, int32_t rows, int32_t hidden, int32_t top_k,
+                                    void *stream) {
   moe::clear_error();
   MOE_REQUIRE(ways >= 1 && ways <= 64, "moe_combine_partials: ways must be in [1, 64] (got %d)",
               ways);
-  if (rows > 0 && hidden > 0)
+  if (rows > 0 && hidden > 0) {
     MOE_REQUIRE(shared_partials != nullptr, "moe_combine_partials: shared_partials is NULL");
+    const int64_t need = static_cast<int64_t>(ways) * rows * hidden * 4;
+    MOE_REQUIRE_CODE(partials_bytes >= need, MOE_ECAPACITY,
+                     "moe_combine_partials: %lld bytes of partials, %d x %d x %d need %lld",
+                     static_cast<long long>(partials_bytes), ways, rows, hidden,
+                     static_cast<long long>(need));
+  }
   return combine_launch("moe_combine_partials", expert_out, ld_e, expert_rows, token_to_perm,
                         topk_weights, nullptr, 0, shared_partials, ways, out, ld_out, rows,
                         hidden, top_k, stream);

@@ -289,15 +289,17 @@ int moe_combine(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
  *
  *   shared_partials  float [ways, rows, hidden], contiguous (hidden fastest)
  *   ways             the split count the partials were written with, in [1, 64]
+ *   partials_bytes   the size of shared_partials in bytes
  *   the other arguments as moe_combine (no shared, ld_s).
- * Requirements (else MOE_EINVAL): those of moe_combine; 1 <= ways <= 64; shared_partials
- * non-NULL and 16-byte aligned when rows * hidden > 0.
+ * Requirements (else MOE_EINVAL / MOE_ECAPACITY): those of moe_combine; 1 <= ways <= 64;
+ * shared_partials non-NULL and 16-byte aligned when rows * hidden > 0; partials_bytes >=
+ * ways * rows * hidden * 4 (MOE_ECAPACITY, nothing enqueued).
  */
 int moe_combine_partials(const uint16_t *expert_out, int64_t ld_e, int32_t expert_rows,
                          const int32_t *token_to_perm, const float *topk_weights,
-                         const float *shared_partials, int32_t ways, uint16_t *out,
-                         int64_t ld_out, int32_t rows, int32_t hidden, int32_t top_k,
-                         void *stream);
+                         const float *shared_partials, int32_t ways, int64_t partials_bytes,
+                         uint16_t *out, int64_t ld_out, int32_t rows, int32_t hidden,
+                         int32_t top_k, void *stream);
 
 /*
  * moe_zero_rows - c[r, j] = 0 for r < rows, j < cols: forward_moe's zero-first step on

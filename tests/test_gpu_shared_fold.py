@@ -111,13 +111,18 @@ def test_partials_bad_arguments(hip):
     out = torch.empty(4, 1024, dtype=torch.bfloat16, device="cuda")
     lib = hip.load()
     p = torch.zeros(4 * 1024, dtype=torch.float32, device="cuda")
+    nbytes = p.numel() * 4
     for bad_ways in (0, 65):
         rc = lib.moe_combine_partials(eo.data_ptr(), 1024, 32, ttp.data_ptr(), wts.data_ptr(),
-                                      p.data_ptr(), bad_ways, out.data_ptr(), 1024, 4, 1024, 8,
-                                      None)
+                                      p.data_ptr(), bad_ways, nbytes, out.data_ptr(), 1024, 4,
+                                      1024, 8, None)
         assert rc == 1  # MOE_EINVAL
     rc = lib.moe_combine_partials(eo.data_ptr(), 1024, 32, ttp.data_ptr(), wts.data_ptr(),
-                                  None, 1, out.data_ptr(), 1024, 4, 1024, 8, None)
+                                  None, 1, nbytes, out.data_ptr(), 1024, 4, 1024, 8, None)
     assert rc == 1
+    # two splits of 4 x 1024 do not fit one's bytes: MOE_ECAPACITY, nothing read
+    rc = lib.moe_combine_partials(eo.data_ptr(), 1024, 32, ttp.data_ptr(), wts.data_ptr(),
+                                  p.data_ptr(), 2, nbytes, out.data_ptr(), 1024, 4, 1024, 8, None)
+    assert rc == 2
     with pytest.raises(ValueError):  # partials of another row count
         hip.moe_combine(eo, ttp, wts, out, hip.SharedPartials(p.view(1, 2, 2048)))
