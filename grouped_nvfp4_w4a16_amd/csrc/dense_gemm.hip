@@ -244,12 +244,14 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_kernel(
 // S ways restores the block count (one to two blocks per CU at the shared expert's
 // shapes).
 //   1. Partial GEMM. 4 waves as 2 x 2, each owning 64 A rows x 64 B rows (16 MFMA tiles,
-//      64 accumulator VGPRs). A and B tiles of 64 k are staged in LDS, double buffered,
-//      one barrier per step; the global loads run three steps ahead in registers. LDS rows
-//      are 128 bytes with the 16-byte pieces XOR-swizzled by the row (piece c of row r
-//      at c ^ (r & 7)), so the 16 rows x 4 pieces an MFMA operand read touches fall in
-//      distinct banks. Each block writes its FP32 partial tile to the workspace in
-//      fragment order (1 KB contiguous per wave and MFMA tile).
+//      64 accumulator VGPRs). A and B tiles of 64 k are staged in LDS, one barrier per
+//      step: when the grid fits one block per CU, loaded straight into LDS, three stages
+//      in flight; else double buffered through registers, the global loads three steps
+//      ahead (two blocks per CU). LDS rows are 128 bytes with the 16-byte pieces
+//      XOR-swizzled by the row (piece c of row r at c ^ (r & 7)), so the 16 rows x 4
+//      pieces an MFMA operand read touches fall in distinct banks. Each block writes its
+//      FP32 partial tile to the workspace in fragment order (1 KB contiguous per wave and
+//      MFMA tile), or row-major for a reduction inside the combine.
 //   2. Reduction. One thread per output fragment (4 columns of one row) sums the S
 //      partials in split order (deterministic), rounds to BF16 and, in the gate/up form,
 //      applies the SwiGLU to the BF16 gate and up sums; the whole chip reads the
