@@ -555,12 +555,20 @@ __global__ __launch_bounds__(kThreads, kSlotsPerCu) void gemv_union_kernel(
 
     // This item's steps in pairs: slot A holds step i, slot B takes step i + 1; after an
     // odd share, the pair's second step is empty. The step after this item's last is the
-    // next item's first, into slot A (a select, so the loads stay unconditional).
-    for (int i = 0; i < n_mine; i += 2) {
+    // next item's first, into slot A. The last pair is peeled out of the loop, so the
+    // pairs before it load from this item with no per-pair selects between the two items
+    // (down GEMV at 8 rows 60.5-62.3 -> 59.6-60.0 us, gate_up level, same bits).
+    int i = 0;
+    for (; i + 2 < n_mine; i += 2) {
+      load_step(sB, cur, i + 1, true);
+      if (cur.on[0]) run_step(sA, tab, cur.on[1]);
+      load_step(sA, cur, i + 2, true);
+      if (cur.on[0]) run_step(sB, tab, cur.on[1]);
+    }
+    if (i < n_mine) {  // uniform
       load_step(sB, cur, i + 1, i + 1 < n_mine);
       if (cur.on[0]) run_step(sA, tab, cur.on[1]);
-      const bool last = i + 2 >= n_mine;
-      load_step(sA, last ? nxt : cur, last ? 0 : i + 2, last ? has_next : true);
+      load_step(sA, nxt, 0, has_next);
       if (i + 1 < n_mine && cur.on[0]) run_step(sB, tab, cur.on[1]);
     }
 
