@@ -225,6 +225,7 @@ def test_dense_split_k_workspace_shared_by_two_shapes(hip):
 
 @pytest.mark.parametrize("m,inter,k,w_scale", [
     (33, 48, 192, 6.0), (19, 16, 1024, 6.0), (100, 768, 2048, 8.0), (256, 2048, 6144, 1.0),
+    (520, 4096, 512, 1.0),  # 320 blocks: the register-staged kernel
 ])
 def test_gate_up_swiglu_split_k_bits_and_oracle(hip, m, inter, k, w_scale):
     a_bits, g_bits = _operands(m + inter + k + 1, m, inter, k, w_scale)
