@@ -383,6 +383,7 @@ def time_decode_leg(hip, torch, steps, probe):
     dws = hip.DecodeWorkspace(rows, top_k, hidden, mi)
     out = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
     u_slot = dws.u_slot[:s * rows]
+    active = dict(active_experts=ws.active_experts, counters=ws.counters)
     n_gu, k_gu = wl.gate_up_shape(w)
     n_dn, k_dn = wl.down_shape(w)
     live = sorted({int(e) for e in ids_host.reshape(-1) if not w.is_null(int(e))})
@@ -408,9 +409,10 @@ def time_decode_leg(hip, torch, steps, probe):
                                                      ws.token_to_perm, ws.active_experts,
                                                      ws.counters, zero=ws.expert_out[:s])),
             ("grouped_gemm_gate_up_swiglu", lambda: hip.moe_w4a16_grouped_gemm_swiglu(
-                x, gt, ws.expert_offsets, ws.act, w.limit, ws.sorted_token_ids, max_rows=s)),
+                x, gt, ws.expert_offsets, ws.act, w.limit, ws.sorted_token_ids, max_rows=s,
+                **active)),
             ("grouped_gemm_down", lambda: hip.moe_w4a16_grouped_gemm(
-                ws.act, dt, ws.expert_offsets, ws.expert_out, None, max_rows=s)),
+                ws.act, dt, ws.expert_offsets, ws.expert_out, None, max_rows=s, **active)),
             ("moe_combine", lambda: hip.moe_combine(ws.expert_out[:s], ws.token_to_perm, wts,
                                                     out))],
     }
@@ -534,24 +536,26 @@ def measure_workload(hip, torch, w, args, probe, steps: int, warmup: int):
     c_single = (torch.empty((max(s, 1), n_gu), dtype=torch.bfloat16, device="cuda")
                 if single else None)
 
+    active = dict(active_experts=ws.active_experts, counters=ws.counters)
+
     def st_single(x, ids, wts):
         hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, c_single, ws.sorted_token_ids,
-                                   max_rows=s)
+                                   max_rows=s, **active)
 
     def st_gate_up(x, ids, wts):
         hip.moe_w4a16_grouped_gemm(x, gt, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
-                                   max_rows=s)
+                                   max_rows=s, **active)
 
     def st_swiglu(x, ids, wts):
         hip.swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], w.limit)
 
     def st_gate_up_swiglu(x, ids, wts):
         hip.moe_w4a16_grouped_gemm_swiglu(x, gt, ws.expert_offsets, ws.act, w.limit,
-                                          ws.sorted_token_ids, max_rows=s)
+                                          ws.sorted_token_ids, max_rows=s, **active)
 
     def st_down(x, ids, wts):
         hip.moe_w4a16_grouped_gemm(ws.act, dt, ws.expert_offsets, ws.expert_out, None,
-                                   max_rows=s)
+                                   max_rows=s, **active)
 
     def st_shared(x, ids, wts):  # split-K: the down reduction runs in the combine
         shared_out[0] = se.for_combine(x, w.limit)

@@ -75,11 +75,11 @@ _SIGNATURES = {
     "moe_align_zero": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                         _vp], ctypes.c_int),
     "moe_w4a16_grouped_gemm": (
-        [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp],
-        ctypes.c_int),
+        [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+         _vp], ctypes.c_int),
     "moe_w4a16_grouped_gemm_swiglu": (
-        [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _f32, _vp],
-        ctypes.c_int),
+        [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+         _f32, _vp], ctypes.c_int),
     "swiglu_clamp": ([_vp, _vp, _i64, _vp, _i64, _i32, _i32, _f32, _vp], ctypes.c_int),
     "moe_combine_partials": ([_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i64, _i32, _i32,
                               _i32, _vp], ctypes.c_int),
@@ -232,15 +232,33 @@ def moe_align(topk_ids, num_experts: int, sorted_token_ids, sorted_expert_ids, e
         _stream(stream)))
 
 
+def _active_list(active_experts, counters, num_experts):
+    """moe_align's active-expert list and counters (both or neither)."""
+    import torch
+
+    if (active_experts is None) != (counters is None):
+        raise ValueError("active_experts and counters go together")
+    _want(active_experts, torch.int32, "active_experts")
+    _want(counters, torch.int32, "counters")
+    if active_experts is not None and (active_experts.numel() < num_experts or
+                                       counters.numel() < 2):
+        raise ValueError("active_experts needs num_experts elements, counters 2")
+    return _p(active_experts), _p(counters)
+
+
 def moe_w4a16_grouped_gemm(a, table: "ExpertTable", expert_offsets, c, a_gather=None,
-                           max_rows: int | None = None, stream=None) -> None:
-    """``c[s] = a[g(s)] @ W_e^T`` for every sorted row s of every present expert e."""
+                           max_rows: int | None = None, stream=None, active_experts=None,
+                           counters=None) -> None:
+    """``c[s] = a[g(s)] @ W_e^T`` for every sorted row s of every present expert e. With
+    moe_align's ``active_experts`` and ``counters``, a launch with fewer rows than experts
+    visits only the experts that have rows (same results)."""
     import torch
 
     a, lda = _bf16_matrix(a, "a")
     c, ldc = _bf16_matrix(c, "c")
     _want(expert_offsets, torch.int32, "expert_offsets")
     _want(a_gather, torch.int32, "a_gather")
+    act_p, cnt_p = _active_list(active_experts, counters, table.num_experts)
     if expert_offsets.numel() < table.num_experts + 1:
         raise ValueError("expert_offsets: needs num_experts + 1 elements")
     rows = c.shape[0] if max_rows is None else max_rows
@@ -252,15 +270,16 @@ def moe_w4a16_grouped_gemm(a, table: "ExpertTable", expert_offsets, c, a_gather=
         raise ValueError("a or c too narrow for the table's k, n")
     _check("moe_w4a16_grouped_gemm", load().moe_w4a16_grouped_gemm(
         _p(a), lda, a.shape[0], _p(a_gather), _p(table.packed_ptrs), _p(table.scale_ptrs),
-        _p(table.scale2), _p(expert_offsets), table.num_experts, _p(c), ldc, rows, table.n,
-        table.k, _stream(stream)))
+        _p(table.scale2), _p(expert_offsets), table.num_experts, act_p, cnt_p, _p(c), ldc,
+        rows, table.n, table.k, _stream(stream)))
 
 
 def moe_w4a16_grouped_gemm_swiglu(a, table: "ExpertTable", expert_offsets, act, limit: float,
                                   a_gather=None, max_rows: int | None = None,
-                                  stream=None) -> None:
+                                  stream=None, active_experts=None, counters=None) -> None:
     """``act[s] = swiglu_clamp(gate, up)`` of ``a[g(s)] @ W_e^T`` for a fused gate_up table
-    (``table.n = 2 mi``), without storing the gate_up values."""
+    (``table.n = 2 mi``), without storing the gate_up values. ``active_experts`` and
+    ``counters`` as for moe_w4a16_grouped_gemm."""
     import torch
 
     if table.n % 2:
@@ -279,10 +298,11 @@ def moe_w4a16_grouped_gemm_swiglu(a, table: "ExpertTable", expert_offsets, act, 
         raise ValueError("without a_gather, a needs max_rows rows")
     if a.shape[1] < table.k or act.shape[1] < mi:
         raise ValueError("a or act too narrow for the table's k, n / 2")
+    act_p, cnt_p = _active_list(active_experts, counters, table.num_experts)
     _check("moe_w4a16_grouped_gemm_swiglu", load().moe_w4a16_grouped_gemm_swiglu(
         _p(a), lda, a.shape[0], _p(a_gather), _p(table.packed_ptrs), _p(table.scale_ptrs),
-        _p(table.scale2), _p(expert_offsets), table.num_experts, _p(act), ld_act, rows, mi,
-        table.k, float(limit), _stream(stream)))
+        _p(table.scale2), _p(expert_offsets), table.num_experts, act_p, cnt_p, _p(act),
+        ld_act, rows, mi, table.k, float(limit), _stream(stream)))
 
 
 
@@ -705,6 +725,8 @@ class ExpertTable:
             sp.append(s.data_ptr())
             if device is None:
                 device = p.device
+        if device is None:  # every entry null
+            device = "cuda"
         self._keep = (list(packed), list(scales))
         self.packed_ptrs = torch.tensor(pp, dtype=torch.int64, device=device)
         self.scale_ptrs = torch.tensor(sp, dtype=torch.int64, device=device)
@@ -768,15 +790,16 @@ def moe_layer(x, topk_ids, topk_weights, gate_up: ExpertTable, down: ExpertTable
               ws.expert_offsets, ws.token_to_perm, ws.active_experts, ws.counters, stream,
               zero=None if all(down.present) else ws.expert_out[:s])
     mi = moe_intermediate
+    active = dict(active_experts=ws.active_experts, counters=ws.counters)
     if fused:
         moe_w4a16_grouped_gemm_swiglu(x, gate_up, ws.expert_offsets, ws.act, limit,
-                                      ws.sorted_token_ids, max_rows=s, stream=stream)
+                                      ws.sorted_token_ids, max_rows=s, stream=stream, **active)
     else:
         moe_w4a16_grouped_gemm(x, gate_up, ws.expert_offsets, ws.gate_up, ws.sorted_token_ids,
-                               max_rows=s, stream=stream)
+                               max_rows=s, stream=stream, **active)
         swiglu_clamp(ws.gate_up[:s, :mi], ws.gate_up[:s, mi:2 * mi], ws.act[:s], limit, stream)
     moe_w4a16_grouped_gemm(ws.act, down, ws.expert_offsets, ws.expert_out, None, max_rows=s,
-                           stream=stream)
+                           stream=stream, **active)
     if isinstance(shared, SharedExpert):
         shared = shared.for_combine(x, limit, stream)
     moe_combine(ws.expert_out[:s], ws.token_to_perm, topk_weights, out, shared, stream)

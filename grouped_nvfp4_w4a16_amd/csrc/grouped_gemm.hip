@@ -188,8 +188,9 @@ __global__ __launch_bounds__(kThreads, kMT == 1 ? 3 : 2) void grouped_gemm_kerne
     const int32_t *__restrict__ gather, const uint64_t *__restrict__ packed_ptrs,
     const uint64_t *__restrict__ scale_ptrs, const float *__restrict__ scale2s,
     const int32_t *__restrict__ offsets, int32_t num_experts, int32_t chunk_rows,
-    uint16_t *__restrict__ c, int64_t ldc, int32_t max_rows, int32_t N, int32_t K,
-    float limit) {
+    const int32_t *__restrict__ active, const int32_t *__restrict__ n_active_p,
+    int32_t expert_rows, uint16_t *__restrict__ c, int64_t ldc, int32_t max_rows, int32_t N,
+    int32_t K, float limit) {
   constexpr int kPassM = kBlockM * kMT;                      // sorted rows per pass
   constexpr int kXBufBytes = kPassM * kLdsRowBytes;
   constexpr int kXP = kPassM * kPiecesPerRow / kThreads;       // pieces per thread per step
@@ -218,20 +219,25 @@ __global__ __launch_bounds__(kThreads, kMT == 1 ? 3 : 2) void grouped_gemm_kerne
   // The room for overflow chunks is a worst-case bound; the rows past the actual chunks
   // exit after one scan of the offsets, and dispatching only a few of them first keeps
   // that cost off the start of a launch whose experts are all light.
+  // With `active` (the sort's list of experts that have rows, and its count), the
+  // expert_rows (< num_experts) expert rows of the grid take the listed experts in turn:
+  // a launch with fewer rows than experts then dispatches no block for an expert without
+  // rows (at 8 decode rows and 256 experts, 2,048 blocks instead of 8,192).
   const int tile = blockIdx.x;
-  int e = blockIdx.y;
-  {
-    const int front = min(static_cast<int>(gridDim.y) - num_experts, kFrontChunks);
-    e = e < front ? num_experts + e : (e < front + num_experts ? e - front : e);
-  }
-  int chunk = 0;
-  const bool over = e >= num_experts;
+  const int y = blockIdx.y;
+  const int front = min(static_cast<int>(gridDim.y) - expert_rows, kFrontChunks);
+  int e = y - front, chunk = 0;
+  const bool over = y < front || y >= front + expert_rows;
   if (over) {
-    const int2 found = find_overflow_chunk(offsets, num_experts, chunk_rows, max_rows,
-                                           e - num_experts);
+    const int oc = y < front ? y : y - expert_rows;
+    const int2 found = find_overflow_chunk(offsets, num_experts, chunk_rows, max_rows, oc);
     if (found.x < 0) return;  // fewer overflow chunks than grid rows
     e = found.x;
     chunk = found.y;
+  } else if (active != nullptr) {  // uniform
+    if (e >= *n_active_p) return;  // fewer experts with rows than expert rows in the grid
+    e = active[e];
+    if (e < 0 || e >= num_experts) return;
   }
   // All of the expert's metadata in one memory round trip: the empty asm needs every
   // value before the early exits, so the five loads are issued together instead of one
@@ -554,16 +560,26 @@ int check_gemm_args(const char *name, const uint16_t *a, int64_t lda, int32_t a_
 // so all experts together (at most max_rows rows) have at most 2 max_rows / (C + 1), and
 // none when max_rows <= C. Where that would pass the grid's row limit, blocks take all of
 // their expert's rows (no overflow chunks).
-int grid_rows(int32_t num_experts, int32_t max_rows, int *chunk_rows) {
+int grid_rows(int32_t expert_rows, int32_t max_rows, int *chunk_rows) {
   const int64_t chunks =
       max_rows > kChunkRows ? 2 * static_cast<int64_t>(max_rows) / (kChunkRows + 1) : 0;
-  const int64_t rows = num_experts + chunks;
+  const int64_t rows = expert_rows + chunks;
   if (rows <= 65535) {
     *chunk_rows = kChunkRows;
     return static_cast<int>(rows);
   }
   *chunk_rows = INT32_MAX;
-  return num_experts;
+  return expert_rows;
+}
+
+// Grid rows for the experts: one per expert, or, given the sort's active-expert list and
+// count, one per slot when there are fewer slots than experts (at most that many experts
+// have rows). The list costs each block one more dependent load, so it is used only
+// where it removes blocks.
+int expert_grid_rows(int32_t num_experts, int32_t max_rows, const int32_t *active,
+                     const int32_t *counters) {
+  return active != nullptr && counters != nullptr && max_rows < num_experts ? max_rows
+                                                                            : num_experts;
 }
 
 // Two 16-row tiles per pass when the experts average at least 24 rows: passes over 32
@@ -580,6 +596,7 @@ extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_
                                       const int32_t *a_gather, const uint64_t *packed_ptrs,
                                       const uint64_t *scale_ptrs, const float *scale2,
                                       const int32_t *expert_offsets, int32_t num_experts,
+                                      const int32_t *active_experts, const int32_t *counters,
                                       uint16_t *c, int64_t ldc, int32_t max_rows, int32_t n,
                                       int32_t k, void *stream) {
   moe::clear_error();
@@ -589,13 +606,16 @@ extern "C" int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_
                                  expert_offsets, num_experts, c, ldc, max_rows, n, n, k);
   if (rc != MOE_OK || max_rows == 0) return rc;
   int chunk_rows = 0;
-  const dim3 grid((n + kBlockN - 1) / kBlockN, grid_rows(num_experts, max_rows, &chunk_rows));
+  const int x_rows = expert_grid_rows(num_experts, max_rows, active_experts, counters);
+  const bool listed = x_rows < num_experts;
+  const dim3 grid((n + kBlockN - 1) / kBlockN, grid_rows(x_rows, max_rows, &chunk_rows));
   return moe::launch("moe_w4a16_grouped_gemm",
                      two_row_tiles(num_experts, max_rows) ? grouped_gemm_kernel<false, 2>
                                                           : grouped_gemm_kernel<false, 1>,
                      grid, dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
-                     scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows, c, ldc,
-                     max_rows, n, k, 0.0f);
+                     scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows,
+                     listed ? active_experts : nullptr, listed ? counters : nullptr, x_rows, c,
+                     ldc, max_rows, n, k, 0.0f);
 }
 
 extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows,
@@ -603,8 +623,10 @@ extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int
                                              const uint64_t *packed_ptrs,
                                              const uint64_t *scale_ptrs, const float *scale2,
                                              const int32_t *expert_offsets, int32_t num_experts,
-                                             uint16_t *act, int64_t ld_act, int32_t max_rows,
-                                             int32_t mi, int32_t k, float limit, void *stream) {
+                                             const int32_t *active_experts,
+                                             const int32_t *counters, uint16_t *act,
+                                             int64_t ld_act, int32_t max_rows, int32_t mi,
+                                             int32_t k, float limit, void *stream) {
   moe::clear_error();
   MOE_REQUIRE(mi > 0 && mi % 16 == 0,
               "grouped_gemm_swiglu: mi must be a positive multiple of 16 (got %d)", mi);
@@ -615,13 +637,16 @@ extern "C" int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int
                                  2 * mi, mi, k);
   if (rc != MOE_OK || max_rows == 0) return rc;
   int chunk_rows = 0;
-  const dim3 grid((mi + kHalfN - 1) / kHalfN, grid_rows(num_experts, max_rows, &chunk_rows));
+  const int x_rows = expert_grid_rows(num_experts, max_rows, active_experts, counters);
+  const bool listed = x_rows < num_experts;
+  const dim3 grid((mi + kHalfN - 1) / kHalfN, grid_rows(x_rows, max_rows, &chunk_rows));
   return moe::launch("moe_w4a16_grouped_gemm_swiglu",
                      two_row_tiles(num_experts, max_rows) ? grouped_gemm_kernel<true, 2>
                                                           : grouped_gemm_kernel<true, 1>,
                      grid, dim3(kThreads), 0, stream, a, lda, a_rows, a_gather, packed_ptrs,
-                     scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows, act, ld_act,
-                     max_rows, 2 * mi, k, limit);
+                     scale_ptrs, scale2, expert_offsets, num_experts, chunk_rows,
+                     listed ? active_experts : nullptr, listed ? counters : nullptr, x_rows,
+                     act, ld_act, max_rows, 2 * mi, k, limit);
 }
 
 extern "C" int moe_w4a16_dequant_bf16(const uint8_t *packed, const uint8_t *scales,

@@ -199,6 +199,14 @@ int moe_align_zero(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t
  *   expert_offsets  int32  [num_experts + 1] as written by moe_align: non-decreasing (a
  *                   prefix sum). Other values are not checked (device data); each row the
  *                   call writes still lies in [0, max_rows), but rows may then be missed.
+ *   active_experts, counters
+ *                   NULL, or moe_align's active_experts [num_experts] and counters [2]
+ *                   for the same ids (the experts with rows, in order, and their count in
+ *                   counters[0]). When both are given and max_rows < num_experts, the
+ *                   launch visits only the listed experts (no block for an expert without
+ *                   rows); the results are the same. Entries outside [0, num_experts) are
+ *                   skipped; a list that leaves out an expert with rows leaves its rows
+ *                   unwritten (device data: not checked).
  *   c               bf16   [max_rows, ldc] output rows in expert-sorted order
  *
  * Requirements (else MOE_EINVAL): n > 0 and n % 16 == 0; k > 0 and k % 256 == 0;
@@ -212,7 +220,8 @@ int moe_align_zero(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t
 int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
                            const int32_t *a_gather, const uint64_t *packed_ptrs,
                            const uint64_t *scale_ptrs, const float *scale2,
-                           const int32_t *expert_offsets, int32_t num_experts, uint16_t *c,
+                           const int32_t *expert_offsets, int32_t num_experts,
+                           const int32_t *active_experts, const int32_t *counters, uint16_t *c,
                            int64_t ldc, int32_t max_rows, int32_t n, int32_t k, void *stream);
 
 /*
@@ -226,8 +235,8 @@ int moe_w4a16_grouped_gemm(const uint16_t *a, int64_t lda, int32_t a_rows,
  *
  * The result is bit-identical to moe_w4a16_grouped_gemm into a [max_rows, 2 mi] buffer
  * followed by swiglu_clamp on its two halves; the gate_up values are never stored. Rows,
- * gathers, null entries and expert_offsets behave as in moe_w4a16_grouped_gemm (rows of a
- * null expert are not written).
+ * gathers, null entries, expert_offsets and the active-expert list behave as in
+ * moe_w4a16_grouped_gemm (rows of a null expert are not written).
  *
  *   act      bf16 [max_rows, ld_act]  output
  *   tables   packed_ptrs[e] -> uint8 [2 mi, k/2], scale_ptrs[e] -> uint8 [2 mi, k/16]
@@ -241,6 +250,7 @@ int moe_w4a16_grouped_gemm_swiglu(const uint16_t *a, int64_t lda, int32_t a_rows
                                   const int32_t *a_gather, const uint64_t *packed_ptrs,
                                   const uint64_t *scale_ptrs, const float *scale2,
                                   const int32_t *expert_offsets, int32_t num_experts,
+                                  const int32_t *active_experts, const int32_t *counters,
                                   uint16_t *act, int64_t ld_act, int32_t max_rows, int32_t mi,
                                   int32_t k, float limit, void *stream);
 

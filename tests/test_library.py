@@ -84,8 +84,8 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     def gemm(**kw):
         a = {**args, **kw}
         return lib.moe_w4a16_grouped_gemm(a["a"], a["lda"], a["a_rows"], a["g"], a["pp"], a["sp"],
-                                          a["s2"], a["off"], a["e"], a["c"], a["ldc"], a["rows"],
-                                          a["nn"], a["k"], n)
+                                          a["s2"], a["off"], a["e"], n, n, a["c"], a["ldc"],
+                                          a["rows"], a["nn"], a["k"], n)
     assert gemm(k=500) == 1
     assert gemm(nn=40) == 1
     assert gemm(a=_bad(0x1008)) == 1
