@@ -93,3 +93,26 @@ def test_decode_layer_graph_replays(hip):
 
     sets_dev = [(dev(i), dev(t), bf16_dev(xb)) for i, t, xb in sets]
     _replays_match_eager(run, (ids, wts, x), sets_dev, out)
+
+
+def test_layer_with_active_expert_list_graph_replays(hip):
+    """moe_layer at 8 rows and 256 experts: the grouped GEMMs' grids hold one expert row
+    per slot and take the experts from the sort's list on the device, so replays with
+    other routing (another set of experts with rows) must follow it."""
+    w = wl.custom("graph_listed", 94, rows=8, num_experts=256, top_k=8, hidden=1024,
+                  moe_intermediate=512, null_from=160)
+    sets = [_inputs(w, s) for s in (4, 5, 4)]
+    live = {int(e) for s in sets for e in s[0].reshape(-1)}
+    assert not live <= set(sets[0][0].reshape(-1).tolist())  # the sets route differently
+    _, _, gt, dt = workload_tables(hip, w, only=live)
+    ids = dev(sets[0][0])
+    wts = dev(sets[0][1])
+    x = bf16_dev(sets[0][2])
+    ws = hip.Workspace(w.rows, w.top_k, w.num_experts, w.hidden, w.moe_intermediate)
+    out = torch.empty((w.rows, w.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        hip.moe_layer(x, ids, wts, gt, dt, w.moe_intermediate, w.limit, ws, out)
+
+    sets_dev = [(dev(i), dev(t), bf16_dev(xb)) for i, t, xb in sets]
+    _replays_match_eager(run, (ids, wts, x), sets_dev, out)
