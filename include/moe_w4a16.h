@@ -204,9 +204,11 @@ int moe_align_zero(const int32_t *topk_ids, int32_t rows, int32_t top_k, int32_t
  *                   for the same ids (the experts with rows, in order, and their count in
  *                   counters[0]). When both are given and max_rows < num_experts, the
  *                   launch visits only the listed experts (no block for an expert without
- *                   rows); the results are the same. Entries outside [0, num_experts) are
- *                   skipped; a list that leaves out an expert with rows leaves its rows
- *                   unwritten (device data: not checked).
+ *                   rows); the results are the same. Grid row i takes entry i, for i <
+ *                   min(counters[0], max_rows): moe_align's ascending order guarantees
+ *                   that an entry past max_rows has no row below max_rows. Entries outside
+ *                   [0, num_experts) are skipped; a list that leaves out an expert with
+ *                   rows leaves its rows unwritten (device data: not checked).
  *   c               bf16   [max_rows, ldc] output rows in expert-sorted order
  *
  * Requirements (else MOE_EINVAL): n > 0 and n % 16 == 0; k > 0 and k % 256 == 0;
