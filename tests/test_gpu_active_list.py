@@ -32,22 +32,24 @@ def _align(hip, ids_np):
     return b
 
 
-def _gemms(hip, w, b, active=None, counters=None):
-    """(gate_up, act, down output) bits of the three grouped GEMM forms over sorted rows."""
+def _gemms(hip, w, b, active=None, counters=None, max_rows=None):
+    """(gate_up, act, down output) bits of the three grouped GEMM forms over sorted rows
+    (the first ``max_rows`` of them; all by default)."""
     _, _, gt, dt = _tables(hip, w)
     s = w.rows * w.top_k
+    cut = s if max_rows is None else max_rows
     mi, hidden = w.moe_intermediate, w.hidden
     kw = dict(active_experts=active, counters=counters)
     x = bf16_dev(wl.activations(w))
     bf16 = dict(dtype=torch.bfloat16, device="cuda")
     gu = torch.full((s, 2 * mi), -3.0, **bf16)
     hip.moe_w4a16_grouped_gemm(x, gt, b["expert_offsets"], gu, b["sorted_token_ids"],
-                               max_rows=s, **kw)
+                               max_rows=cut, **kw)
     act = torch.full((s, mi), -3.0, **bf16)
     hip.moe_w4a16_grouped_gemm_swiglu(x, gt, b["expert_offsets"], act, w.limit,
-                                      b["sorted_token_ids"], max_rows=s, **kw)
+                                      b["sorted_token_ids"], max_rows=cut, **kw)
     out = torch.full((s, hidden), -3.0, **bf16)
-    hip.moe_w4a16_grouped_gemm(act, dt, b["expert_offsets"], out, None, max_rows=s, **kw)
+    hip.moe_w4a16_grouped_gemm(act, dt, b["expert_offsets"], out, None, max_rows=cut, **kw)
     torch.cuda.synchronize()
     return _bits(gu), _bits(act), _bits(out)
 
@@ -122,6 +124,20 @@ def test_shuffled_list_with_out_of_range_entries(hip):
     got = _gemms(hip, w, b, active, counters)
     for r, g in zip(ref, got):
         assert np.array_equal(g, r)
+
+
+def test_row_cut_off_below_the_list_length(hip):
+    """max_rows = 35 of 64 sorted rows with ~56 listed experts: the grid's 35 expert rows
+    take the first 35 entries; the experts past them start at row 35 or later."""
+    w, ids_np = _workload("act_softmax_8", 78, 8, 8)
+    b = _align(hip, ids_np)
+    assert int(b["counters"][0]) > 35
+    ref = _gemms(hip, w, b, max_rows=35)
+    got = _gemms(hip, w, b, b["active_experts"], b["counters"], max_rows=35)
+    poison = _bits(torch.tensor(-3.0, dtype=torch.bfloat16))
+    for r, g in zip(ref, got):
+        assert np.array_equal(g, r)
+        assert (g[35:] == poison).all()
 
 
 def test_no_valid_ids_writes_nothing(hip):
