@@ -371,8 +371,8 @@ def time_decode_leg(hip, torch, steps, probe):
     union GEMV gate_up with the SwiGLU -> union GEMV down -> combine) and the sorted path
     (moe_align_zero -> grouped GEMMs -> combine) on the same rows. Its weights (0.68 GB)
     would partly stay in the 256 MB last-level cache from one step to the next, so every
-    timed step follows a cache-evicting stream outside its events. GB/s is unique weight
-    bytes (live experts, both projections) per step."""
+    timed step follows a cache-evicting stream outside its events; times are medians over
+    the steps. GB/s is unique weight bytes (live experts, both projections) per step."""
     import workloads as wl
 
     w = wl.WORKLOADS["small_m"]
@@ -432,10 +432,12 @@ def time_decode_leg(hip, torch, steps, probe):
                 fn()
             ev[i][len(stages)].record(stream)
         torch.cuda.synchronize()
-        step_us = float(np.mean([ev[i][0].elapsed_time(ev[i][len(stages)]) * 1000.0
-                                 for i in range(steps)]))
-        kus = {n: round(float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0
-                                       for i in range(steps)])), 2)
+        # medians: a host stall while the queue is empty (between a stage's start event
+        # and its launch) lands in one step's times and would move a mean
+        step_us = float(np.median([ev[i][0].elapsed_time(ev[i][len(stages)]) * 1000.0
+                                   for i in range(steps)]))
+        kus = {n: round(float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0
+                                         for i in range(steps)])), 2)
                for j, (n, _) in enumerate(stages)}
         res[name] = {"step_us": round(step_us, 2), "GBps": round(wbytes / step_us / 1e3, 1),
                      "kernel_us": kus}
@@ -449,7 +451,8 @@ def time_decode_leg(hip, torch, steps, probe):
     # same rows is reported beside it.
     return {"workload": w.name, "rows": rows, "live_experts": len(live),
             "unique_weight_bytes": int(wbytes),
-            "timing": "each step after a 2 GiB cache-evicting read", **res,
+            "timing": "each step after a 2 GiB cache-evicting read; medians over the steps",
+            **res,
             "faster_path": min(res, key=lambda k: res[k]["step_us"]),
             "roofline": roof("moe_w4a16_gemv_union_swiglu (gate_up + SwiGLU)",
                              res["union"]["kernel_us"]["gemv_union_gate_up_swiglu"]),
